@@ -1,0 +1,138 @@
+/*
+ * padecode.h -- C ABI of libpadecode.so: single-token decode attention over a
+ * paged KV cache on MI355X (gfx950).
+ *
+ * The operation (stated on the pages only in words; no formula is printed):
+ *  - "rvLLM: High-performance LLM inference in Rust", section "Kernel Compiler
+ *    Stack": decode attention with an online softmax over a paged KV cache and
+ *    grouped-query heads, one of the per-layer decode ops; section "FA3 v3
+ *    Attention Kernel": split-KV spreads one long context over several
+ *    workgroups; section "What's Inside": a paged KV cache in f16 or FP8;
+ *    section "Optional Features": an FP8 KV cache.
+ *  - "RapidLLM", feature table, row "Decode context parallelism": partial
+ *    attention over disjoint KV ranges is combined by log-sum-exp.
+ *  - "Litellama", section "Architecture": the per-step KV bookkeeping (block
+ *    table and context lengths) is handed to the kernels.
+ *
+ * For each sequence b < batch and query head h < num_q_heads, with
+ * G = num_q_heads / num_kv_heads, KV head g = h / G and L = context_lens[b]:
+ *     s_t = scale * sum_d q[b][h][d] * K_t[d]          t = 0 .. L-1
+ *     out[b][h][:] = sum_t softmax(s)_t * V_t
+ *     lse[b][h]    = log sum_t exp(s_t)                (natural log)
+ * where token t of sequence b lives in physical block block_table[b][t / 16],
+ * slot t % 16. An fp8 cache holds codes c with value e4m3(c) * k_scale[g]
+ * (resp. v_scale[g]).
+ *
+ * Memory layouts (all row-major, all DEVICE memory owned by the caller):
+ *   q            [batch][num_q_heads][head_dim]                io_dtype
+ *   out          [batch][num_q_heads][head_dim]                io_dtype
+ *   k_cache      [num_blocks][num_kv_heads][head_dim/X][16][X] kv_dtype
+ *                  X = 16 / sizeof(kv element): 4 (f32), 8 (f16, bf16), 16 (fp8)
+ *                  i.e. every 16-byte run holds X consecutive head-dim
+ *                  elements of one token.
+ *   v_cache      [num_blocks][num_kv_heads][head_dim][16]      kv_dtype
+ *                  i.e. each (block, head) page is stored transposed: one
+ *                  row of 16 token values per head-dim element.
+ *   block_table  int32 [batch][max_blocks_per_seq]
+ *   context_lens int32 [batch]
+ *   k_scale, v_scale  float32 [num_kv_heads] (fp8 cache only)
+ *   lse_out      float32 [batch][num_q_heads] (optional, natural log)
+ * One (block, KV head) page of K or of V is one contiguous 16*head_dim run.
+ *
+ * Errors: every argument is checked on the host before anything is enqueued;
+ * a status other than PA_OK means nothing was launched. Nothing falls back to
+ * another path: unsupported combinations are errors.
+ *
+ * Device-side metadata (context_lens, block_table) cannot be checked on the
+ * host. The contract is 0 <= context_lens[b] <= 16 * max_blocks_per_seq and
+ * 0 <= block_table[b][j] < num_blocks for j < ceil(context_lens[b] / 16);
+ * entries past a sequence's last block are never read. The kernels never read
+ * outside the caches when the contract is broken: a sequence with an
+ * out-of-range length or block id gets NaN outputs instead.
+ *
+ * Thread safety: the library keeps no state between calls apart from what
+ * the caller passes in. Calls are enqueued on `stream`; inputs must stay
+ * alive and unmodified until the stream passes the call. Two calls that share
+ * a workspace must be ordered on one stream.
+ */
+#ifndef PADECODE_H
+#define PADECODE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PA_F32 = 0,
+  PA_F16 = 1,
+  PA_BF16 = 2,
+  PA_FP8_E4M3 = 3 /* OCP E4M3, no infinities; S.1111.111 is NaN; max 448 */
+} pa_dtype;
+
+typedef enum {
+  PA_OK = 0,
+  PA_ERR_NULL = 1,      /* a required pointer is NULL */
+  PA_ERR_SHAPE = 2,     /* unsupported or inconsistent sizes */
+  PA_ERR_DTYPE = 3,     /* unsupported io/kv dtype combination */
+  PA_ERR_WORKSPACE = 4, /* workspace missing or smaller than required */
+  PA_ERR_ALIGN = 5,     /* a tensor pointer is not 16-byte aligned */
+  PA_ERR_HIP = 6        /* the HIP runtime refused the launch */
+} pa_status;
+
+typedef struct {
+  int32_t batch;              /* >= 0; 0 is a no-op */
+  int32_t num_q_heads;        /* >= 1, a multiple of num_kv_heads */
+  int32_t num_kv_heads;       /* >= 1; num_q_heads / num_kv_heads <= 16 */
+  int32_t head_dim;           /* 64 or 128 */
+  int32_t block_size;         /* must be 16 */
+  int32_t max_blocks_per_seq; /* row stride of block_table, >= 1 */
+  int32_t num_blocks;         /* physical blocks in each cache, >= 1 */
+  int32_t partition_size;     /* 0: one pass per sequence; else a positive
+                                 multiple of 16 tokens: split-K partitions of
+                                 that many tokens, merged by log-sum-exp */
+} pa_shape;
+
+/* Bytes of workspace pa_decode needs for this shape: 0 when
+ * partition_size == 0, else room for float32 partial outputs and
+ * log-sum-exps of every (sequence, query head, partition) plus one counter
+ * per (sequence, KV head). A workspace must be zero-filled once before its
+ * first use (pa_workspace_reset does this on a stream); every completed call
+ * leaves it zero-filled again where that matters. Returns 0 for a NULL or
+ * invalid shape. */
+size_t pa_decode_workspace_bytes(const pa_shape* shape);
+
+/* Decode attention, enqueued on `stream` (a hipStream_t; NULL = the default
+ * stream).
+ *   scale        softmax scale (e.g. 1/sqrt(head_dim))
+ *   io_dtype     dtype of q and out: PA_F32, PA_F16 or PA_BF16
+ *   kv_dtype     dtype of the caches: io_dtype, or PA_FP8_E4M3 when io_dtype
+ *                is PA_F16 or PA_BF16
+ *   k_scale, v_scale  required for PA_FP8_E4M3, ignored otherwise
+ *   workspace    device memory of at least pa_decode_workspace_bytes(shape)
+ *                bytes (ignored when partition_size == 0), 256-byte aligned
+ *   lse_out      optional (NULL to skip)
+ * Returns PA_OK once the work is enqueued. */
+pa_status pa_decode(const pa_shape* shape, const void* q, const void* k_cache,
+                    const void* v_cache, const int32_t* block_table,
+                    const int32_t* context_lens, float scale, pa_dtype io_dtype,
+                    pa_dtype kv_dtype, const float* k_scale,
+                    const float* v_scale, void* workspace,
+                    size_t workspace_bytes, void* out, float* lse_out,
+                    void* stream);
+
+/* Zero-fill a workspace on `stream` with a fill kernel (safe to capture in a
+ * HIP graph). */
+pa_status pa_workspace_reset(void* workspace, size_t workspace_bytes,
+                             void* stream);
+
+/* Static description of a status code; never NULL. */
+const char* pa_status_str(pa_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PADECODE_H */

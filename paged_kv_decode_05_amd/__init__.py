@@ -1,0 +1,11 @@
+"""Paged single-token decode attention for MI355X (gfx950).
+
+The compute path is the HIP library built from csrc/ (libpadecode.so); the
+Python side only marshals torch tensors into its C ABI. Importing this package
+does not load the library; `decode()` does, and raises if it is missing.
+"""
+from ._lib import (PaError, decode, library_path, load_library,
+                   workspace_bytes, reset_workspace)
+
+__all__ = ["PaError", "decode", "library_path", "load_library",
+           "workspace_bytes", "reset_workspace"]

@@ -1,0 +1,149 @@
+"""ctypes binding to libpadecode.so (C ABI in include/padecode.h).
+
+Argument marshalling only: shapes and dtypes are read off torch tensors and
+passed as plain pointers; every step of the computation runs in the HIP
+kernels. There is no fallback: if the library is missing, `decode` raises.
+"""
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_NAME = "libpadecode.so"
+
+PA_F32, PA_F16, PA_BF16, PA_FP8_E4M3 = 0, 1, 2, 3
+DTYPE_CODE = {"f32": PA_F32, "f16": PA_F16, "bf16": PA_BF16, "fp8_e4m3": PA_FP8_E4M3}
+
+EXPORTED = ("pa_decode", "pa_decode_workspace_bytes", "pa_workspace_reset",
+            "pa_status_str")
+
+
+class PaError(RuntimeError):
+    def __init__(self, status, msg):
+        super().__init__(f"pa_decode failed ({status}): {msg}")
+        self.status = status
+
+
+class PaShape(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "batch", "num_q_heads", "num_kv_heads", "head_dim", "block_size",
+        "max_blocks_per_seq", "num_blocks", "partition_size")]
+
+
+_lib = None
+
+
+def library_path():
+    return os.path.join(_HERE, LIB_NAME)
+
+
+def load_library(path=None):
+    """Load libpadecode.so (after torch, so both share one HIP runtime)."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    import torch  # noqa: F401  -- torch's HIP runtime must be loaded first
+    p = path or library_path()
+    if not os.path.exists(p):
+        raise PaError(-1, f"{p} is not built; run __graft_entry__.build()")
+    lib = ctypes.CDLL(p)
+    vp, i32p, f32p = ctypes.c_void_p, ctypes.POINTER(ctypes.c_int32), ctypes.c_void_p
+    lib.pa_decode_workspace_bytes.argtypes = [ctypes.POINTER(PaShape)]
+    lib.pa_decode_workspace_bytes.restype = ctypes.c_size_t
+    lib.pa_decode.argtypes = [ctypes.POINTER(PaShape), vp, vp, vp, vp, vp, ctypes.c_float,
+                              ctypes.c_int, ctypes.c_int, vp, vp, vp, ctypes.c_size_t, vp,
+                              vp, vp]
+    lib.pa_decode.restype = ctypes.c_int
+    lib.pa_workspace_reset.argtypes = [vp, ctypes.c_size_t, vp]
+    lib.pa_workspace_reset.restype = ctypes.c_int
+    lib.pa_status_str.argtypes = [ctypes.c_int]
+    lib.pa_status_str.restype = ctypes.c_char_p
+    del i32p, f32p
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def status_str(code):
+    return load_library().pa_status_str(code).decode()
+
+
+def _check(code):
+    if code != 0:
+        raise PaError(code, status_str(code))
+
+
+def _torch_dtype_name(t):
+    import torch
+    return {torch.float32: "f32", torch.float16: "f16", torch.bfloat16: "bf16",
+            torch.float8_e4m3fn: "fp8_e4m3", torch.uint8: "fp8_e4m3"}.get(t.dtype)
+
+
+def make_shape(q, k_cache, block_table, partition_size):
+    B, Hq, D = q.shape
+    return PaShape(batch=B, num_q_heads=Hq, num_kv_heads=k_cache.shape[1], head_dim=D,
+                   block_size=k_cache.shape[3], max_blocks_per_seq=block_table.shape[1],
+                   num_blocks=k_cache.shape[0], partition_size=partition_size)
+
+
+def workspace_bytes(q, k_cache, block_table, partition_size):
+    shape = make_shape(q, k_cache, block_table, partition_size)
+    return int(load_library().pa_decode_workspace_bytes(ctypes.byref(shape)))
+
+
+def reset_workspace(workspace, stream=None):
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream()
+    _check(load_library().pa_workspace_reset(workspace.data_ptr(), workspace.numel()
+                                             * workspace.element_size(), s.cuda_stream))
+
+
+def decode(q, k_cache, v_cache, block_table, context_lens, scale, *, k_scale=None,
+           v_scale=None, partition_size=0, out=None, workspace=None, lse_out=None,
+           stream=None):
+    """out[b, h] = softmax(scale * q[b, h] . K^T) V over sequence b's paged cache.
+
+    q [B, Hq, D] (float32 | float16 | bfloat16); k_cache [nb, Hkv, D/X, 16, X];
+    v_cache [nb, Hkv, D, 16] (q's dtype, or float8_e4m3fn / uint8 codes with
+    float32 k_scale, v_scale [Hkv]); block_table int32 [B, MBS];
+    context_lens int32 [B]. `workspace` (uint8, zero-filled once) is required
+    when partition_size > 0; `workspace_bytes` gives its size.
+    """
+    import torch
+    lib = load_library()
+    io = _torch_dtype_name(q)
+    kv = _torch_dtype_name(k_cache)
+    if io is None or kv is None or _torch_dtype_name(v_cache) != kv:
+        raise PaError(3, f"unsupported dtypes q={q.dtype} k={k_cache.dtype} v={v_cache.dtype}")
+    for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache),
+                    ("block_table", block_table), ("context_lens", context_lens)):
+        if not t.is_cuda or not t.is_contiguous():
+            raise PaError(2, f"{name} must be a contiguous device tensor")
+    if block_table.dtype != torch.int32 or context_lens.dtype != torch.int32:
+        raise PaError(3, "block_table and context_lens must be int32")
+    if q.dim() != 3 or k_cache.dim() != 5 or v_cache.dim() != 4 or block_table.dim() != 2:
+        raise PaError(2, "expected q [B,Hq,D], k_cache [nb,Hkv,D/X,16,X], v_cache [nb,Hkv,D,16]")
+    B, Hq, D = q.shape
+    nb, Hkv = k_cache.shape[0], k_cache.shape[1]
+    if (tuple(v_cache.shape) != (nb, Hkv, D, k_cache.shape[3])
+            or k_cache.shape[2] * k_cache.shape[4] != D
+            or tuple(block_table.shape[:1]) != (B,) or tuple(context_lens.shape) != (B,)):
+        raise PaError(2, "inconsistent tensor shapes")
+    if out is None:
+        out = torch.empty_like(q)
+    shape = make_shape(q, k_cache, block_table, partition_size)
+    ws_ptr, ws_bytes = None, 0
+    if partition_size:
+        need = int(lib.pa_decode_workspace_bytes(ctypes.byref(shape)))
+        if workspace is None:
+            workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    ks = k_scale.data_ptr() if k_scale is not None else None
+    vs = v_scale.data_ptr() if v_scale is not None else None
+    s = stream if stream is not None else torch.cuda.current_stream()
+    code = lib.pa_decode(ctypes.byref(shape), q.data_ptr(), k_cache.data_ptr(),
+                         v_cache.data_ptr(), block_table.data_ptr(), context_lens.data_ptr(),
+                         float(scale), DTYPE_CODE[io], DTYPE_CODE[kv], ks, vs, ws_ptr,
+                         ws_bytes, out.data_ptr(),
+                         lse_out.data_ptr() if lse_out is not None else None, s.cuda_stream)
+    _check(code)
+    return out
