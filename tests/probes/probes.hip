@@ -1,0 +1,86 @@
+// Test-only probes of gfx950 building blocks the decode kernels rely on:
+//  * the lane layout of the 16x16 MFMA operands and accumulator
+//    (A: lane l holds row l%16, B: lane l holds column l%16, both with the
+//    same per-lane k-slots; C: lane l holds rows 4*(l/16)+i of column l%16);
+//  * exactness of the E4M3 -> f16 / bf16 conversion instructions.
+// Each probe is one 64-thread workgroup over small, fully in-bounds buffers.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// which: 0 = f16 16x16x32, 1 = bf16 16x16x32, 2 = f16 16x16x16, 3 = bf16 16x16x16,
+//        4 = f32 16x16x4.  A is [16][K] row-major, B is [K][16] row-major, both in
+// the operand type (f32 for which 4); C is [16][16] f32.
+__global__ void mfma_probe_kernel(int which, const void* A, const void* B, float* C) {
+  const int l = threadIdx.x, r = l % 16, j = l / 16;
+  f32x4 c = {0.f, 0.f, 0.f, 0.f};
+  if (which == 0 || which == 1) {
+    const uint16_t* a = (const uint16_t*)A;
+    const uint16_t* b = (const uint16_t*)B;
+    uint16_t av[8], bv[8];
+    for (int i = 0; i < 8; ++i) {
+      av[i] = a[r * 32 + 8 * j + i];
+      bv[i] = b[(8 * j + i) * 16 + r];
+    }
+    if (which == 0) {
+      f16x8 x = __builtin_bit_cast(f16x8, av), y = __builtin_bit_cast(f16x8, bv);
+      c = __builtin_amdgcn_mfma_f32_16x16x32_f16(x, y, c, 0, 0, 0);
+    } else {
+      bf16x8 x = __builtin_bit_cast(bf16x8, av), y = __builtin_bit_cast(bf16x8, bv);
+      c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x, y, c, 0, 0, 0);
+    }
+  } else if (which == 2 || which == 3) {
+    const uint16_t* a = (const uint16_t*)A;
+    const uint16_t* b = (const uint16_t*)B;
+    uint16_t av[4], bv[4];
+    for (int i = 0; i < 4; ++i) {
+      av[i] = a[r * 16 + 4 * j + i];
+      bv[i] = b[(4 * j + i) * 16 + r];
+    }
+    if (which == 2) {
+      f16x4 x = __builtin_bit_cast(f16x4, av), y = __builtin_bit_cast(f16x4, bv);
+      c = __builtin_amdgcn_mfma_f32_16x16x16f16(x, y, c, 0, 0, 0);
+    } else {
+      bf16x4 x = __builtin_bit_cast(bf16x4, av), y = __builtin_bit_cast(bf16x4, bv);
+      c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(x, y, c, 0, 0, 0);
+    }
+  } else {
+    const float* a = (const float*)A;
+    const float* b = (const float*)B;
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[r * 4 + j], b[j * 16 + r], c, 0, 0, 0);
+  }
+  for (int i = 0; i < 4; ++i) C[(4 * j + i) * 16 + r] = c[i];
+}
+
+// codes: 256 bytes (one dword = 4 codes per lane); out16/outb: 256 16-bit words.
+__global__ void fp8_probe_kernel(const uint32_t* codes, uint32_t* out16, uint32_t* outb) {
+  const int l = threadIdx.x;
+  const uint32_t w = codes[l];
+  f16x2 lo = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false);
+  f16x2 hi = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true);
+  out16[2 * l] = __builtin_bit_cast(uint32_t, lo);
+  out16[2 * l + 1] = __builtin_bit_cast(uint32_t, hi);
+  bf16x2 blo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false);
+  bf16x2 bhi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true);
+  outb[2 * l] = __builtin_bit_cast(uint32_t, blo);
+  outb[2 * l + 1] = __builtin_bit_cast(uint32_t, bhi);
+}
+
+extern "C" int pa_probe_mfma(int which, const void* A, const void* B, float* C, void* stream) {
+  if (which < 0 || which > 4) return 1;
+  hipLaunchKernelGGL(mfma_probe_kernel, dim3(1), dim3(64), 0, (hipStream_t)stream, which, A, B, C);
+  return hipGetLastError() == hipSuccess ? 0 : 2;
+}
+
+extern "C" int pa_probe_fp8(const void* codes, void* out16, void* outb, void* stream) {
+  hipLaunchKernelGGL(fp8_probe_kernel, dim3(1), dim3(64), 0, (hipStream_t)stream,
+                     (const uint32_t*)codes, (uint32_t*)out16, (uint32_t*)outb);
+  return hipGetLastError() == hipSuccess ? 0 : 2;
+}
