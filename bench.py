@@ -1,0 +1,252 @@
+#!/usr/bin/env python3
+"""Paged decode attention on one MI355X: KV-read GB/s, % of HBM peak and
+sequence-tokens per second.
+
+One step is one pa_decode call (one kernel launch) over the whole batch of the
+Qwen2.5-7B-shaped workload: 32 sequences, 28 query / 4 KV heads, head_dim 128,
+f16 q/K/V, context lengths uniform in [512, 4096], 16-token blocks shuffled
+over the pool, split-K partitions of 512 tokens merged by log-sum-exp
+(`--workload` picks one of the other four for information). Inputs are
+resident in HBM before timing starts. Calls rotate over enough copies of the
+KV pool (>= 3 x 256 MiB) that the 256 MiB Infinity Cache cannot serve repeats.
+
+    python bench.py [--steps K] [--warmup W] [--workload 1..5]
+
+Prints one JSON line. `value` is KV-read GB/s: the K and V bytes of every
+(sequence, cached token, KV head) the call attends, divided by the time per
+call (HIP events on the launching stream around the K timed calls).
+`cpu_baseline` times the float64 CPU oracle on the host on the same workload
+and checks the GPU output against it.
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "paged decode attention KV-read GB/s (% of HBM peak) and seqs·tokens/sec"
+PEAK_GBPS = 8000.0            # MI355X HBM3E, published
+MALL_BYTES = 256 << 20        # Infinity Cache
+KERNEL_SRC = os.path.join(ROOT, "paged_kv_decode_05_amd", "csrc", "pa_decode.hip")
+PROBES = os.path.join(ROOT, "tests", "probes", "libpaprobes.so")
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--workload", type=int, default=3, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="minimum host time spent timing the oracle")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-stream-ceiling", action="store_true")
+    ap.add_argument("--pmc-pass", action="store_true",
+                    help="run a 1 GiB device copy and 20 decode calls, print nothing else "
+                         "(for rocprofv3 --pmc counter passes)")
+    return ap.parse_args()
+
+
+def kernel_sha256():
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def traffic_from_profile(wl_name):
+    """HBM bytes per launch from the committed counter summary, if it was taken
+    on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"pmc_traffic_{wl_name}.md")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        for line in f:
+            m = re.match(r"^machine:\s*(\{.*\})\s*$", line)
+            if m:
+                rec = json.loads(m.group(1))
+                if rec.get("kernel_sha256") == kernel_sha256():
+                    return rec.get("traffic_bytes_per_launch")
+    return None
+
+
+def stream_read_ceiling(torch):
+    """GB/s of a plain streaming-read kernel over 2 GiB on this GPU."""
+    import ctypes
+    if not os.path.exists(PROBES):
+        return None
+    lib = ctypes.CDLL(PROBES)
+    lib.pa_probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                         ctypes.c_int, ctypes.c_void_p]
+    nbytes = 2 << 30
+    buf = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda")
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    s = torch.cuda.current_stream()
+    best = 0.0
+    for blocks in (1024, 2048, 4096, 8192):
+        for _ in range(2):
+            assert lib.pa_probe_stream_read(buf.data_ptr(), nbytes, sink.data_ptr(), blocks,
+                                            s.cuda_stream) == 0
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(s)
+        n = 10
+        for _ in range(n):
+            lib.pa_probe_stream_read(buf.data_ptr(), nbytes, sink.data_ptr(), blocks,
+                                     s.cuda_stream)
+        e1.record(s)
+        torch.cuda.synchronize()
+        best = max(best, nbytes * n / (e0.elapsed_time(e1) / 1e3) / 1e9)
+    del buf
+    return best
+
+
+def cpu_baseline(wl, gpu_out_f64, min_seconds):
+    """Time the float64 oracle on the host over the whole workload (repeated
+    until min_seconds have passed) and compare the GPU output with it."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = 1
+    s = wl.spec
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        ref = oracle.paged_decode_ref(wl.q, wl.k_cache, wl.v_cache, wl.block_table,
+                                      wl.context_lens, wl.scale, s.io_dtype, s.kv_dtype,
+                                      wl.k_scale, wl.v_scale)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= min_seconds:
+            break
+    per_call = el / reps
+    err = np.abs(gpu_out_f64 - ref)
+    return {
+        "value": round(wl.kv_bytes_logical() / per_call / 1e9, 4),
+        "unit": "GB/s",
+        "cores": int(cores),
+        "kind": "oracle",
+        "sample": f"the whole workload ({s.batch} sequences, "
+                  f"{int(wl.context_lens.sum())} cached tokens), {reps} full oracle "
+                  f"passes in {el:.1f} s; float64 numpy, BLAS threads = cores",
+        "seconds_per_step": round(per_call, 4),
+        "parity_vs_gpu": {"max_abs": float(err.max()), "mean_abs": float(err.mean())},
+    }
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: the decode path runs whole on one MI355X and "
+              "has no multi-GPU mode; run it with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import paged_kv_decode_05_amd as pkd
+    from paged_kv_decode_05_amd import workloads as W
+
+    spec = W.SPECS[args.workload]
+    wl = W.make_workload(spec)
+    dev = torch.device("cuda:0")
+    t = W.to_device(wl, dev)
+    pool_bytes = t["k_cache"].numel() * t["k_cache"].element_size() * 2
+    reps = max(1, math.ceil(3 * MALL_BYTES / pool_bytes))
+    kcs = [t["k_cache"]] + [t["k_cache"].clone() for _ in range(reps - 1)]
+    vcs = [t["v_cache"]] + [t["v_cache"].clone() for _ in range(reps - 1)]
+    out = torch.empty_like(t["q"])
+    ps = spec.partition_size
+    ws = None
+    if ps:
+        ws = torch.empty(pkd.workspace_bytes(t["q"], t["k_cache"], t["block_table"], ps),
+                         dtype=torch.uint8, device=dev)
+        pkd.reset_workspace(ws)
+    stream = torch.cuda.current_stream()
+    calls = [pkd.prepare(t["q"], kcs[i], vcs[i], t["block_table"], t["context_lens"],
+                         float(wl.scale), k_scale=t["k_scale"], v_scale=t["v_scale"],
+                         partition_size=ps, out=out, workspace=ws, stream=stream)
+             for i in range(reps)]
+
+    if args.pmc_pass:
+        src = torch.ones(1 << 28, dtype=torch.int32, device=dev)      # 1 GiB
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        for i in range(20):
+            calls[i % reps]()
+        torch.cuda.synchronize()
+        return
+
+    for i in range(args.warmup):
+        calls[i % reps]()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(args.steps):
+        calls[i % reps]()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    gpu_out = out.float().cpu().numpy().astype(np.float64)
+
+    kv_bytes = wl.kv_bytes_logical()
+    gbps = kv_bytes / (ms / 1e3) / 1e9
+    sum_tokens = int(wl.context_lens.astype(np.int64).sum())
+    traffic = traffic_from_profile(spec.name)
+    ceiling = None if args.no_stream_ceiling else stream_read_ceiling(torch)
+
+    rec = {
+        "metric": METRIC,
+        "value": round(gbps, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {"f32": "f32", "f16": "f16", "bf16": "bf16"}[spec.io_dtype]
+                 + ("" if spec.kv_dtype == spec.io_dtype else "+fp8_e4m3_kv"),
+        "data": "synthetic (seeded N(0,1) q/K/V, seeded lengths and block permutation)",
+        "config": {
+            "workload": spec.name,
+            "batch": spec.batch,
+            "q_heads": spec.num_q_heads,
+            "kv_heads": spec.num_kv_heads,
+            "head_dim": spec.head_dim,
+            "block_size": 16,
+            "context_lens": f"{spec.lens[0]} {list(spec.lens[1:])}",
+            "sum_context_tokens": sum_tokens,
+            "partition_size": ps,
+            "kv_bytes_per_step": kv_bytes,
+            "kv_bytes_unique_per_step": wl.kv_bytes_unique(),
+            "pool_copies_rotated": reps,
+        },
+        "pct_hbm_peak": round(100.0 * gbps / PEAK_GBPS, 2),
+        "seq_tokens_per_s": round(sum_tokens / (ms / 1e3), 1),
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(gbps, 2),
+            "peak": PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(gbps / PEAK_GBPS, 4),
+            "traffic": traffic,
+        },
+        "stream_read_ceiling_GBps": None if ceiling is None else round(ceiling, 1),
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(wl, gpu_out, args.cpu_seconds)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

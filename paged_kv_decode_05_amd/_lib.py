@@ -46,7 +46,7 @@ def load_library(path=None):
     if not os.path.exists(p):
         raise PaError(-1, f"{p} is not built; run __graft_entry__.build()")
     lib = ctypes.CDLL(p)
-    vp, i32p, f32p = ctypes.c_void_p, ctypes.POINTER(ctypes.c_int32), ctypes.c_void_p
+    vp = ctypes.c_void_p
     lib.pa_decode_workspace_bytes.argtypes = [ctypes.POINTER(PaShape)]
     lib.pa_decode_workspace_bytes.restype = ctypes.c_size_t
     lib.pa_decode.argtypes = [ctypes.POINTER(PaShape), vp, vp, vp, vp, vp, ctypes.c_float,
@@ -57,7 +57,6 @@ def load_library(path=None):
     lib.pa_workspace_reset.restype = ctypes.c_int
     lib.pa_status_str.argtypes = [ctypes.c_int]
     lib.pa_status_str.restype = ctypes.c_char_p
-    del i32p, f32p
     if path is None:
         _lib = lib
     return lib
@@ -100,6 +99,29 @@ def reset_workspace(workspace, stream=None):
 def decode(q, k_cache, v_cache, block_table, context_lens, scale, *, k_scale=None,
            v_scale=None, partition_size=0, out=None, workspace=None, lse_out=None,
            stream=None):
+    return prepare(q, k_cache, v_cache, block_table, context_lens, scale, k_scale=k_scale,
+                   v_scale=v_scale, partition_size=partition_size, out=out,
+                   workspace=workspace, lse_out=lse_out, stream=stream)()
+
+
+class Prepared:
+    """A pa_decode call with its arguments marshalled once; calling it enqueues
+    the decode again on the same buffers (their contents may change)."""
+
+    def __init__(self, lib, args, out, keep):
+        self._fn = lib.pa_decode
+        self._args = args
+        self.out = out
+        self._keep = keep
+
+    def __call__(self):
+        _check(self._fn(*self._args))
+        return self.out
+
+
+def prepare(q, k_cache, v_cache, block_table, context_lens, scale, *, k_scale=None,
+            v_scale=None, partition_size=0, out=None, workspace=None, lse_out=None,
+            stream=None):
     """out[b, h] = softmax(scale * q[b, h] . K^T) V over sequence b's paged cache.
 
     q [B, Hq, D] (float32 | float16 | bfloat16); k_cache [nb, Hkv, D/X, 16, X];
@@ -140,10 +162,10 @@ def decode(q, k_cache, v_cache, block_table, context_lens, scale, *, k_scale=Non
     ks = k_scale.data_ptr() if k_scale is not None else None
     vs = v_scale.data_ptr() if v_scale is not None else None
     s = stream if stream is not None else torch.cuda.current_stream()
-    code = lib.pa_decode(ctypes.byref(shape), q.data_ptr(), k_cache.data_ptr(),
-                         v_cache.data_ptr(), block_table.data_ptr(), context_lens.data_ptr(),
-                         float(scale), DTYPE_CODE[io], DTYPE_CODE[kv], ks, vs, ws_ptr,
-                         ws_bytes, out.data_ptr(),
-                         lse_out.data_ptr() if lse_out is not None else None, s.cuda_stream)
-    _check(code)
-    return out
+    args = (ctypes.byref(shape), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+            block_table.data_ptr(), context_lens.data_ptr(), float(scale), DTYPE_CODE[io],
+            DTYPE_CODE[kv], ks, vs, ws_ptr, ws_bytes, out.data_ptr(),
+            lse_out.data_ptr() if lse_out is not None else None, s.cuda_stream)
+    keep = (shape, q, k_cache, v_cache, block_table, context_lens, k_scale, v_scale,
+            workspace, out, lse_out)
+    return Prepared(lib, args, out, keep)

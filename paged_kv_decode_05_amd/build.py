@@ -14,6 +14,9 @@ COMMON = [
     "-O3", "--offload-arch=gfx950", "-std=c++17", "-fPIC", "-shared",
     # keep hipcc from forming packed fp32 instructions
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # matrix-core accumulators in ordinary VGPRs: the online-softmax rescale
+    # multiplies them in place instead of copying through AGPRs
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-I", os.path.join(ROOT, "include"),
 ]
 

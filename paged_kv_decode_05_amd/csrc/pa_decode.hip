@@ -11,23 +11,26 @@
 // One kernel does the whole call. A workgroup of kWaves wavefronts owns one
 // (sequence b, KV head g, partition p) unit. Its waves take the unit's
 // 16-token pages round-robin; per page a wave
-//   1. reads the physical block id (block table, kept in a VGPR and read out
-//      with readlane),
+//   1. reads the physical block id (block ids are fetched 64 pages at a time
+//      into a VGPR, one chunk ahead, and read out with readlane, so page
+//      addresses are wave-uniform scalars),
 //   2. loads the K page and the V page straight from HBM into registers in the
-//      layout the matrix cores consume (the cache layouts in padecode.h are
-//      chosen so that these loads are contiguous 16-byte or 8-byte runs),
+//      layout the matrix cores consume (the cache layouts in padecode.h make
+//      every one of these loads a contiguous run); loads run one to three
+//      pages ahead of the math through a ring of register buffers,
 //   3. computes S^T[token][head] = K Q^T for the whole GQA group with MFMA
 //      (query heads padded to 16 columns),
-//   4. masks tokens past the partition end, updates the running max / sum in
+//   4. masks tokens past the unit's end, updates the running max and sum in
 //      base 2 (scale * log2 e folded into one multiplier),
 //   5. rounds P to the 16-bit operand type and accumulates O^T += V^T P^T with
-//      MFMA; the running sum uses the same rounded P.
-// The page loads of page i+1 are issued before page i is computed.
+//      MFMA; the running sum uses the same rounded P. The accumulator is
+//      rescaled only when some head's running max moved.
 // The waves' partial results are merged through LDS. With split-K, the
-// partition's normalised output and base-2 log-sum-exp go to the workspace,
-// and the last workgroup of each (b, g) to finish (an atomic counter) merges
-// all partitions of that sequence in a fixed order and writes the output, then
-// resets the counter to zero.
+// partition's normalised output and base-2 log-sum-exp go to the workspace
+// through agent-coherent stores; the last workgroup of each (b, g) to finish
+// (device-scope atomic counter) reads them back with agent-coherent loads,
+// merges all partitions of that sequence in a fixed order, writes the output
+// and resets the counter to zero.
 //
 // fp8 (OCP E4M3) caches are widened exactly to f16/bf16 with the gfx950
 // conversion instructions; k_scale folds into the score multiplier and
@@ -36,6 +39,8 @@
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 #include "padecode.h"
 
@@ -75,7 +80,7 @@ struct Params {
   uint8_t* out;
   float* lse_out;
   float* ws_o;       // [B][Hq][p_max][D]
-  float* ws_lse;     // [B][Hq][p_max]   base-2, scaled score units
+  float* ws_lse;     // [B][Hq][p_max]   base 2, in units of the scaled scores
   uint32_t* ws_cnt;  // [B][Hkv]
   float scale;
   int32_t num_q_heads;
@@ -90,8 +95,8 @@ struct Params {
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float log2_fast(float x) { return __builtin_amdgcn_logf(x); }
 
+// Lanes l, l^16, l^32, l^48 hold the same query head.
 __device__ __forceinline__ float wave_max_rows(float x) {
-  // lanes l, l^16, l^32, l^48 hold the same query head
   x = fmaxf(x, __shfl_xor(x, 16));
   x = fmaxf(x, __shfl_xor(x, 32));
   return x;
@@ -102,28 +107,42 @@ __device__ __forceinline__ float wave_sum_rows(float x) {
   return x;
 }
 
-template <typename T>
-__device__ __forceinline__ T load_nt(const T* p) {
-  return *p;
+// Global-memory pointer every lane agrees on, kept in scalar registers, so
+// loads take the saddr + 32-bit voffset form of global_load.
+typedef const __attribute__((address_space(1))) uint8_t* gptr;
+__device__ __forceinline__ gptr uniform_ptr(const uint8_t* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32));
+  return (gptr)((static_cast<uint64_t>(hi) << 32) | lo);
+}
+
+template <typename V>
+__device__ __forceinline__ V ld(gptr base, uint32_t off) {
+  return *(const __attribute__((address_space(1))) V*)(base + off);
+}
+
+// Agent-coherent (write-through / cache-revalidating) float store and load.
+__device__ __forceinline__ void st_agent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_agent(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ---------------------------------------------------------------------------
-// Per-dtype pieces. A "family" fixes the matrix-core operand type.
-//
-// 16-bit family (q/out f16 or bf16): QK^T uses 16x16x32 MFMA (8 head-dim
-// elements per lane per instruction), PV uses 16x16x16 (4 tokens per lane).
-// fp32 family: both use 16x16x4 f32 MFMA (1 element per lane).
+// Matrix-core operand types.
 //
 // Lane l of a wave is (r = l % 16, jj = l / 16). In the QK^T product lane l
-// feeds token r of the page (A operand) and query head r (B operand); its
-// k-slots are the head-dim elements of 16-byte group jj + 4*i of the K page.
-// The 16x16 accumulator leaves lane l with rows 4*jj .. 4*jj+3 (tokens) of
-// column r (query head), which is exactly the B operand of the PV product
-// (k = token 4*jj + i, n = head r); its A operand is V^T[16*t + r][4*jj + i].
-// The result O^T[16*t + 4*jj + i][head r] thus stays with the lane that owns
-// head r's softmax state.
+// feeds token r of the page (A operand) and query head r (B operand); both
+// operands put the same head-dim elements in the same k-slots of the lane,
+// namely the elements of 16-byte K-page groups jj + 4*i. The 16x16
+// accumulator leaves lane l with rows 4*jj .. 4*jj+3 (tokens) of column r
+// (query head), which is exactly the B operand of the PV product (k = token
+// 4*jj + i, n = head r); its A operand is V^T[16*t + r][4*jj + i]. So the
+// result O^T[16*t + 4*jj + i][head r] stays with the lane that owns head r's
+// softmax state.
 // ---------------------------------------------------------------------------
-
 template <typename IO>
 struct Op16;
 template <>
@@ -137,14 +156,12 @@ struct Op16<F16> {
   static __device__ __forceinline__ f32x4 pv(A4 a, A4 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
   }
-  // 4 fp8 codes (one dword) -> 4 exact f16 values
+  // 4 fp8 codes (one dword, lowest byte first) -> 4 exact f16 values
   static __device__ __forceinline__ A4 fp8x4(uint32_t w) {
-    f16x2 lo = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false);
-    f16x2 hi = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true);
-    A4 r = {lo[0], lo[1], hi[0], hi[1]};
-    return r;
+    const f16x2 lo = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false);
+    const f16x2 hi = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true);
+    return A4{lo[0], lo[1], hi[0], hi[1]};
   }
-  static __device__ __forceinline__ float out_f(E x) { return (float)x; }
 };
 template <>
 struct Op16<BF16> {
@@ -158,180 +175,203 @@ struct Op16<BF16> {
     return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
   }
   static __device__ __forceinline__ A4 fp8x4(uint32_t w) {
-    bf16x2 lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false);
-    bf16x2 hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true);
-    A4 r = {lo[0], lo[1], hi[0], hi[1]};
-    return r;
+    const bf16x2 lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false);
+    const bf16x2 hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true);
+    return A4{lo[0], lo[1], hi[0], hi[1]};
   }
-  static __device__ __forceinline__ float out_f(E x) { return (float)x; }
 };
-
-template <typename T>
-__device__ __forceinline__ T bitcast16(u32x4 x) {
-  return __builtin_bit_cast(T, x);
-}
-
-// Register tile of one page for the 16-bit family.
-//   KV16 = true: 16-bit cache. K: D/32 loads of 16 B; V: D/16 loads of 8 B.
-//   KV16 = false: fp8 cache.   K: D/64 loads of 16 B; V: D/16 loads of 4 B.
-template <int D, bool KV16>
-struct PageRegs16 {
-  static constexpr int kKLoads = KV16 ? D / 32 : D / 64;
-  static constexpr int kVTiles = D / 16;
-  u32x4 k[kKLoads];
-  typename std::conditional<KV16, u32x2, uint32_t>::type v[kVTiles];
-};
-
-template <int D, bool KV16>
-__device__ __forceinline__ void load_page16(PageRegs16<D, KV16>& r, const uint8_t* kpage,
-                                            const uint8_t* vpage, int lane) {
-  const int rr = lane & 15, jj = lane >> 4;
-#pragma unroll
-  for (int i = 0; i < PageRegs16<D, KV16>::kKLoads; ++i)
-    r.k[i] = *reinterpret_cast<const u32x4*>(kpage + i * 1024 + lane * 16);
-  // V^T row d = 16*t + rr holds 16 tokens; this lane wants tokens 4*jj..4*jj+3.
-  constexpr int esz = KV16 ? 2 : 1;
-#pragma unroll
-  for (int t = 0; t < PageRegs16<D, KV16>::kVTiles; ++t) {
-    const uint8_t* p = vpage + (size_t)(16 * t + rr) * (16 * esz) + jj * 4 * esz;
-    if constexpr (KV16)
-      r.v[t] = *reinterpret_cast<const u32x2*>(p);
-    else
-      r.v[t] = *reinterpret_cast<const uint32_t*>(p);
-  }
-}
-
-// fp32 family page registers. K: D/16 loads of 16 B; V: D/16 loads of 16 B.
-template <int D>
-struct PageRegs32 {
-  static constexpr int kKLoads = D / 16;
-  static constexpr int kVTiles = D / 16;
-  f32x4 k[kKLoads];
-  f32x4 v[kVTiles];
-};
-
-template <int D>
-__device__ __forceinline__ void load_page32(PageRegs32<D>& r, const uint8_t* kpage,
-                                            const uint8_t* vpage, int lane) {
-  const int rr = lane & 15, jj = lane >> 4;
-#pragma unroll
-  for (int i = 0; i < PageRegs32<D>::kKLoads; ++i)
-    r.k[i] = *reinterpret_cast<const f32x4*>(kpage + i * 1024 + lane * 16);
-#pragma unroll
-  for (int t = 0; t < PageRegs32<D>::kVTiles; ++t)
-    r.v[t] = *reinterpret_cast<const f32x4*>(vpage + (size_t)(16 * t + rr) * 64 + jj * 16);
-}
 
 // ---------------------------------------------------------------------------
-// Online-softmax state of one wave: lane (rr, jj) tracks query head rr.
+// Page tiles: what one wave holds of one page and how it feeds the MFMAs.
+//   kKoff / kVoff: per-lane byte offsets inside a K / V page (loop constants)
+//   load(): issue the page's loads;  scores(): S^T for the page;
+//   pvt(): the V^T operand of tile t (4 tokens of row 16*t + r).
 // ---------------------------------------------------------------------------
-template <int D>
-struct WaveState {
-  float m;       // running max of scaled base-2 scores (same on the 4 lanes of a head)
-  float l;       // this lane's share of the running sum
-  f32x4 acc[D / 16];
+
+// q/out f16 or bf16 with a cache of the same type.
+template <typename IO, int D>
+struct Tile16 {
+  using O = Op16<IO>;
+  typedef typename O::A8 A8;
+  typedef typename O::A4 A4;
+  typedef A4 P;                            // PV B operand: 4 rounded probabilities
+  static constexpr int kK = D / 32;        // 16-byte K loads = QK MFMAs
+  static constexpr int kT = D / 16;        // V tiles (8-byte loads)
+  static constexpr int kStages = D == 128 ? 2 : 3;   // register ring depth
+  struct Regs {
+    u32x4 k[kK];
+    u32x2 v[kT];
+  };
+  struct Q {
+    A8 c[kK];
+  };
+  static __device__ __forceinline__ uint32_t koff(int lane) { return lane * 16; }
+  static __device__ __forceinline__ uint32_t voff(int lane) { return (lane & 15) * 32 + (lane >> 4) * 8; }
+  static __device__ __forceinline__ void load_q(Q& q, gptr qrow, int jj, bool ok) {
+#pragma unroll
+    for (int c = 0; c < kK; ++c) {
+      u32x4 raw = ld<u32x4>(qrow, 16 * (jj + 4 * c));   // head-dim 8*(jj + 4c) .. +7
+      if (!ok) raw = u32x4{0u, 0u, 0u, 0u};
+      q.c[c] = __builtin_bit_cast(A8, raw);
+    }
+  }
+  static __device__ __forceinline__ void load(Regs& r, gptr kp, gptr vp,
+                                              uint32_t ko, uint32_t vo) {
+#pragma unroll
+    for (int i = 0; i < kK; ++i) r.k[i] = ld<u32x4>(kp, ko + i * 1024);
+#pragma unroll
+    for (int t = 0; t < kT; ++t) r.v[t] = ld<u32x2>(vp, vo + t * 512);
+  }
+  static __device__ __forceinline__ f32x4 scores(const Regs& r, const Q& q) {
+    f32x4 s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < kK; ++c) s = O::qk(__builtin_bit_cast(A8, r.k[c]), q.c[c], s);
+    return s;
+  }
+  static __device__ __forceinline__ A4 pvt(const Regs& r, int t) {
+    return __builtin_bit_cast(A4, r.v[t]);
+  }
+  static __device__ __forceinline__ P pack(const float p[4]) {
+    return P{(typename O::E)p[0], (typename O::E)p[1], (typename O::E)p[2], (typename O::E)p[3]};
+  }
+  static __device__ __forceinline__ float psum(P p) {
+    return ((float)p[0] + (float)p[1]) + ((float)p[2] + (float)p[3]);
+  }
+  static __device__ __forceinline__ f32x4 pv(A4 a, P b, f32x4 c) { return O::pv(a, b, c); }
+  static __device__ __forceinline__ A4 zero_tail(A4 a, int jj, int nvalid) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (4 * jj + i >= nvalid) a[i] = (typename O::E)0.0f;
+    return a;
+  }
 };
 
-// Score scaling, masking and the online-softmax update for one page.
-// Returns the (unrounded) probabilities of this lane's 4 tokens in p[].
-__device__ __forceinline__ void softmax_page(float& m, float& alpha, float p[4], f32x4 s,
-                                             float cmul, int nvalid, int jj) {
-  float sc[4];
+// q/out f16 or bf16 with an fp8-e4m3 cache.
+template <typename IO, int D>
+struct Tile8 {
+  using O = Op16<IO>;
+  typedef typename O::A8 A8;
+  typedef typename O::A4 A4;
+  typedef A4 P;
+  static constexpr int kK = D / 64;        // 16-byte K loads, two QK MFMAs each
+  static constexpr int kT = D / 16;        // V tiles (4-byte loads)
+  static constexpr int kStages = D == 128 ? 3 : 4;
+  struct Regs {
+    u32x4 k[kK];
+    uint32_t v[kT];
+  };
+  struct Q {
+    A8 c[2 * kK];
+  };
+  static __device__ __forceinline__ uint32_t koff(int lane) { return lane * 16; }
+  static __device__ __forceinline__ uint32_t voff(int lane) { return (lane & 15) * 16 + (lane >> 4) * 4; }
+  static __device__ __forceinline__ void load_q(Q& q, gptr qrow, int jj, bool ok) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    float x = s[i] * cmul;
-    sc[i] = (4 * jj + i < nvalid) ? x : -INFINITY;
+    for (int c = 0; c < 2 * kK; ++c) {
+      // head-dim 16*(jj + 4*(c/2)) + 8*(c%2) .. +7
+      u32x4 raw = ld<u32x4>(qrow, 2 * (16 * (jj + 4 * (c / 2)) + 8 * (c % 2)));
+      if (!ok) raw = u32x4{0u, 0u, 0u, 0u};
+      q.c[c] = __builtin_bit_cast(A8, raw);
+    }
   }
-  float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
-  mx = wave_max_rows(mx);
-  const float mnew = fmaxf(m, mx);
-  alpha = exp2_fast(m - mnew);
+  static __device__ __forceinline__ void load(Regs& r, gptr kp, gptr vp,
+                                              uint32_t ko, uint32_t vo) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) p[i] = exp2_fast(sc[i] - mnew);
-  m = mnew;
-}
+    for (int i = 0; i < kK; ++i) r.k[i] = ld<u32x4>(kp, ko + i * 1024);
+#pragma unroll
+    for (int t = 0; t < kT; ++t) r.v[t] = ld<uint32_t>(vp, vo + t * 256);
+  }
+  static __device__ __forceinline__ f32x4 scores(const Regs& r, const Q& q) {
+    f32x4 s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < kK; ++c) {
+      const A4 a0 = O::fp8x4(r.k[c][0]), a1 = O::fp8x4(r.k[c][1]);
+      const A4 a2 = O::fp8x4(r.k[c][2]), a3 = O::fp8x4(r.k[c][3]);
+      const A8 lo = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+      const A8 hi = {a2[0], a2[1], a2[2], a2[3], a3[0], a3[1], a3[2], a3[3]};
+      s = O::qk(lo, q.c[2 * c], s);
+      s = O::qk(hi, q.c[2 * c + 1], s);
+    }
+    return s;
+  }
+  static __device__ __forceinline__ A4 pvt(const Regs& r, int t) { return O::fp8x4(r.v[t]); }
+  static __device__ __forceinline__ P pack(const float p[4]) {
+    return Tile16<IO, D>::pack(p);
+  }
+  static __device__ __forceinline__ float psum(P p) { return Tile16<IO, D>::psum(p); }
+  static __device__ __forceinline__ f32x4 pv(A4 a, P b, f32x4 c) { return O::pv(a, b, c); }
+  static __device__ __forceinline__ A4 zero_tail(A4 a, int jj, int nvalid) {
+    return Tile16<IO, D>::zero_tail(a, jj, nvalid);
+  }
+};
+
+// q/out and cache f32: 16x16x4 f32 MFMAs, one element per lane per step.
+template <int D>
+struct Tile32 {
+  typedef f32x4 A4;
+  typedef f32x4 P;
+  static constexpr int kK = D / 16;        // 16-byte K loads, four QK MFMAs each
+  static constexpr int kT = D / 16;        // V tiles (16-byte loads)
+  static constexpr int kStages = D == 128 ? 1 : 2;
+  struct Regs {
+    f32x4 k[kK];
+    f32x4 v[kT];
+  };
+  struct Q {
+    f32x4 c[kK];
+  };
+  static __device__ __forceinline__ uint32_t koff(int lane) { return lane * 16; }
+  static __device__ __forceinline__ uint32_t voff(int lane) { return (lane & 15) * 64 + (lane >> 4) * 16; }
+  static __device__ __forceinline__ void load_q(Q& q, gptr qrow, int jj, bool ok) {
+#pragma unroll
+    for (int c = 0; c < kK; ++c) {
+      const f32x4 raw = ld<f32x4>(qrow, 16 * (jj + 4 * c));   // head-dim 4*(jj + 4c) .. +3
+      q.c[c] = ok ? raw : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  }
+  static __device__ __forceinline__ void load(Regs& r, gptr kp, gptr vp,
+                                              uint32_t ko, uint32_t vo) {
+#pragma unroll
+    for (int i = 0; i < kK; ++i) r.k[i] = ld<f32x4>(kp, ko + i * 1024);
+#pragma unroll
+    for (int t = 0; t < kT; ++t) r.v[t] = ld<f32x4>(vp, vo + t * 1024);
+  }
+  static __device__ __forceinline__ f32x4 scores(const Regs& r, const Q& q) {
+    f32x4 s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < kK; ++c)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        s = __builtin_amdgcn_mfma_f32_16x16x4f32(r.k[c][e], q.c[c][e], s, 0, 0, 0);
+    return s;
+  }
+  static __device__ __forceinline__ A4 pvt(const Regs& r, int t) { return r.v[t]; }
+  static __device__ __forceinline__ P pack(const float p[4]) { return P{p[0], p[1], p[2], p[3]}; }
+  static __device__ __forceinline__ float psum(P p) { return (p[0] + p[1]) + (p[2] + p[3]); }
+  static __device__ __forceinline__ f32x4 pv(A4 a, P b, f32x4 c) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[e], b[e], c, 0, 0, 0);
+    return c;
+  }
+  static __device__ __forceinline__ A4 zero_tail(A4 a, int jj, int nvalid) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (4 * jj + i >= nvalid) a[i] = 0.0f;
+    return a;
+  }
+};
 
 template <typename IO, typename KV, int D>
-__device__ __forceinline__ void compute_page16(WaveState<D>& st, const PageRegs16<D, std::is_same<KV, IO>::value>& r,
-                                               const typename Op16<IO>::A8* qop, float cmul,
-                                               int nvalid, int lane) {
-  using O = Op16<IO>;
-  using A8 = typename O::A8;
-  using A4 = typename O::A4;
-  constexpr bool kv16 = std::is_same<KV, IO>::value;
-  const int jj = lane >> 4;
-  f32x4 s = {0.f, 0.f, 0.f, 0.f};
-  if constexpr (kv16) {
-#pragma unroll
-    for (int c = 0; c < D / 32; ++c) s = O::qk(bitcast16<A8>(r.k[c]), qop[c], s);
-  } else {
-#pragma unroll
-    for (int c = 0; c < D / 64; ++c) {
-      A4 a0 = O::fp8x4(r.k[c][0]), a1 = O::fp8x4(r.k[c][1]);
-      A4 a2 = O::fp8x4(r.k[c][2]), a3 = O::fp8x4(r.k[c][3]);
-      A8 lo = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
-      A8 hi = {a2[0], a2[1], a2[2], a2[3], a3[0], a3[1], a3[2], a3[3]};
-      s = O::qk(lo, qop[2 * c], s);
-      s = O::qk(hi, qop[2 * c + 1], s);
-    }
-  }
-  float alpha, p[4];
-  softmax_page(st.m, alpha, p, s, cmul, nvalid, jj);
-  A4 pk;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) pk[i] = (typename O::E)p[i];
-  const float ps = (O::out_f(pk[0]) + O::out_f(pk[1])) + (O::out_f(pk[2]) + O::out_f(pk[3]));
-  st.l = st.l * alpha + ps;
-  const bool partial = nvalid < kBlock;
-#pragma unroll
-  for (int t = 0; t < D / 16; ++t) {
-    A4 va;
-    if constexpr (kv16) {
-      va = __builtin_bit_cast(A4, r.v[t]);
-    } else {
-      va = O::fp8x4(r.v[t]);
-    }
-    if (partial) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (4 * jj + i >= nvalid) va[i] = (typename O::E)0.0f;
-    }
-    st.acc[t] = O::pv(va, pk, st.acc[t] * alpha);
-  }
-}
-
+struct TileOf {
+  typedef typename std::conditional<std::is_same<KV, FP8>::value, Tile8<IO, D>, Tile16<IO, D>>::type type;
+};
 template <int D>
-__device__ __forceinline__ void compute_page32(WaveState<D>& st, const PageRegs32<D>& r,
-                                               const f32x4* qop, float cmul, int nvalid,
-                                               int lane) {
-  const int jj = lane >> 4;
-  f32x4 s = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int c = 0; c < D / 16; ++c) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) s = __builtin_amdgcn_mfma_f32_16x16x4f32(r.k[c][e], qop[c][e], s, 0, 0, 0);
-  }
-  float alpha, p[4];
-  softmax_page(st.m, alpha, p, s, cmul, nvalid, jj);
-  st.l = st.l * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
-  const bool partial = nvalid < kBlock;
-#pragma unroll
-  for (int t = 0; t < D / 16; ++t) {
-    f32x4 va = r.v[t];
-    if (partial) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (4 * jj + i >= nvalid) va[i] = 0.0f;
-    }
-    f32x4 a = st.acc[t] * alpha;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) a = __builtin_amdgcn_mfma_f32_16x16x4f32(va[e], p[e], a, 0, 0, 0);
-    st.acc[t] = a;
-  }
-}
+struct TileOf<F32, F32, D> {
+  typedef Tile32<D> type;
+};
 
 // ---------------------------------------------------------------------------
-// Output conversion.
+// Output conversion and sizes.
 // ---------------------------------------------------------------------------
 template <typename IO>
 __device__ __forceinline__ void store_out(uint8_t* out, size_t idx, float x);
@@ -348,16 +388,9 @@ __device__ __forceinline__ void store_out<BF16>(uint8_t* out, size_t idx, float 
   reinterpret_cast<__bf16*>(out)[idx] = (__bf16)x;
 }
 
-template <typename IO>
-struct IoSize { static constexpr int v = 2; };
-template <>
-struct IoSize<F32> { static constexpr int v = 4; };
-template <typename KV>
-struct KvSize { static constexpr int v = 2; };
-template <>
-struct KvSize<F32> { static constexpr int v = 4; };
-template <>
-struct KvSize<FP8> { static constexpr int v = 1; };
+template <typename T> struct ElemSize { static constexpr int v = 2; };
+template <> struct ElemSize<F32> { static constexpr int v = 4; };
+template <> struct ElemSize<FP8> { static constexpr int v = 1; };
 
 // ---------------------------------------------------------------------------
 // LDS for the cross-wave merge and the cross-partition merge.
@@ -372,31 +405,31 @@ struct Smem {
 };
 
 // Merge the partitions of (b, g) stored in the workspace and write the final
-// output of its `group` query heads. Partitions are combined in a fixed order
-// (thread slice s takes p = s, s + S, ...; slices are then folded 0, 1, ...),
-// so the result does not depend on which workgroup finished last.
+// output of its query heads. Thread slice s folds partitions p = s, s + S, ...
+// with a running max; slices are then combined in order 0, 1, ..., so the
+// result does not depend on which workgroup finished last.
 template <typename IO, int D>
 __device__ void merge_partitions(const Params& a, Smem<D>& sm, int b, int g, int nparts) {
   constexpr int kQuads = D / 4;
   constexpr int kSlices = kThreads / kQuads;
   const int tid = threadIdx.x;
   const int dq = tid % kQuads, sl = tid / kQuads;
-  float* red = &sm.acc[0][0][0];            // [kSlices][D]
-  float* redm = &sm.m[0][0];                // [kSlices]
-  float* redw = &sm.l[0][0];                // [kSlices]
+  float* red = &sm.acc[0][0][0];   // [kSlices][D]
+  float* redm = &sm.m[0][0];       // [kSlices]
+  float* redw = &sm.l[0][0];       // [kSlices]
   for (int h = 0; h < a.group; ++h) {
-    const int hq = g * a.group + h;
-    const size_t row = (size_t)b * a.num_q_heads + hq;
+    const size_t row = (size_t)b * a.num_q_heads + g * a.group + h;
     const float* lse = a.ws_lse + row * a.p_max;
-    const f32x4* o = reinterpret_cast<const f32x4*>(a.ws_o + row * a.p_max * D);
+    const float* o = a.ws_o + row * a.p_max * D + 4 * dq;
     float mr = -INFINITY, wr = 0.f;
     f32x4 ar = {0.f, 0.f, 0.f, 0.f};
     for (int p = sl; p < nparts; p += kSlices) {
-      const float lp = lse[p];
-      const f32x4 op = o[(size_t)p * kQuads + dq];
+      const float lp = ld_agent(lse + p);
+      const float* op = o + (size_t)p * D;
+      const f32x4 ov = {ld_agent(op), ld_agent(op + 1), ld_agent(op + 2), ld_agent(op + 3)};
       const float mn = fmaxf(mr, lp);
       const float sa = exp2_fast(mr - mn), sb = exp2_fast(lp - mn);
-      ar = ar * sa + op * sb;
+      ar = ar * sa + ov * sb;
       wr = wr * sa + sb;
       mr = mn;
     }
@@ -428,12 +461,12 @@ __device__ void merge_partitions(const Params& a, Smem<D>& sm, int b, int g, int
 // The kernel.
 // ---------------------------------------------------------------------------
 template <typename IO, typename KV, int D>
-__global__ void __launch_bounds__(kThreads) pa_decode_kernel(const Params a) {
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3)))
+pa_decode_kernel(const Params a) {
+  using T = typename TileOf<IO, KV, D>::type;
   __shared__ Smem<D> sm;
-  constexpr bool kFam32 = std::is_same<IO, F32>::value;
   constexpr bool kFp8 = std::is_same<KV, FP8>::value;
-  constexpr int kEsz = KvSize<KV>::v;
-  constexpr size_t kPageBytes = (size_t)kBlock * D * kEsz;
+  constexpr size_t kPageBytes = (size_t)kBlock * D * ElemSize<KV>::v;
 
   const int p = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x;
@@ -464,10 +497,8 @@ __global__ void __launch_bounds__(kThreads) pa_decode_kernel(const Params a) {
   const int npages = (t1 - t0 + kBlock - 1) / kBlock;
   const int nmine = npages > w ? (npages - w + kWaves - 1) / kWaves : 0;
 
-  // Query operand: lane (rr, jj) feeds query head rr (zero beyond the group).
   const int rr = lane & 15, jj = lane >> 4;
   const bool head_ok = rr < G;
-  const uint8_t* qrow = a.q + ((size_t)b * a.num_q_heads + hq0 + (head_ok ? rr : 0)) * D * IoSize<IO>::v;
 
   float kmul = a.scale * kLog2e;
   float vmul = 1.0f;
@@ -476,117 +507,129 @@ __global__ void __launch_bounds__(kThreads) pa_decode_kernel(const Params a) {
     vmul = a.v_scale[g];
   }
 
-  const int32_t* bt = a.block_table + (size_t)b * a.max_blocks_per_seq + page0;
-  const uint8_t* kbase = a.k + (size_t)g * kPageBytes;
-  const uint8_t* vbase = a.v + (size_t)g * kPageBytes;
-  const size_t block_stride = (size_t)a.num_kv_heads * kPageBytes;
+  typename T::Q qop;
+  T::load_q(qop, (gptr)(a.q + ((size_t)b * a.num_q_heads + hq0 + (head_ok ? rr : 0)) * D * ElemSize<IO>::v),
+            jj, head_ok);
 
-  WaveState<D> st;
-  st.m = -INFINITY;
-  st.l = 0.f;
-#pragma unroll
-  for (int t = 0; t < D / 16; ++t) st.acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-  bool bad_blk = false;
-
-  // Block ids of this wave's pages: lane i holds page w + kWaves * (i + 64 * chunk).
-  int btv = 0;
+  // This wave's pages are w, w + kWaves, ...; lane i of btv holds the block id
+  // of the wave's page (i + 64 * chunk).
+  const int32_t* bt = a.block_table + (size_t)b * a.max_blocks_per_seq + page0 + w;
   auto fetch_bt = [&](int chunk) {
     const int i = chunk * 64 + lane;
-    btv = i < nmine ? bt[w + kWaves * i] : 0;
+    return i < nmine ? bt[kWaves * i] : 0;
   };
-  auto page_ptrs = [&](int i, const uint8_t*& kp, const uint8_t*& vp) {
-    int phys = __builtin_amdgcn_readlane(btv, i & 63);
+  int bt_cur = fetch_bt(0);
+  int bt_next = nmine > 64 ? fetch_bt(1) : 0;
+
+  const gptr kbase = uniform_ptr(a.k + (size_t)g * kPageBytes);
+  const gptr vbase = uniform_ptr(a.v + (size_t)g * kPageBytes);
+  const size_t block_stride = (size_t)a.num_kv_heads * kPageBytes;
+  const uint32_t ko = T::koff(lane), vo = T::voff(lane);
+  bool bad_blk = false;
+
+  auto issue = [&](typename T::Regs& r, int i) {
+    if (i > 0 && (i & 63) == 0) {
+      bt_cur = bt_next;
+      if (nmine > i + 64) bt_next = fetch_bt((i >> 6) + 1);
+    }
+    int phys = __builtin_amdgcn_readlane(bt_cur, i & 63);
     if ((unsigned)phys >= (unsigned)a.num_blocks) {
       bad_blk = true;
       phys = 0;
     }
-    kp = kbase + (size_t)phys * block_stride;
-    vp = vbase + (size_t)phys * block_stride;
+    const size_t off = (size_t)phys * block_stride;
+    T::load(r, kbase + off, vbase + off, ko, vo);
   };
-  auto nvalid_of = [&](int i) { return t1 - (t0 + (w + kWaves * i) * kBlock); };
 
-  if constexpr (!kFam32) {
-    using O = Op16<IO>;
-    using A8 = typename O::A8;
-    constexpr bool kv16 = !kFp8;
-    A8 qop[D / 32];
+  float m = -INFINITY, lsum = 0.f;
+  f32x4 acc[D / 16];
 #pragma unroll
-    for (int c = 0; c < D / 32; ++c) {
-      // d-slots of chunk c: 16-bit cache -> 8*(jj + 4c) + e;
-      // fp8 cache -> 16*(jj + 4*(c/2)) + 8*(c%2) + e.
-      const int d0 = kv16 ? 8 * (jj + 4 * c) : 16 * (jj + 4 * (c / 2)) + 8 * (c % 2);
-      u32x4 raw = *reinterpret_cast<const u32x4*>(qrow + d0 * 2);
-      if (!head_ok) raw = u32x4{0u, 0u, 0u, 0u};
-      qop[c] = bitcast16<A8>(raw);
+  for (int t = 0; t < D / 16; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // One page of the online softmax. kMasked: the page may end before its
+  // 16th token (only a wave's last page can).
+  auto compute = [&](const typename T::Regs& r, int i, auto masked_tag) {
+    constexpr bool kMasked = decltype(masked_tag)::value;
+    const f32x4 s = T::scores(r, qop);
+    int nvalid = kBlock;
+    float sc[4];
+    if constexpr (kMasked) {
+      nvalid = t1 - (t0 + (w + kWaves * i) * kBlock);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sc[e] = (4 * jj + e < nvalid) ? s[e] * kmul : -INFINITY;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sc[e] = s[e] * kmul;
     }
-    PageRegs16<D, kv16> ra, rb;
-    const uint8_t *kp, *vp;
-    if (nmine > 0) {
-      fetch_bt(0);
-      page_ptrs(0, kp, vp);
-      load_page16<D, kv16>(ra, kp, vp, lane);
+    const float mx = wave_max_rows(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])));
+    const float mnew = fmaxf(m, mx);
+    const float alpha = exp2_fast(m - mnew);
+    float pr[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) pr[e] = exp2_fast(sc[e] - mnew);
+    const typename T::P pk = T::pack(pr);
+    lsum = lsum * alpha + T::psum(pk);
+    m = mnew;
+    if (__any(alpha != 1.0f)) {
+#pragma unroll
+      for (int t = 0; t < D / 16; ++t) acc[t] *= alpha;
     }
-    for (int i = 0; i < nmine; i += 2) {
-      if (i + 1 < nmine) {
-        if (((i + 1) & 63) == 0) fetch_bt((i + 1) >> 6);
-        page_ptrs(i + 1, kp, vp);
-        load_page16<D, kv16>(rb, kp, vp, lane);
-      }
-      compute_page16<IO, KV, D>(st, ra, qop, kmul, nvalid_of(i), lane);
-      if (i + 1 < nmine) {
-        if (i + 2 < nmine) {
-          if (((i + 2) & 63) == 0) fetch_bt((i + 2) >> 6);
-          page_ptrs(i + 2, kp, vp);
-          load_page16<D, kv16>(ra, kp, vp, lane);
-        }
-        compute_page16<IO, KV, D>(st, rb, qop, kmul, nvalid_of(i + 1), lane);
-      }
+#pragma unroll
+    for (int t = 0; t < D / 16; ++t) {
+      typename T::A4 va = T::pvt(r, t);
+      if constexpr (kMasked) va = T::zero_tail(va, jj, nvalid);
+      acc[t] = T::pv(va, pk, acc[t]);
+    }
+  };
+  using Full = std::integral_constant<bool, false>;
+  using Tail = std::integral_constant<bool, true>;
+
+  // Register ring: page i + kStages - 1 is loading while page i is computed.
+  // The steady-state block issues unconditionally and never holds a wave's
+  // last page (the only one that can be partial); the peeled remainder
+  // (at most 2 * kStages - 2 pages) issues and masks as needed.
+  constexpr int kStages = T::kStages;
+  typename T::Regs ring[kStages];
+#pragma unroll
+  for (int u = 0; u < kStages - 1; ++u)
+    if (u < nmine) issue(ring[u], u);
+  int i0 = 0;
+  if constexpr (kStages == 1) {
+    for (; i0 < nmine; ++i0) {
+      issue(ring[0], i0);
+      compute(ring[0], i0, Tail{});
     }
   } else {
-    f32x4 qop[D / 16];
+    for (; i0 + 2 * kStages - 2 < nmine; i0 += kStages) {
 #pragma unroll
-    for (int c = 0; c < D / 16; ++c) {
-      f32x4 raw = *reinterpret_cast<const f32x4*>(qrow + (size_t)4 * (jj + 4 * c) * 4);
-      qop[c] = head_ok ? raw : f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-    PageRegs32<D> ra, rb;
-    const uint8_t *kp, *vp;
-    if (nmine > 0) {
-      fetch_bt(0);
-      page_ptrs(0, kp, vp);
-      load_page32<D>(ra, kp, vp, lane);
-    }
-    for (int i = 0; i < nmine; i += 2) {
-      if (i + 1 < nmine) {
-        if (((i + 1) & 63) == 0) fetch_bt((i + 1) >> 6);
-        page_ptrs(i + 1, kp, vp);
-        load_page32<D>(rb, kp, vp, lane);
+      for (int u = 0; u < kStages; ++u) {
+        issue(ring[(u + kStages - 1) % kStages], i0 + u + kStages - 1);
+        compute(ring[u], i0 + u, Full{});
       }
-      compute_page32<D>(st, ra, qop, kmul, nvalid_of(i), lane);
-      if (i + 1 < nmine) {
-        if (i + 2 < nmine) {
-          if (((i + 2) & 63) == 0) fetch_bt((i + 2) >> 6);
-          page_ptrs(i + 2, kp, vp);
-          load_page32<D>(ra, kp, vp, lane);
-        }
-        compute_page32<D>(st, rb, qop, kmul, nvalid_of(i + 1), lane);
+    }
+#pragma unroll
+    for (int u = 0; u < 2 * kStages - 2; ++u) {
+      const int i = i0 + u;
+      if (i < nmine) {
+        if (i + kStages - 1 < nmine) issue(ring[(u + kStages - 1) % kStages], i + kStages - 1);
+        compute(ring[u % kStages], i, Tail{});
       }
     }
   }
 
   // ---- merge the waves through LDS --------------------------------------
-  const float lsum = wave_sum_rows(st.l);
+  lsum = wave_sum_rows(lsum);
   if (tid == 0) sm.bad = 0;
   __syncthreads();
   if (bad_blk) sm.bad = 1;
   if (head_ok) {
     if (jj == 0) {
-      sm.m[w][rr] = st.m;
+      sm.m[w][rr] = m;
       sm.l[w][rr] = lsum;
     }
 #pragma unroll
     for (int t = 0; t < D / 16; ++t)
-      *reinterpret_cast<f32x4*>(&sm.acc[w][rr][16 * t + 4 * jj]) = st.acc[t];
+      *reinterpret_cast<f32x4*>(&sm.acc[w][rr][16 * t + 4 * jj]) = acc[t];
   }
   __syncthreads();
   const bool bad = sm.bad != 0;
@@ -612,29 +655,30 @@ __global__ void __launch_bounds__(kThreads) pa_decode_kernel(const Params a) {
       store_out<IO>(a.out, row * D + d, val);
       if (d == 0 && a.lse_out) a.lse_out[row] = lse2 * kLn2;
     } else {
-      a.ws_o[(row * a.p_max + p) * D + d] = val;
-      if (d == 0) a.ws_lse[row * a.p_max + p] = lse2;
+      st_agent(a.ws_o + (row * a.p_max + p) * D + d, val);
+      if (d == 0) st_agent(a.ws_lse + row * a.p_max + p, lse2);
     }
   }
   if (!split) return;
 
   // ---- split-K: the last partition of (b, g) to finish merges ------------
-  __threadfence();
+  // Every wave waits until its agent-coherent stores have completed before the
+  // barrier, so the counter increment is ordered after all of them.
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
+  uint32_t* cnt = a.ws_cnt + (size_t)b * a.num_kv_heads + g;
   if (tid == 0) {
-    uint32_t* cnt = a.ws_cnt + (size_t)b * a.num_kv_heads + g;
-    const uint32_t done = atomicAdd(cnt, 1u);
+    const uint32_t done = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     sm.last = done == (uint32_t)(nparts - 1);
   }
   __syncthreads();
   if (!sm.last) return;
-  __threadfence();
   merge_partitions<IO, D>(a, sm, b, g, nparts);
-  if (tid == 0) atomicExch(a.ws_cnt + (size_t)b * a.num_kv_heads + g, 0u);
+  if (tid == 0) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 __global__ void fill_zero_kernel(uint8_t* p, size_t n) {
-  size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   const size_t n16 = n / 16;
   for (size_t j = i; j < n16; j += (size_t)gridDim.x * blockDim.x)
     reinterpret_cast<u32x4*>(p)[j] = u32x4{0u, 0u, 0u, 0u};
@@ -737,9 +781,10 @@ pa_status pa_decode(const pa_shape* shape, const void* q, const void* k_cache,
   prm.out = static_cast<uint8_t*>(out);
   prm.lse_out = lse_out;
   uint8_t* ws = static_cast<uint8_t*>(workspace);
-  prm.ws_o = shape->partition_size > 0 ? reinterpret_cast<float*>(ws + wl.o_off) : nullptr;
-  prm.ws_lse = shape->partition_size > 0 ? reinterpret_cast<float*>(ws + wl.lse_off) : nullptr;
-  prm.ws_cnt = shape->partition_size > 0 ? reinterpret_cast<uint32_t*>(ws + wl.cnt_off) : nullptr;
+  const bool split = shape->partition_size > 0;
+  prm.ws_o = split ? reinterpret_cast<float*>(ws + wl.o_off) : nullptr;
+  prm.ws_lse = split ? reinterpret_cast<float*>(ws + wl.lse_off) : nullptr;
+  prm.ws_cnt = split ? reinterpret_cast<uint32_t*>(ws + wl.cnt_off) : nullptr;
   prm.scale = scale;
   prm.num_q_heads = shape->num_q_heads;
   prm.num_kv_heads = shape->num_kv_heads;

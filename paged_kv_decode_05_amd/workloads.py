@@ -228,3 +228,33 @@ def small_variant(spec, batch, lens, max_blocks_per_seq=None, name_suffix="small
     prefix = min(spec.shared_prefix_tokens, mbs * BLOCK_SIZE)
     return replace(spec, name=f"{spec.name}_{name_suffix}", batch=batch, lens=lens,
                    max_blocks_per_seq=mbs, shared_prefix_tokens=prefix)
+
+
+# ---------------------------------------------------------------------------
+# Upload to device tensors (storage bits unchanged).
+
+def storage_tensor(raw, dtype):
+    """A torch CPU tensor over the storage bits, typed for the binding."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(raw))
+    if dtype == "f32":
+        return t
+    if dtype in ("f16", "bf16"):
+        return t.view(torch.int16).view(torch.float16 if dtype == "f16" else torch.bfloat16)
+    if dtype == "fp8_e4m3":
+        return t.view(torch.uint8)
+    raise ValueError(dtype)
+
+
+def to_device(wl, device="cuda:0"):
+    import torch
+    s = wl.spec
+    return {
+        "q": storage_tensor(wl.q, s.io_dtype).to(device),
+        "k_cache": storage_tensor(wl.k_cache, s.kv_dtype).to(device),
+        "v_cache": storage_tensor(wl.v_cache, s.kv_dtype).to(device),
+        "block_table": torch.from_numpy(wl.block_table).to(device),
+        "context_lens": torch.from_numpy(wl.context_lens).to(device),
+        "k_scale": None if wl.k_scale is None else torch.from_numpy(wl.k_scale).to(device),
+        "v_scale": None if wl.v_scale is None else torch.from_numpy(wl.v_scale).to(device),
+    }
