@@ -83,6 +83,7 @@ struct Params {
   float* ws_lse;     // [B][Hq][p_max]   base 2, in units of the scaled scores
   uint32_t* ws_cnt;  // [B][Hkv]
   float scale;
+  int32_t batch;
   int32_t num_q_heads;
   int32_t num_kv_heads;
   int32_t group;
@@ -405,54 +406,84 @@ struct Smem {
 };
 
 // Merge the partitions of (b, g) stored in the workspace and write the final
-// output of its query heads. Thread slice s folds partitions p = s, s + S, ...
-// with a running max; slices are then combined in order 0, 1, ..., so the
-// result does not depend on which workgroup finished last.
+// output of its query heads. Threads take (head, 4-float quad) pairs; when the
+// group leaves threads over, S slices split the partitions (slice s takes
+// p = s, s + S, ...). Every thread issues the loads of 8 partitions before
+// folding them with a running max, and slices are combined in order 0, 1, ...,
+// so the result does not depend on which workgroup finished last.
 template <typename IO, int D>
 __device__ void merge_partitions(const Params& a, Smem<D>& sm, int b, int g, int nparts) {
   constexpr int kQuads = D / 4;
-  constexpr int kSlices = kThreads / kQuads;
+  constexpr int kBatch = 8;
   const int tid = threadIdx.x;
-  const int dq = tid % kQuads, sl = tid / kQuads;
-  float* red = &sm.acc[0][0][0];   // [kSlices][D]
-  float* redm = &sm.m[0][0];       // [kSlices]
-  float* redw = &sm.l[0][0];       // [kSlices]
-  for (int h = 0; h < a.group; ++h) {
+  const int npair = a.group * kQuads;
+  const int S = npair >= kThreads ? 1 : kThreads / npair;
+  for (int base = 0; base < npair * S; base += kThreads) {
+    const int idx = base + tid;
+    const bool active = idx < npair * S;
+    const int pair = idx % npair, sl = idx / npair;
+    const int h = pair / kQuads, dq = pair % kQuads;
     const size_t row = (size_t)b * a.num_q_heads + g * a.group + h;
     const float* lse = a.ws_lse + row * a.p_max;
     const float* o = a.ws_o + row * a.p_max * D + 4 * dq;
     float mr = -INFINITY, wr = 0.f;
     f32x4 ar = {0.f, 0.f, 0.f, 0.f};
-    for (int p = sl; p < nparts; p += kSlices) {
-      const float lp = ld_agent(lse + p);
-      const float* op = o + (size_t)p * D;
-      const f32x4 ov = {ld_agent(op), ld_agent(op + 1), ld_agent(op + 2), ld_agent(op + 3)};
-      const float mn = fmaxf(mr, lp);
-      const float sa = exp2_fast(mr - mn), sb = exp2_fast(lp - mn);
-      ar = ar * sa + ov * sb;
-      wr = wr * sa + sb;
-      mr = mn;
-    }
-    __syncthreads();
-    *reinterpret_cast<f32x4*>(&red[sl * D + 4 * dq]) = ar;
-    if (dq == 0) {
-      redm[sl] = mr;
-      redw[sl] = wr;
-    }
-    __syncthreads();
-    if (tid < D) {
-      float M = -INFINITY;
+    if (active) {
+      for (int p0 = sl; p0 < nparts; p0 += kBatch * S) {
+        float lp[kBatch];
+        f32x4 ov[kBatch];
 #pragma unroll
-      for (int s = 0; s < kSlices; ++s) M = fmaxf(M, redm[s]);
-      float W = 0.f, acc = 0.f;
+        for (int u = 0; u < kBatch; ++u) {
+          const int p = p0 + u * S;
+          if (p < nparts) {
+            const float* op = o + (size_t)p * D;
+            lp[u] = ld_agent(lse + p);
+            ov[u] = f32x4{ld_agent(op), ld_agent(op + 1), ld_agent(op + 2), ld_agent(op + 3)};
+          }
+        }
 #pragma unroll
-      for (int s = 0; s < kSlices; ++s) {
-        const float e = exp2_fast(redm[s] - M);
-        W += e * redw[s];
-        acc += e * red[s * D + tid];
+        for (int u = 0; u < kBatch; ++u) {
+          if (p0 + u * S < nparts) {
+            const float mn = fmaxf(mr, lp[u]);
+            const float sa = exp2_fast(mr - mn), sb = exp2_fast(lp[u] - mn);
+            ar = ar * sa + ov[u] * sb;
+            wr = wr * sa + sb;
+            mr = mn;
+          }
+        }
       }
-      store_out<IO>(a.out, row * D + tid, acc / W);
-      if (tid == 0 && a.lse_out) a.lse_out[row] = (M + log2_fast(W)) * kLn2;
+    }
+    if (S > 1) {
+      // npair * S <= kThreads: one pass, every thread is here.
+      float* red = &sm.acc[0][0][0];   // [S][npair] quads, then m, then w
+      float* redm = red + 4 * npair * S;
+      float* redw = redm + npair * S;
+      if (active) {
+        *reinterpret_cast<f32x4*>(&red[4 * idx]) = ar;
+        redm[idx] = mr;
+        redw[idx] = wr;
+      }
+      __syncthreads();
+      if (active && sl == 0) {
+        float M = -INFINITY;
+        for (int s2 = 0; s2 < S; ++s2) M = fmaxf(M, redm[s2 * npair + pair]);
+        float W = 0.f;
+        f32x4 A = {0.f, 0.f, 0.f, 0.f};
+        for (int s2 = 0; s2 < S; ++s2) {
+          const int j = s2 * npair + pair;
+          const float e = exp2_fast(redm[j] - M);
+          W += e * redw[j];
+          A += e * *reinterpret_cast<const f32x4*>(&red[4 * j]);
+        }
+        mr = M;
+        wr = W;
+        ar = A;
+      }
+    }
+    if (active && sl == 0) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) store_out<IO>(a.out, row * D + 4 * dq + e, ar[e] / wr);
+      if (dq == 0 && a.lse_out) a.lse_out[row] = (mr + log2_fast(wr)) * kLn2;
     }
   }
 }
@@ -468,16 +499,39 @@ pa_decode_kernel(const Params a) {
   constexpr bool kFp8 = std::is_same<KV, FP8>::value;
   constexpr size_t kPageBytes = (size_t)kBlock * D * ElemSize<KV>::v;
 
-  const int p = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  // Work unit of this workgroup. Units are numbered partition-major,
+  // unit = p * (B * Hkv) + b * Hkv + g, because the hardware hands
+  // consecutive workgroups to the eight XCDs in turn: every XCD then gets an
+  // even share of each partition level, whose population shrinks with p.
+  const int nbg = a.batch * a.num_kv_heads;
+  const int p = blockIdx.x / nbg;
+  const int bg = blockIdx.x - p * nbg;
+  const int b = bg / a.num_kv_heads, g = bg - b * a.num_kv_heads;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int G = a.group;
   const int hq0 = g * G;
 
+  const int PT = a.part_tokens;
+  const int page0 = PT > 0 ? p * (PT / kBlock) : 0;
+  const int rr = lane & 15, jj = lane >> 4;
+  const bool head_ok = rr < G;
+
+  // Issued before the context length is known (all indices stay in bounds):
+  // the block ids of this wave's first 64 pages and the query operand.
+  const int32_t* bt = a.block_table + (size_t)b * a.max_blocks_per_seq + w;
+  const int bt_last = a.max_blocks_per_seq - 1 - w;
+  auto fetch_bt = [&](int chunk) {
+    return bt[min(page0 + kWaves * (chunk * 64 + lane), bt_last)];
+  };
+  int bt_cur = fetch_bt(0);
+  typename T::Q qop;
+  T::load_q(qop, (gptr)(a.q + ((size_t)b * a.num_q_heads + hq0 + (head_ok ? rr : 0)) * D * ElemSize<IO>::v),
+            jj, head_ok);
+
   const int L = a.context_lens[b];
   const bool bad_len = L < 0 || L > a.max_blocks_per_seq * kBlock;
-  const int PT = a.part_tokens;
   const int nparts = (bad_len || L == 0) ? 1 : (PT > 0 ? (L + PT - 1) / PT : 1);
   if (p >= nparts) return;
 
@@ -493,12 +547,8 @@ pa_decode_kernel(const Params a) {
 
   const int t0 = PT > 0 ? p * PT : 0;
   const int t1 = PT > 0 ? min(t0 + PT, L) : L;
-  const int page0 = t0 / kBlock;
   const int npages = (t1 - t0 + kBlock - 1) / kBlock;
   const int nmine = npages > w ? (npages - w + kWaves - 1) / kWaves : 0;
-
-  const int rr = lane & 15, jj = lane >> 4;
-  const bool head_ok = rr < G;
 
   float kmul = a.scale * kLog2e;
   float vmul = 1.0f;
@@ -507,18 +557,6 @@ pa_decode_kernel(const Params a) {
     vmul = a.v_scale[g];
   }
 
-  typename T::Q qop;
-  T::load_q(qop, (gptr)(a.q + ((size_t)b * a.num_q_heads + hq0 + (head_ok ? rr : 0)) * D * ElemSize<IO>::v),
-            jj, head_ok);
-
-  // This wave's pages are w, w + kWaves, ...; lane i of btv holds the block id
-  // of the wave's page (i + 64 * chunk).
-  const int32_t* bt = a.block_table + (size_t)b * a.max_blocks_per_seq + page0 + w;
-  auto fetch_bt = [&](int chunk) {
-    const int i = chunk * 64 + lane;
-    return i < nmine ? bt[kWaves * i] : 0;
-  };
-  int bt_cur = fetch_bt(0);
   int bt_next = nmine > 64 ? fetch_bt(1) : 0;
 
   const gptr kbase = uniform_ptr(a.k + (size_t)g * kPageBytes);
@@ -706,6 +744,10 @@ static bool shape_ok(const pa_shape* s) {
   if (s->max_blocks_per_seq < 1 || s->max_blocks_per_seq > (1 << 26)) return false;
   if (s->num_blocks < 1) return false;
   if (s->partition_size < 0 || s->partition_size % kBlock != 0) return false;
+  // work units B * Hkv * partitions must fit a 1-D grid
+  const long long parts =
+      s->partition_size ? ((long long)s->max_blocks_per_seq * kBlock + s->partition_size - 1) / s->partition_size : 1;
+  if ((long long)s->batch * s->num_kv_heads * parts > 0x7fffffffLL) return false;
   return true;
 }
 
@@ -786,6 +828,7 @@ pa_status pa_decode(const pa_shape* shape, const void* q, const void* k_cache,
   prm.ws_lse = split ? reinterpret_cast<float*>(ws + wl.lse_off) : nullptr;
   prm.ws_cnt = split ? reinterpret_cast<uint32_t*>(ws + wl.cnt_off) : nullptr;
   prm.scale = scale;
+  prm.batch = shape->batch;
   prm.num_q_heads = shape->num_q_heads;
   prm.num_kv_heads = shape->num_kv_heads;
   prm.group = shape->num_q_heads / shape->num_kv_heads;
@@ -794,7 +837,9 @@ pa_status pa_decode(const pa_shape* shape, const void* q, const void* k_cache,
   prm.part_tokens = shape->partition_size;
   prm.p_max = wl.p_max;
 
-  const dim3 grid(wl.p_max, shape->num_kv_heads, shape->batch);
+  // 1-D grid of work units (see the kernel)
+  const long long nbg = (long long)shape->batch * shape->num_kv_heads;
+  const dim3 grid((unsigned)(nbg * wl.p_max), 1, 1);
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t e;
   const int D = shape->head_dim;
