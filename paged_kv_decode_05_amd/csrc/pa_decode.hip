@@ -491,22 +491,15 @@ __device__ void merge_partitions(const Params& a, Smem<D>& sm, int b, int g, int
 // ---------------------------------------------------------------------------
 // The kernel.
 // ---------------------------------------------------------------------------
+// One work unit: partition p of sequence b for KV head g, by the whole
+// workgroup. Control flow is uniform across the workgroup.
 template <typename IO, typename KV, int D>
-__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3)))
-pa_decode_kernel(const Params a) {
+__device__ __forceinline__ void decode_unit(const Params& a, Smem<D>& sm, const int p, const int b,
+                                            const int g) {
   using T = typename TileOf<IO, KV, D>::type;
-  __shared__ Smem<D> sm;
   constexpr bool kFp8 = std::is_same<KV, FP8>::value;
   constexpr size_t kPageBytes = (size_t)kBlock * D * ElemSize<KV>::v;
 
-  // Work unit of this workgroup. Units are numbered partition-major,
-  // unit = p * (B * Hkv) + b * Hkv + g, because the hardware hands
-  // consecutive workgroups to the eight XCDs in turn: every XCD then gets an
-  // even share of each partition level, whose population shrinks with p.
-  const int nbg = a.batch * a.num_kv_heads;
-  const int p = blockIdx.x / nbg;
-  const int bg = blockIdx.x - p * nbg;
-  const int b = bg / a.num_kv_heads, g = bg - b * a.num_kv_heads;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -710,9 +703,24 @@ pa_decode_kernel(const Params a) {
     sm.last = done == (uint32_t)(nparts - 1);
   }
   __syncthreads();
-  if (!sm.last) return;
+  if (!__builtin_amdgcn_readfirstlane(sm.last)) return;   // uniform: a scalar branch
   merge_partitions<IO, D>(a, sm, b, g, nparts);
   if (tid == 0) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <typename IO, typename KV, int D>
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3)))
+pa_decode_kernel(const Params a) {
+  __shared__ Smem<D> sm;
+  // Work units are numbered partition-major, unit = p * (B * Hkv) + b * Hkv
+  // + g, because the hardware hands consecutive workgroups to the eight XCDs
+  // in turn: every XCD then gets an even share of each partition level, whose
+  // population shrinks with p.
+  const int nbg = a.batch * a.num_kv_heads;
+  const int p = blockIdx.x / nbg;
+  const int bg = blockIdx.x - p * nbg;
+  const int b = bg / a.num_kv_heads;
+  decode_unit<IO, KV, D>(a, sm, p, b, bg - b * a.num_kv_heads);
 }
 
 __global__ void fill_zero_kernel(uint8_t* p, size_t n) {
