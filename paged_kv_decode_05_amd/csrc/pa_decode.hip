@@ -398,7 +398,9 @@ template <> struct ElemSize<FP8> { static constexpr int v = 1; };
 // ---------------------------------------------------------------------------
 template <int D>
 struct Smem {
-  float acc[kWaves][kMaxGroup][D];
+  // rows padded by 4 floats: the waves' float4 row writes (rows of 16 heads)
+  // then fall on distinct LDS banks
+  float acc[kWaves][kMaxGroup][D + 4];
   float m[kWaves][kMaxGroup];
   float l[kWaves][kMaxGroup];
   int bad;
