@@ -16,8 +16,9 @@
 //      addresses are wave-uniform scalars),
 //   2. loads the K page and the V page straight from HBM into registers in the
 //      layout the matrix cores consume (the cache layouts in padecode.h make
-//      every one of these loads a contiguous run); loads run one to three
-//      pages ahead of the math through a ring of register buffers,
+//      every one of these loads a contiguous run); K loads run two or three
+//      pages ahead of the math and V loads one page ahead, through rings of
+//      register buffers,
 //   3. computes S^T[token][head] = K Q^T for the whole GQA group with MFMA
 //      (query heads padded to 16 columns),
 //   4. masks tokens past the unit's end, updates the running max and sum in
@@ -92,6 +93,8 @@ struct Params {
   int32_t part_tokens;  // 0: whole sequence in one unit
   int32_t p_max;
 };
+
+constexpr int gcd_c(int x, int y) { return y == 0 ? x : gcd_c(y, x % y); }
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float log2_fast(float x) { return __builtin_amdgcn_logf(x); }
@@ -185,7 +188,7 @@ struct Op16<BF16> {
 // ---------------------------------------------------------------------------
 // Page tiles: what one wave holds of one page and how it feeds the MFMAs.
 //   kKoff / kVoff: per-lane byte offsets inside a K / V page (loop constants)
-//   load(): issue the page's loads;  scores(): S^T for the page;
+//   load_k()/load_v(): issue the page's K / V loads;  scores(): S^T for the page;
 //   pvt(): the V^T operand of tile t (4 tokens of row 16*t + r).
 // ---------------------------------------------------------------------------
 
@@ -198,9 +201,14 @@ struct Tile16 {
   typedef A4 P;                            // PV B operand: 4 rounded probabilities
   static constexpr int kK = D / 32;        // 16-byte K loads = QK MFMAs
   static constexpr int kT = D / 16;        // V tiles (8-byte loads)
-  static constexpr int kStages = D == 128 ? 2 : 3;   // register ring depth
-  struct Regs {
+  // register ring depths (pages in flight per wave for K and for V); a third
+  // K stage at D = 128 does not fit in the 168 VGPRs of 3 waves per SIMD
+  static constexpr int kKStages = D == 128 ? 2 : 4;
+  static constexpr int kVStages = 2;
+  struct KRegs {
     u32x4 k[kK];
+  };
+  struct VRegs {
     u32x2 v[kT];
   };
   struct Q {
@@ -216,20 +224,21 @@ struct Tile16 {
       q.c[c] = __builtin_bit_cast(A8, raw);
     }
   }
-  static __device__ __forceinline__ void load(Regs& r, gptr kp, gptr vp,
-                                              uint32_t ko, uint32_t vo) {
+  static __device__ __forceinline__ void load_k(KRegs& r, gptr kp, uint32_t ko) {
 #pragma unroll
     for (int i = 0; i < kK; ++i) r.k[i] = ld<u32x4>(kp, ko + i * 1024);
+  }
+  static __device__ __forceinline__ void load_v(VRegs& r, gptr vp, uint32_t vo) {
 #pragma unroll
     for (int t = 0; t < kT; ++t) r.v[t] = ld<u32x2>(vp, vo + t * 512);
   }
-  static __device__ __forceinline__ f32x4 scores(const Regs& r, const Q& q) {
+  static __device__ __forceinline__ f32x4 scores(const KRegs& r, const Q& q) {
     f32x4 s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int c = 0; c < kK; ++c) s = O::qk(__builtin_bit_cast(A8, r.k[c]), q.c[c], s);
     return s;
   }
-  static __device__ __forceinline__ A4 pvt(const Regs& r, int t) {
+  static __device__ __forceinline__ A4 pvt(const VRegs& r, int t) {
     return __builtin_bit_cast(A4, r.v[t]);
   }
   static __device__ __forceinline__ P pack(const float p[4]) {
@@ -256,9 +265,12 @@ struct Tile8 {
   typedef A4 P;
   static constexpr int kK = D / 64;        // 16-byte K loads, two QK MFMAs each
   static constexpr int kT = D / 16;        // V tiles (4-byte loads)
-  static constexpr int kStages = D == 128 ? 3 : 4;
-  struct Regs {
+  static constexpr int kKStages = 4;
+  static constexpr int kVStages = 2;
+  struct KRegs {
     u32x4 k[kK];
+  };
+  struct VRegs {
     uint32_t v[kT];
   };
   struct Q {
@@ -275,14 +287,15 @@ struct Tile8 {
       q.c[c] = __builtin_bit_cast(A8, raw);
     }
   }
-  static __device__ __forceinline__ void load(Regs& r, gptr kp, gptr vp,
-                                              uint32_t ko, uint32_t vo) {
+  static __device__ __forceinline__ void load_k(KRegs& r, gptr kp, uint32_t ko) {
 #pragma unroll
     for (int i = 0; i < kK; ++i) r.k[i] = ld<u32x4>(kp, ko + i * 1024);
+  }
+  static __device__ __forceinline__ void load_v(VRegs& r, gptr vp, uint32_t vo) {
 #pragma unroll
     for (int t = 0; t < kT; ++t) r.v[t] = ld<uint32_t>(vp, vo + t * 256);
   }
-  static __device__ __forceinline__ f32x4 scores(const Regs& r, const Q& q) {
+  static __device__ __forceinline__ f32x4 scores(const KRegs& r, const Q& q) {
     f32x4 s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int c = 0; c < kK; ++c) {
@@ -295,7 +308,7 @@ struct Tile8 {
     }
     return s;
   }
-  static __device__ __forceinline__ A4 pvt(const Regs& r, int t) { return O::fp8x4(r.v[t]); }
+  static __device__ __forceinline__ A4 pvt(const VRegs& r, int t) { return O::fp8x4(r.v[t]); }
   static __device__ __forceinline__ P pack(const float p[4]) {
     return Tile16<IO, D>::pack(p);
   }
@@ -313,9 +326,12 @@ struct Tile32 {
   typedef f32x4 P;
   static constexpr int kK = D / 16;        // 16-byte K loads, four QK MFMAs each
   static constexpr int kT = D / 16;        // V tiles (16-byte loads)
-  static constexpr int kStages = D == 128 ? 1 : 2;
-  struct Regs {
+  static constexpr int kKStages = D == 128 ? 1 : 2;
+  static constexpr int kVStages = D == 128 ? 1 : 2;
+  struct KRegs {
     f32x4 k[kK];
+  };
+  struct VRegs {
     f32x4 v[kT];
   };
   struct Q {
@@ -330,14 +346,15 @@ struct Tile32 {
       q.c[c] = ok ? raw : f32x4{0.f, 0.f, 0.f, 0.f};
     }
   }
-  static __device__ __forceinline__ void load(Regs& r, gptr kp, gptr vp,
-                                              uint32_t ko, uint32_t vo) {
+  static __device__ __forceinline__ void load_k(KRegs& r, gptr kp, uint32_t ko) {
 #pragma unroll
     for (int i = 0; i < kK; ++i) r.k[i] = ld<f32x4>(kp, ko + i * 1024);
+  }
+  static __device__ __forceinline__ void load_v(VRegs& r, gptr vp, uint32_t vo) {
 #pragma unroll
     for (int t = 0; t < kT; ++t) r.v[t] = ld<f32x4>(vp, vo + t * 1024);
   }
-  static __device__ __forceinline__ f32x4 scores(const Regs& r, const Q& q) {
+  static __device__ __forceinline__ f32x4 scores(const KRegs& r, const Q& q) {
     f32x4 s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int c = 0; c < kK; ++c)
@@ -346,7 +363,7 @@ struct Tile32 {
         s = __builtin_amdgcn_mfma_f32_16x16x4f32(r.k[c][e], q.c[c][e], s, 0, 0, 0);
     return s;
   }
-  static __device__ __forceinline__ A4 pvt(const Regs& r, int t) { return r.v[t]; }
+  static __device__ __forceinline__ A4 pvt(const VRegs& r, int t) { return r.v[t]; }
   static __device__ __forceinline__ P pack(const float p[4]) { return P{p[0], p[1], p[2], p[3]}; }
   static __device__ __forceinline__ float psum(P p) { return (p[0] + p[1]) + (p[2] + p[3]); }
   static __device__ __forceinline__ f32x4 pv(A4 a, P b, f32x4 c) {
@@ -560,7 +577,20 @@ __device__ __forceinline__ void decode_unit(const Params& a, Smem<D>& sm, const 
   const uint32_t ko = T::koff(lane), vo = T::voff(lane);
   bool bad_blk = false;
 
-  auto issue = [&](typename T::Regs& r, int i) {
+  // Register rings: K pages are loaded kKS - 1 pages ahead of the page being
+  // computed, V pages kVS - 1 ahead (V is needed only after the softmax).
+  // poff[] keeps each K slot's page offset so the later V load of the same
+  // page reuses it.
+  constexpr int kKS = T::kKStages, kVS = T::kVStages;
+  constexpr int dK = kKS - 1, dV = kVS - 1;
+  static_assert(kKS >= 1 && kVS >= 1 && dV <= dK, "ring depths");
+  // the steady-state block must stop short of a wave's last page
+  constexpr int kAhead = dK > 1 ? dK : 1;
+  typename T::KRegs ring_k[kKS];
+  typename T::VRegs ring_v[kVS];
+  size_t poff[kKS];
+
+  auto issue_k = [&](int slot, int i) {
     if (i > 0 && (i & 63) == 0) {
       bt_cur = bt_next;
       if (nmine > i + 64) bt_next = fetch_bt((i >> 6) + 1);
@@ -570,9 +600,10 @@ __device__ __forceinline__ void decode_unit(const Params& a, Smem<D>& sm, const 
       bad_blk = true;
       phys = 0;
     }
-    const size_t off = (size_t)phys * block_stride;
-    T::load(r, kbase + off, vbase + off, ko, vo);
+    poff[slot] = (size_t)phys * block_stride;
+    T::load_k(ring_k[slot], kbase + poff[slot], ko);
   };
+  auto issue_v = [&](int vslot, int kslot) { T::load_v(ring_v[vslot], vbase + poff[kslot], vo); };
 
   float m = -INFINITY, lsum = 0.f;
   f32x4 acc[D / 16];
@@ -581,9 +612,9 @@ __device__ __forceinline__ void decode_unit(const Params& a, Smem<D>& sm, const 
 
   // One page of the online softmax. kMasked: the page may end before its
   // 16th token (only a wave's last page can).
-  auto compute = [&](const typename T::Regs& r, int i, auto masked_tag) {
+  auto compute = [&](int kslot, int vslot, int i, auto masked_tag) {
     constexpr bool kMasked = decltype(masked_tag)::value;
-    const f32x4 s = T::scores(r, qop);
+    const f32x4 s = T::scores(ring_k[kslot], qop);
     int nvalid = kBlock;
     float sc[4];
     if constexpr (kMasked) {
@@ -609,7 +640,7 @@ __device__ __forceinline__ void decode_unit(const Params& a, Smem<D>& sm, const 
     }
 #pragma unroll
     for (int t = 0; t < D / 16; ++t) {
-      typename T::A4 va = T::pvt(r, t);
+      typename T::A4 va = T::pvt(ring_v[vslot], t);
       if constexpr (kMasked) va = T::zero_tail(va, jj, nvalid);
       acc[t] = T::pv(va, pk, acc[t]);
     }
@@ -617,36 +648,32 @@ __device__ __forceinline__ void decode_unit(const Params& a, Smem<D>& sm, const 
   using Full = std::integral_constant<bool, false>;
   using Tail = std::integral_constant<bool, true>;
 
-  // Register ring: page i + kStages - 1 is loading while page i is computed.
-  // The steady-state block issues unconditionally and never holds a wave's
-  // last page (the only one that can be partial); the peeled remainder
-  // (at most 2 * kStages - 2 pages) issues and masks as needed.
-  constexpr int kStages = T::kStages;
-  typename T::Regs ring[kStages];
+  // The steady-state block (kU = lcm(kKS, kVS) pages) issues unconditionally
+  // and never holds a wave's last page (the only one that can be partial);
+  // the peeled remainder issues and masks as needed.
+  constexpr int kU = kKS * kVS / gcd_c(kKS, kVS);
 #pragma unroll
-  for (int u = 0; u < kStages - 1; ++u)
-    if (u < nmine) issue(ring[u], u);
+  for (int j = 0; j < dK; ++j)
+    if (j < nmine) issue_k(j, j);
+#pragma unroll
+  for (int j = 0; j < dV; ++j)
+    if (j < nmine) issue_v(j, j);
   int i0 = 0;
-  if constexpr (kStages == 1) {
-    for (; i0 < nmine; ++i0) {
-      issue(ring[0], i0);
-      compute(ring[0], i0, Tail{});
-    }
-  } else {
-    for (; i0 + 2 * kStages - 2 < nmine; i0 += kStages) {
+  for (; i0 + kU - 1 + kAhead < nmine; i0 += kU) {
 #pragma unroll
-      for (int u = 0; u < kStages; ++u) {
-        issue(ring[(u + kStages - 1) % kStages], i0 + u + kStages - 1);
-        compute(ring[u], i0 + u, Full{});
-      }
+    for (int u = 0; u < kU; ++u) {
+      issue_k((u + dK) % kKS, i0 + u + dK);
+      issue_v((u + dV) % kVS, (u + dV) % kKS);
+      compute(u % kKS, u % kVS, i0 + u, Full{});
     }
+  }
 #pragma unroll
-    for (int u = 0; u < 2 * kStages - 2; ++u) {
-      const int i = i0 + u;
-      if (i < nmine) {
-        if (i + kStages - 1 < nmine) issue(ring[(u + kStages - 1) % kStages], i + kStages - 1);
-        compute(ring[u % kStages], i, Tail{});
-      }
+  for (int u = 0; u < kU + kAhead; ++u) {
+    const int i = i0 + u;
+    if (i < nmine) {
+      if (i + dK < nmine) issue_k((u + dK) % kKS, i + dK);
+      if (i + dV < nmine) issue_v((u + dV) % kVS, (u + dV) % kKS);
+      compute(u % kKS, u % kVS, i, Tail{});
     }
   }
 

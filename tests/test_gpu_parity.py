@@ -269,3 +269,17 @@ def test_out_of_contract_metadata_gives_nan_not_a_fault():
     got = to_f64(run(wl, t))
     assert np.isnan(got[0]).all() and np.isnan(got[1]).all()
     check(wl, got, ref(wl), seqs=[2], label="badmeta-ok-seq")
+
+
+@pytest.mark.parametrize("io,kv", [("f16", "f16"), ("bf16", "bf16"), ("f16", "fp8_e4m3"),
+                                   ("f32", "f32")])
+@pytest.mark.parametrize("ps", [0, 8192])
+def test_long_units_cross_block_id_chunks(io, kv, ps):
+    # A wave reads block ids 64 pages at a time; units of up to 9000 tokens
+    # give each wave up to 141 pages, so the chunk refresh runs while K and V
+    # loads for neighbouring pages are in flight.
+    spec = W.Spec(f"long_{io}_{kv}_ps{ps}", 4, 8, 2, 128, io, kv,
+                  ("fixed", [9000, 4097, 4096, 6100]), 563, ("ratio", 1.2), ps, 0, 31)
+    print(f"case {spec.name}", flush=True)
+    wl = W.make_workload(spec)
+    check(wl, to_f64(run(wl)), ref(wl), label=spec.name)
