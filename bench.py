@@ -5,12 +5,18 @@ sequence-tokens per second.
 One step is one pa_decode call (one kernel launch) over the whole batch of the
 Qwen2.5-7B-shaped workload: 32 sequences, 28 query / 4 KV heads, head_dim 128,
 f16 q/K/V, context lengths uniform in [512, 4096], 16-token blocks shuffled
-over the pool, split-K partitions of 512 tokens merged by log-sum-exp
-(`--workload` picks one of the other four for information). Inputs are
-resident in HBM before timing starts. Calls rotate over enough copies of the
-KV pool (>= 3 x 256 MiB) that the 256 MiB Infinity Cache cannot serve repeats.
+over the pool, split-K pieces merged by log-sum-exp (`--workload` picks one of
+the other four for information). Inputs are resident in HBM before timing
+starts. Calls rotate over enough copies of the KV pool (>= 3 x 256 MiB) that
+the 256 MiB Infinity Cache cannot serve repeats.
 
-    python bench.py [--steps K] [--warmup W] [--workload 1..5]
+Two ways of splitting the work are timed, each over K calls: the balanced
+split (equal page shares per workgroup; `value`, unless --split spec) and the
+workload's own partitioning (512-token partitions for workloads 3-5, one pass
+for 1-2), reported under "modes". Both compute the same result up to float
+rounding and meet the same parity bar.
+
+    python bench.py [--steps K] [--warmup W] [--workload 1..5] [--split balanced|spec]
 
 Prints one JSON line. `value` is KV-read GB/s: the K and V bytes of every
 (sequence, cached token, KV head) the call attends, divided by the time per
@@ -44,6 +50,11 @@ def parse():
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", type=int, default=3, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--split", choices=["balanced", "spec"], default="balanced",
+                    help="mode reported as `value`: the balanced split, or the "
+                         "workload's own partition size")
+    ap.add_argument("--partition-size", type=int, default=None,
+                    help="time only this partition size (0 = one pass, -1 = balanced)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="minimum host time spent timing the oracle")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -59,10 +70,14 @@ def kernel_sha256():
         return hashlib.sha256(f.read()).hexdigest()
 
 
-def traffic_from_profile(wl_name):
+def mode_name(ps):
+    return {0: "one_pass", -1: "balanced"}.get(ps, f"partition{ps}")
+
+
+def traffic_from_profile(wl_name, ps):
     """HBM bytes per launch from the committed counter summary, if it was taken
     on the current kernel source; else None."""
-    path = os.path.join(ROOT, "profiles", f"pmc_traffic_{wl_name}.md")
+    path = os.path.join(ROOT, "profiles", f"pmc_traffic_{wl_name}_{mode_name(ps)}.md")
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -163,19 +178,31 @@ def main():
     kcs = [t["k_cache"]] + [t["k_cache"].clone() for _ in range(reps - 1)]
     vcs = [t["v_cache"]] + [t["v_cache"].clone() for _ in range(reps - 1)]
     out = torch.empty_like(t["q"])
-    ps = spec.partition_size
-    ws = None
-    if ps:
-        ws = torch.empty(pkd.workspace_bytes(t["q"], t["k_cache"], t["block_table"], ps),
-                         dtype=torch.uint8, device=dev)
-        pkd.reset_workspace(ws)
     stream = torch.cuda.current_stream()
-    calls = [pkd.prepare(t["q"], kcs[i], vcs[i], t["block_table"], t["context_lens"],
-                         float(wl.scale), k_scale=t["k_scale"], v_scale=t["v_scale"],
-                         partition_size=ps, out=out, workspace=ws, stream=stream)
-             for i in range(reps)]
+
+    def make_calls(ps):
+        ws = None
+        if ps:
+            need = pkd.workspace_bytes(t["q"], t["k_cache"], t["block_table"], ps)
+            if need <= 0:
+                raise SystemExit(f"no workspace size for partition_size={ps}")
+            ws = torch.empty(need, dtype=torch.uint8, device=dev)
+            pkd.reset_workspace(ws)
+        return [pkd.prepare(t["q"], kcs[i], vcs[i], t["block_table"], t["context_lens"],
+                            float(wl.scale), k_scale=t["k_scale"], v_scale=t["v_scale"],
+                            partition_size=ps, out=out, workspace=ws, stream=stream)
+                for i in range(reps)]
+
+    if args.partition_size is not None:
+        modes = [args.partition_size]
+    elif args.split == "balanced":
+        modes = [pkd.SPLIT_BALANCED, spec.partition_size]
+    else:
+        modes = [spec.partition_size, pkd.SPLIT_BALANCED]
+    ps = modes[0]
 
     if args.pmc_pass:
+        calls = make_calls(ps)
         src = torch.ones(1 << 28, dtype=torch.int32, device=dev)      # 1 GiB
         dst = torch.empty_like(src)
         dst.copy_(src)
@@ -184,23 +211,29 @@ def main():
         torch.cuda.synchronize()
         return
 
-    for i in range(args.warmup):
-        calls[i % reps]()
-    torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for i in range(args.steps):
-        calls[i % reps]()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / args.steps
-    gpu_out = out.float().cpu().numpy().astype(np.float64)
+    def time_mode(mode):
+        calls = make_calls(mode)
+        for i in range(args.warmup):
+            calls[i % reps]()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(args.steps):
+            calls[i % reps]()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps, out.float().cpu().numpy().astype(np.float64)
+
+    timed = {}
+    for mode in modes:
+        timed[mode] = time_mode(mode)
+    ms, gpu_out = timed[ps]
 
     kv_bytes = wl.kv_bytes_logical()
     gbps = kv_bytes / (ms / 1e3) / 1e9
     sum_tokens = int(wl.context_lens.astype(np.int64).sum())
-    traffic = traffic_from_profile(spec.name)
+    traffic = traffic_from_profile(spec.name, ps)
     ceiling = None if args.no_stream_ceiling else stream_read_ceiling(torch)
 
     rec = {
@@ -226,6 +259,7 @@ def main():
             "block_size": 16,
             "context_lens": f"{spec.lens[0]} {list(spec.lens[1:])}",
             "sum_context_tokens": sum_tokens,
+            "split": mode_name(ps),
             "partition_size": ps,
             "kv_bytes_per_step": kv_bytes,
             "kv_bytes_unique_per_step": wl.kv_bytes_unique(),
@@ -242,6 +276,10 @@ def main():
             "traffic": traffic,
         },
         "stream_read_ceiling_GBps": None if ceiling is None else round(ceiling, 1),
+        "modes": {mode_name(m): {"partition_size": m, "ms_per_step": round(v[0], 6),
+                                 "GBps": round(kv_bytes / (v[0] / 1e3) / 1e9, 2),
+                                 "max_abs_vs_value_mode": float(np.abs(v[1] - gpu_out).max())}
+                  for m, v in timed.items()},
     }
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(wl, gpu_out, args.cpu_seconds)

@@ -90,18 +90,36 @@ typedef struct {
   int32_t block_size;         /* must be 16 */
   int32_t max_blocks_per_seq; /* row stride of block_table, >= 1 */
   int32_t num_blocks;         /* physical blocks in each cache, >= 1 */
-  int32_t partition_size;     /* 0: one pass per sequence; else a positive
-                                 multiple of 16 tokens: split-K partitions of
-                                 that many tokens, merged by log-sum-exp */
+  int32_t partition_size;     /* 0: one pass per sequence;
+                                 a positive multiple of 16 tokens: split-K
+                                 partitions of that many tokens, merged by
+                                 log-sum-exp;
+                                 PA_SPLIT_BALANCED: balanced split (below) */
 } pa_shape;
+
+/* partition_size value for the balanced split. The pages of every
+ * (sequence, KV head) pair, laid end to end, are cut into equal shares, one
+ * per workgroup the GPU holds at once, so every compute unit reads the same
+ * number of pages whatever the context lengths; a pair cut by share
+ * boundaries is merged by log-sum-exp like split-K partitions ("RapidLLM",
+ * feature table, row "Decode context parallelism"; "rvLLM", section "FA3 v3
+ * Attention Kernel": split-KV spreads a context over workgroups). The result
+ * equals the other modes' up to float rounding. Requires batch <= 4096 and
+ * batch * num_kv_heads * max_blocks_per_seq < 2^31 - 12288. */
+#define PA_SPLIT_BALANCED (-1)
 
 /* Bytes of workspace pa_decode needs for this shape: 0 when
  * partition_size == 0, else room for float32 partial outputs and
- * log-sum-exps of every (sequence, query head, partition) plus one counter
- * per (sequence, KV head). A workspace must be zero-filled once before its
- * first use (pa_workspace_reset does this on a stream); every completed call
- * leaves it zero-filled again where that matters. Returns 0 for a NULL or
- * invalid shape. */
+ * log-sum-exps of every (sequence, query head, partition) -- for the balanced
+ * split, of (shares + batch * num_kv_heads) pieces per query head of a group,
+ * where shares depends on the current device's compute units -- plus one
+ * counter per (sequence, KV head). The counters come first: the workspace's
+ * first 4 * batch * num_kv_heads bytes, rounded up to 256; every completed
+ * call leaves them zero, and the rest is scratch. So a workspace needs
+ * pa_workspace_reset (a zero fill on a stream) before its first use, and again
+ * before a call whose batch * num_kv_heads is larger than that of any earlier
+ * call since the last reset (its counters would cover old scratch bytes).
+ * Returns 0 for a NULL or invalid shape. */
 size_t pa_decode_workspace_bytes(const pa_shape* shape);
 
 /* Decode attention, enqueued on `stream` (a hipStream_t; NULL = the default

@@ -11,6 +11,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_NAME = "libpadecode.so"
 
 PA_F32, PA_F16, PA_BF16, PA_FP8_E4M3 = 0, 1, 2, 3
+SPLIT_BALANCED = -1   # partition_size value of the balanced split (PA_SPLIT_BALANCED)
 DTYPE_CODE = {"f32": PA_F32, "f16": PA_F16, "bf16": PA_BF16, "fp8_e4m3": PA_FP8_E4M3}
 
 EXPORTED = ("pa_decode", "pa_decode_workspace_bytes", "pa_workspace_reset",
@@ -127,8 +128,11 @@ def prepare(q, k_cache, v_cache, block_table, context_lens, scale, *, k_scale=No
     q [B, Hq, D] (float32 | float16 | bfloat16); k_cache [nb, Hkv, D/X, 16, X];
     v_cache [nb, Hkv, D, 16] (q's dtype, or float8_e4m3fn / uint8 codes with
     float32 k_scale, v_scale [Hkv]); block_table int32 [B, MBS];
-    context_lens int32 [B]. `workspace` (uint8, zero-filled once) is required
-    when partition_size > 0; `workspace_bytes` gives its size.
+    context_lens int32 [B]. partition_size: 0 = one pass per sequence, a
+    positive multiple of 16 = split-K partitions of that many tokens,
+    SPLIT_BALANCED = equal page shares per workgroup. `workspace` (uint8,
+    zero-filled once) is used when partition_size != 0; `workspace_bytes`
+    gives its size.
     """
     import torch
     lib = load_library()

@@ -18,6 +18,7 @@ COMMON = [
     # multiplies them in place instead of copying through AGPRs
     "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-I", os.path.join(ROOT, "include"),
+    "-I", os.path.join(HERE, "csrc"),
 ]
 
 TARGETS = [

@@ -44,6 +44,7 @@
 #include <type_traits>
 
 #include "padecode.h"
+#include "pa_schedule.h"
 
 namespace pa {
 
@@ -80,9 +81,9 @@ struct Params {
   const float* v_scale;
   uint8_t* out;
   float* lse_out;
-  float* ws_o;       // [B][Hq][p_max][D]
-  float* ws_lse;     // [B][Hq][p_max]   base 2, in units of the scaled scores
-  uint32_t* ws_cnt;  // [B][Hkv]
+  float* ws_o;       // [slot][G][D]   partial outputs, normalised
+  float* ws_lse;     // [slot][G]      base 2, in units of the scaled scores
+  uint32_t* ws_cnt;  // [B][Hkv]       pieces of (b, g) finished so far
   float scale;
   int32_t batch;
   int32_t num_q_heads;
@@ -91,7 +92,7 @@ struct Params {
   int32_t max_blocks_per_seq;
   int32_t num_blocks;
   int32_t part_tokens;  // 0: whole sequence in one unit
-  int32_t p_max;
+  int32_t p_max;        // fixed partitions: slots per (b, g)
 };
 
 constexpr int gcd_c(int x, int y) { return y == 0 ? x : gcd_c(y, x % y); }
@@ -422,16 +423,19 @@ struct Smem {
   float l[kWaves][kMaxGroup];
   int bad;
   int last;
+  int wsum[kWaves];   // balanced split: per-wave sums of the work-line scan
+  int b0, pre0;       // balanced split: sequence holding the share's start
 };
 
-// Merge the partitions of (b, g) stored in the workspace and write the final
-// output of its query heads. Threads take (head, 4-float quad) pairs; when the
-// group leaves threads over, S slices split the partitions (slice s takes
-// p = s, s + S, ...). Every thread issues the loads of 8 partitions before
+// Merge the nparts pieces of (b, g) stored in workspace slots slot0 ...
+// slot0 + nparts - 1 (partitions, or shares of the balanced split) and write
+// the final output of its query heads. Threads take (head, 4-float quad)
+// pairs; when the group leaves threads over, S slices split the pieces (slice
+// s takes p = s, s + S, ...). Every thread issues the loads of 8 partitions before
 // folding them with a running max, and slices are combined in order 0, 1, ...,
 // so the result does not depend on which workgroup finished last.
 template <typename IO, int D>
-__device__ void merge_partitions(const Params& a, Smem<D>& sm, int b, int g, int nparts) {
+__device__ void merge_partitions(const Params& a, Smem<D>& sm, int b, int g, int slot0, int nparts) {
   constexpr int kQuads = D / 4;
   constexpr int kBatch = 8;
   const int tid = threadIdx.x;
@@ -443,8 +447,9 @@ __device__ void merge_partitions(const Params& a, Smem<D>& sm, int b, int g, int
     const int pair = idx % npair, sl = idx / npair;
     const int h = pair / kQuads, dq = pair % kQuads;
     const size_t row = (size_t)b * a.num_q_heads + g * a.group + h;
-    const float* lse = a.ws_lse + row * a.p_max;
-    const float* o = a.ws_o + row * a.p_max * D + 4 * dq;
+    const float* lse = a.ws_lse + (size_t)slot0 * a.group + h;
+    const float* o = a.ws_o + ((size_t)slot0 * a.group + h) * D + 4 * dq;
+    const size_t lse_step = a.group, o_step = (size_t)a.group * D;   // per slot
     float mr = -INFINITY, wr = 0.f;
     f32x4 ar = {0.f, 0.f, 0.f, 0.f};
     if (active) {
@@ -455,8 +460,8 @@ __device__ void merge_partitions(const Params& a, Smem<D>& sm, int b, int g, int
         for (int u = 0; u < kBatch; ++u) {
           const int p = p0 + u * S;
           if (p < nparts) {
-            const float* op = o + (size_t)p * D;
-            lp[u] = ld_agent(lse + p);
+            const float* op = o + (size_t)p * o_step;
+            lp[u] = ld_agent(lse + (size_t)p * lse_step);
             ov[u] = f32x4{ld_agent(op), ld_agent(op + 1), ld_agent(op + 2), ld_agent(op + 3)};
           }
         }
@@ -510,23 +515,37 @@ __device__ void merge_partitions(const Params& a, Smem<D>& sm, int b, int g, int
 // ---------------------------------------------------------------------------
 // The kernel.
 // ---------------------------------------------------------------------------
-// One work unit: partition p of sequence b for KV head g, by the whole
-// workgroup. Control flow is uniform across the workgroup.
-template <typename IO, typename KV, int D>
-__device__ __forceinline__ void decode_unit(const Params& a, Smem<D>& sm, const int p, const int b,
-                                            const int g) {
+// What the caller knows of a piece once the context length is in.
+struct Piece {
+  int L;        // context length of the sequence
+  int pg_hi;    // one past the piece's last page (tokens past L are cut off)
+  int k;        // index of the piece among the pieces of (b, g)
+  int nparts;   // pieces of (b, g); 1: write the output directly; 0: no work
+  int slot0;    // workspace slot of piece 0 of (b, g)
+};
+
+// One piece: pages page0 .. pg_hi - 1 of sequence b for KV head g, by the
+// whole workgroup. resolve() returns the Piece; it is called after the loads
+// that do not depend on it are issued. Control flow is uniform across the
+// workgroup.
+template <typename IO, typename KV, int D, typename Resolve>
+__device__ __forceinline__ void decode_piece(const Params& a, Smem<D>& sm, const int b, const int g,
+                                             const int page0, Resolve resolve) {
   using T = typename TileOf<IO, KV, D>::type;
   constexpr bool kFp8 = std::is_same<KV, FP8>::value;
   constexpr size_t kPageBytes = (size_t)kBlock * D * ElemSize<KV>::v;
 
-  const int tid = threadIdx.x;
+  // The thread index passes through an empty asm statement so that the
+  // per-lane offsets below are recomputed for every piece rather than hoisted
+  // out of the balanced kernel's piece loop, where they would stay live (and
+  // spill) across all of it.
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int G = a.group;
   const int hq0 = g * G;
 
-  const int PT = a.part_tokens;
-  const int page0 = PT > 0 ? p * (PT / kBlock) : 0;
   const int rr = lane & 15, jj = lane >> 4;
   const bool head_ok = rr < G;
 
@@ -542,11 +561,10 @@ __device__ __forceinline__ void decode_unit(const Params& a, Smem<D>& sm, const 
   T::load_q(qop, (gptr)(a.q + ((size_t)b * a.num_q_heads + hq0 + (head_ok ? rr : 0)) * D * ElemSize<IO>::v),
             jj, head_ok);
 
-  const int L = a.context_lens[b];
+  const Piece pc = resolve();
+  if (pc.nparts == 0) return;
+  const int L = pc.L;
   const bool bad_len = L < 0 || L > a.max_blocks_per_seq * kBlock;
-  const int nparts = (bad_len || L == 0) ? 1 : (PT > 0 ? (L + PT - 1) / PT : 1);
-  if (p >= nparts) return;
-
   if (bad_len || L == 0) {
     // No tokens (or an out-of-contract length): zeros, resp. NaN.
     const float fill = bad_len ? __builtin_nanf("") : 0.f;
@@ -557,8 +575,8 @@ __device__ __forceinline__ void decode_unit(const Params& a, Smem<D>& sm, const 
     return;
   }
 
-  const int t0 = PT > 0 ? p * PT : 0;
-  const int t1 = PT > 0 ? min(t0 + PT, L) : L;
+  const int t0 = page0 * kBlock;
+  const int t1 = min(pc.pg_hi * kBlock, L);
   const int npages = (t1 - t0 + kBlock - 1) / kBlock;
   const int nmine = npages > w ? (npages - w + kWaves - 1) / kWaves : 0;
 
@@ -694,7 +712,8 @@ __device__ __forceinline__ void decode_unit(const Params& a, Smem<D>& sm, const 
   __syncthreads();
   const bool bad = sm.bad != 0;
 
-  const bool split = nparts > 1;
+  const bool split = pc.nparts > 1;
+  const size_t slot = (size_t)pc.slot0 + pc.k;
   for (int i = tid; i < G * D; i += kThreads) {
     const int h = i / D, d = i - h * D;
     float M = -INFINITY;
@@ -715,8 +734,8 @@ __device__ __forceinline__ void decode_unit(const Params& a, Smem<D>& sm, const 
       store_out<IO>(a.out, row * D + d, val);
       if (d == 0 && a.lse_out) a.lse_out[row] = lse2 * kLn2;
     } else {
-      st_agent(a.ws_o + (row * a.p_max + p) * D + d, val);
-      if (d == 0) st_agent(a.ws_lse + row * a.p_max + p, lse2);
+      st_agent(a.ws_o + (slot * G + h) * D + d, val);
+      if (d == 0) st_agent(a.ws_lse + slot * G + h, lse2);
     }
   }
   if (!split) return;
@@ -729,14 +748,16 @@ __device__ __forceinline__ void decode_unit(const Params& a, Smem<D>& sm, const 
   uint32_t* cnt = a.ws_cnt + (size_t)b * a.num_kv_heads + g;
   if (tid == 0) {
     const uint32_t done = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    sm.last = done == (uint32_t)(nparts - 1);
+    sm.last = done == (uint32_t)(pc.nparts - 1);
   }
   __syncthreads();
   if (!__builtin_amdgcn_readfirstlane(sm.last)) return;   // uniform: a scalar branch
-  merge_partitions<IO, D>(a, sm, b, g, nparts);
+  merge_partitions<IO, D>(a, sm, b, g, pc.slot0, pc.nparts);
   if (tid == 0) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Fixed schedule: one workgroup per (sequence b, KV head g, partition p) unit
+// (partition = the whole sequence when part_tokens == 0).
 template <typename IO, typename KV, int D>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3)))
 pa_decode_kernel(const Params a) {
@@ -745,11 +766,105 @@ pa_decode_kernel(const Params a) {
   // + g, because the hardware hands consecutive workgroups to the eight XCDs
   // in turn: every XCD then gets an even share of each partition level, whose
   // population shrinks with p.
-  const int nbg = a.batch * a.num_kv_heads;
+  const int H = a.num_kv_heads;
+  const int nbg = a.batch * H;
   const int p = blockIdx.x / nbg;
   const int bg = blockIdx.x - p * nbg;
-  const int b = bg / a.num_kv_heads;
-  decode_unit<IO, KV, D>(a, sm, p, b, bg - b * a.num_kv_heads);
+  const int b = bg / H;
+  const int g = bg - b * H;
+  const int PT = a.part_tokens;
+  const int page0 = PT > 0 ? p * (PT / kBlock) : 0;
+  decode_piece<IO, KV, D>(a, sm, b, g, page0, [&]() {
+    Piece pc;
+    pc.L = a.context_lens[b];
+    const bool bad_len = pc.L < 0 || pc.L > a.max_blocks_per_seq * kBlock;
+    const int n = (bad_len || pc.L == 0) ? 1 : (PT > 0 ? (pc.L + PT - 1) / PT : 1);
+    pc.nparts = p < n ? n : 0;
+    pc.k = p;
+    pc.pg_hi = PT > 0 ? page0 + PT / kBlock : a.max_blocks_per_seq;
+    pc.slot0 = bg * a.p_max;
+    return pc;
+  });
+}
+
+// Balanced schedule: the work line (pa_schedule.h) is cut into gridDim.x
+// equal shares, one per workgroup; the grid (kWgPerCu workgroups per CU) is
+// resident all at once, so every CU gets the same number of pages. Each workgroup first sums
+// the line positions of all sequences (an exclusive scan over the workgroup,
+// batch <= kThreads * kScanPerThread), finds the sequence holding its share's
+// start, then decodes the share's pieces in line order.
+constexpr int kScanPerThread = 16;
+static_assert(kMinSharePages >= kWaves, "a share gives every wave a page");
+
+template <typename IO, typename KV, int D>
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3)))
+pa_decode_balanced_kernel(const Params a) {
+  __shared__ Smem<D> sm;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int B = a.batch, H = a.num_kv_heads, mbs = a.max_blocks_per_seq;
+
+  // line positions of this thread's sequences [bbeg, bbeg + per)
+  const int per = (B + kThreads - 1) / kThreads;
+  const int bbeg = tid * per;
+  int mine = 0;
+  for (int i = 0; i < per; ++i) {
+    const int bb = bbeg + i;
+    if (bb < B) mine += line_pages(a.context_lens[bb], mbs);
+  }
+  int incl = mine;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(incl, d);
+    if (lane >= d) incl += y;
+  }
+  if (lane == 63) sm.wsum[w] = incl;
+  if (tid == 0) sm.b0 = sm.pre0 = 0;
+  __syncthreads();
+  int before = 0, total = 0;
+#pragma unroll
+  for (int ww = 0; ww < kWaves; ++ww) {
+    const int v = sm.wsum[ww];
+    total += v;
+    if (ww < w) before += v;
+  }
+  total = __builtin_amdgcn_readfirstlane(total);
+  const int N = total * H;
+  const int S = share_count(N, (int)gridDim.x);
+  const int wg = blockIdx.x;
+  if (wg >= S) return;   // uniform: a short line takes fewer shares
+  const int x0 = share_start(wg, N, S);
+  const int x1 = share_start(wg + 1, N, S);
+
+  // the sequence whose pairs hold line position x0
+  int pre = before + incl - mine;
+  for (int i = 0; i < per; ++i) {
+    const int bb = bbeg + i;
+    if (bb < B) {
+      const int cb = line_pages(a.context_lens[bb], mbs);
+      if (H * pre <= x0 && x0 < H * (pre + cb)) {
+        sm.b0 = bb;
+        sm.pre0 = pre;
+      }
+      pre += cb;
+    }
+  }
+  __syncthreads();
+  const int b0 = __builtin_amdgcn_readfirstlane(sm.b0);
+  const int pre0 = __builtin_amdgcn_readfirstlane(sm.pre0);
+
+  bool first = true;
+  walk_share(
+      wg, x0, x1, b0, pre0, B, H, N, S, mbs,
+      [&](int bb) { return __builtin_amdgcn_readfirstlane(a.context_lens[bb]); },
+      [&](int bb, int L, const LinePiece& lp) {
+        if (!first) __syncthreads();   // the previous piece's LDS reads are done
+        first = false;
+        decode_piece<IO, KV, D>(a, sm, bb, lp.g, lp.pg_lo, [&]() {
+          return Piece{L, lp.pg_hi, lp.k, lp.nparts, lp.slot0};
+        });
+      });
 }
 
 __global__ void fill_zero_kernel(uint8_t* p, size_t n) {
@@ -770,6 +885,24 @@ struct WsLayout {
 
 static inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+// Shares of the balanced split per CU. The register budget lets a CU hold
+// three workgroups, but two larger shares per CU measure faster on MI355X
+// than three (and one per CU as fast on f16/bf16 caches, slower on fp8):
+// every share pays a fixed latency at its start (lengths, block ids, first
+// pages) and end (partial store and hand-off), so fewer, longer shares stream
+// a larger part of the time, while two workgroups still keep enough loads in
+// flight per CU.
+constexpr int kWgPerCu = 2;
+
+// Shares of the balanced split on the current device, or -1.
+static int balanced_shares() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return -1;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return -1;
+  if (cus <= 0 || cus > 4096) return -1;
+  return cus * kWgPerCu;
+}
+
 static bool shape_ok(const pa_shape* s) {
   if (!s) return false;
   if (s->batch < 0 || s->batch > 65535) return false;
@@ -780,6 +913,12 @@ static bool shape_ok(const pa_shape* s) {
   if (s->block_size != kBlock) return false;
   if (s->max_blocks_per_seq < 1 || s->max_blocks_per_seq > (1 << 26)) return false;
   if (s->num_blocks < 1) return false;
+  if (s->partition_size == PA_SPLIT_BALANCED) {
+    // the workgroup-wide scan covers the batch, and line positions fit int32
+    if (s->batch > kThreads * kScanPerThread) return false;
+    const long long line = (long long)s->batch * s->num_kv_heads * s->max_blocks_per_seq;
+    return line + 4096LL * 3 < 0x7fffffffLL;   // + shares (4096 CUs at most, 3 per CU)
+  }
   if (s->partition_size < 0 || s->partition_size % kBlock != 0) return false;
   // work units B * Hkv * partitions must fit a 1-D grid
   const long long parts =
@@ -788,28 +927,42 @@ static bool shape_ok(const pa_shape* s) {
   return true;
 }
 
-static WsLayout ws_layout(const pa_shape* s) {
+// shares: the balanced split's workgroup count (ignored otherwise)
+static WsLayout ws_layout(const pa_shape* s, int shares) {
   WsLayout w{0, 0, 0, 0, 1};
   if (s->partition_size == 0) return w;
-  const long long tokens = (long long)s->max_blocks_per_seq * kBlock;
-  w.p_max = (int)((tokens + s->partition_size - 1) / s->partition_size);
-  const size_t rows = (size_t)s->batch * s->num_q_heads * w.p_max;
-  w.o_off = 0;
-  w.lse_off = align_up(rows * s->head_dim * sizeof(float), 256);
-  w.cnt_off = w.lse_off + align_up(rows * sizeof(float), 256);
-  w.total = w.cnt_off + align_up((size_t)s->batch * s->num_kv_heads * sizeof(uint32_t), 256);
+  size_t slots;
+  if (s->partition_size == PA_SPLIT_BALANCED) {
+    w.p_max = 0;
+    slots = (size_t)shares + (size_t)s->batch * s->num_kv_heads;
+  } else {
+    const long long tokens = (long long)s->max_blocks_per_seq * kBlock;
+    w.p_max = (int)((tokens + s->partition_size - 1) / s->partition_size);
+    slots = (size_t)s->batch * s->num_kv_heads * w.p_max;
+  }
+  const size_t rows = slots * (s->num_q_heads / s->num_kv_heads);
+  // counters first: their bytes stay where they are for every shape, so a
+  // smaller call after a larger one finds them zero
+  w.cnt_off = 0;
+  w.o_off = align_up((size_t)s->batch * s->num_kv_heads * sizeof(uint32_t), 256);
+  w.lse_off = w.o_off + align_up(rows * s->head_dim * sizeof(float), 256);
+  w.total = w.lse_off + align_up(rows * sizeof(float), 256);
   return w;
 }
 
 template <typename IO, typename KV, int D>
-static hipError_t launch(const Params& prm, dim3 grid, hipStream_t stream) {
-  hipLaunchKernelGGL((pa_decode_kernel<IO, KV, D>), grid, dim3(kThreads), 0, stream, prm);
+static hipError_t launch(const Params& prm, dim3 grid, bool balanced, hipStream_t stream) {
+  if (balanced)
+    hipLaunchKernelGGL((pa_decode_balanced_kernel<IO, KV, D>), grid, dim3(kThreads), 0, stream, prm);
+  else
+    hipLaunchKernelGGL((pa_decode_kernel<IO, KV, D>), grid, dim3(kThreads), 0, stream, prm);
   return hipGetLastError();
 }
 
 template <typename IO, typename KV>
-static hipError_t launch_d(int D, const Params& prm, dim3 grid, hipStream_t stream) {
-  return D == 64 ? launch<IO, KV, 64>(prm, grid, stream) : launch<IO, KV, 128>(prm, grid, stream);
+static hipError_t launch_d(int D, const Params& prm, dim3 grid, bool balanced, hipStream_t stream) {
+  return D == 64 ? launch<IO, KV, 64>(prm, grid, balanced, stream)
+                 : launch<IO, KV, 128>(prm, grid, balanced, stream);
 }
 
 static inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
@@ -820,7 +973,12 @@ extern "C" {
 
 size_t pa_decode_workspace_bytes(const pa_shape* shape) {
   if (!pa::shape_ok(shape)) return 0;
-  return pa::ws_layout(shape).total;
+  int shares = 0;
+  if (shape->partition_size == PA_SPLIT_BALANCED) {
+    shares = pa::balanced_shares();
+    if (shares < 0) return 0;
+  }
+  return pa::ws_layout(shape, shares).total;
 }
 
 pa_status pa_decode(const pa_shape* shape, const void* q, const void* k_cache,
@@ -842,8 +1000,14 @@ pa_status pa_decode(const pa_shape* shape, const void* q, const void* k_cache,
   if (((uintptr_t)block_table & 3u) || ((uintptr_t)context_lens & 3u) ||
       ((uintptr_t)lse_out & 3u))
     return PA_ERR_ALIGN;
-  const WsLayout wl = ws_layout(shape);
-  if (shape->partition_size > 0) {
+  const bool balanced = shape->partition_size == PA_SPLIT_BALANCED;
+  int shares = 0;
+  if (balanced) {
+    shares = balanced_shares();
+    if (shares < 0) return PA_ERR_HIP;
+  }
+  const WsLayout wl = ws_layout(shape, shares);
+  if (shape->partition_size != 0) {
     if (!workspace || workspace_bytes < wl.total) return PA_ERR_WORKSPACE;
     if ((uintptr_t)workspace & 255u) return PA_ERR_ALIGN;
   }
@@ -860,7 +1024,7 @@ pa_status pa_decode(const pa_shape* shape, const void* q, const void* k_cache,
   prm.out = static_cast<uint8_t*>(out);
   prm.lse_out = lse_out;
   uint8_t* ws = static_cast<uint8_t*>(workspace);
-  const bool split = shape->partition_size > 0;
+  const bool split = shape->partition_size != 0;
   prm.ws_o = split ? reinterpret_cast<float*>(ws + wl.o_off) : nullptr;
   prm.ws_lse = split ? reinterpret_cast<float*>(ws + wl.lse_off) : nullptr;
   prm.ws_cnt = split ? reinterpret_cast<uint32_t*>(ws + wl.cnt_off) : nullptr;
@@ -874,20 +1038,20 @@ pa_status pa_decode(const pa_shape* shape, const void* q, const void* k_cache,
   prm.part_tokens = shape->partition_size;
   prm.p_max = wl.p_max;
 
-  // 1-D grid of work units (see the kernel)
+  // 1-D grid: one workgroup per unit, or one per share (see the kernels)
   const long long nbg = (long long)shape->batch * shape->num_kv_heads;
-  const dim3 grid((unsigned)(nbg * wl.p_max), 1, 1);
+  const dim3 grid(balanced ? (unsigned)shares : (unsigned)(nbg * wl.p_max), 1, 1);
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t e;
   const int D = shape->head_dim;
   if (io_dtype == PA_F32)
-    e = launch_d<F32, F32>(D, prm, grid, st);
+    e = launch_d<F32, F32>(D, prm, grid, balanced, st);
   else if (io_dtype == PA_F16)
-    e = kv_dtype == PA_FP8_E4M3 ? launch_d<F16, FP8>(D, prm, grid, st)
-                                : launch_d<F16, F16>(D, prm, grid, st);
+    e = kv_dtype == PA_FP8_E4M3 ? launch_d<F16, FP8>(D, prm, grid, balanced, st)
+                                : launch_d<F16, F16>(D, prm, grid, balanced, st);
   else
-    e = kv_dtype == PA_FP8_E4M3 ? launch_d<BF16, FP8>(D, prm, grid, st)
-                                : launch_d<BF16, BF16>(D, prm, grid, st);
+    e = kv_dtype == PA_FP8_E4M3 ? launch_d<BF16, FP8>(D, prm, grid, balanced, st)
+                                : launch_d<BF16, BF16>(D, prm, grid, balanced, st);
   return e == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 

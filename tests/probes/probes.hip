@@ -4,8 +4,13 @@
 //    same per-lane k-slots; C: lane l holds rows 4*(l/16)+i of column l%16);
 //  * exactness of the E4M3 -> f16 / bf16 conversion instructions.
 // Each probe is one 64-thread workgroup over small, fully in-bounds buffers.
+// pa_probe_schedule runs the balanced split's work-line arithmetic (the same
+// header the kernel uses) on the host, so its coverage can be checked without
+// a GPU.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include "pa_schedule.h"
 
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
@@ -111,4 +116,40 @@ extern "C" int pa_probe_stream_read(const void* p, size_t bytes, void* sink, int
   hipLaunchKernelGGL(stream_read_kernel, dim3(blocks), dim3(256), 0, (hipStream_t)stream,
                      (const u32x4*)p, bytes / 16, (uint32_t*)sink);
   return hipGetLastError() == hipSuccess ? 0 : 2;
+}
+
+// Host-side walk of every share of the balanced split. Writes one row of 8
+// ints per piece -- share, sequence, KV head, first page, end page, piece
+// index, pieces of the pair, slot of piece 0 -- up to max_rows rows, and
+// returns the number of pieces (or -1 for bad arguments). The start of each
+// share is found by a plain linear search over the sequences.
+extern "C" int pa_probe_schedule(const int* lens, int B, int H, int max_blocks, int shares,
+                                 int* rows, int max_rows) {
+  if (!lens || B < 1 || H < 1 || max_blocks < 1 || shares < 1) return -1;
+  long long total = 0;
+  for (int b = 0; b < B; ++b) total += pa::line_pages(lens[b], max_blocks);
+  if (total * H > 0x7fffffffLL) return -1;
+  const int N = (int)total * H;
+  const int S = pa::share_count(N, shares);
+  int n = 0;
+  for (int wg = 0; wg < S; ++wg) {
+    const int x0 = pa::share_start(wg, N, S);
+    const int x1 = pa::share_start(wg + 1, N, S);
+    int b = 0, pre = 0;
+    while (H * (pre + pa::line_pages(lens[b], max_blocks)) <= x0) {
+      pre += pa::line_pages(lens[b], max_blocks);
+      ++b;
+    }
+    pa::walk_share(
+        wg, x0, x1, b, pre, B, H, N, S, max_blocks, [&](int bb) { return lens[bb]; },
+        [&](int bb, int, const pa::LinePiece& p) {
+          if (rows && n < max_rows) {
+            int* r = rows + 8 * n;
+            r[0] = wg; r[1] = bb; r[2] = p.g; r[3] = p.pg_lo;
+            r[4] = p.pg_hi; r[5] = p.k; r[6] = p.nparts; r[7] = p.slot0;
+          }
+          ++n;
+        });
+  }
+  return n;
 }

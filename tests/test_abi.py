@@ -60,7 +60,11 @@ def test_null_arguments_are_rejected_before_any_launch():
     dict(num_q_heads=7), dict(num_q_heads=40, num_kv_heads=2), dict(head_dim=96),
     dict(head_dim=256), dict(block_size=32), dict(partition_size=24),
     dict(partition_size=-16), dict(max_blocks_per_seq=0), dict(num_blocks=0),
-    dict(batch=-1), dict(num_kv_heads=0), dict(batch=70000)])
+    dict(batch=-1), dict(num_kv_heads=0), dict(batch=70000), dict(partition_size=-2),
+    # balanced split: batch beyond the workgroup-wide scan, line beyond int32
+    dict(partition_size=-1, batch=4097),
+    dict(partition_size=-1, batch=4096, num_q_heads=64, num_kv_heads=64,
+         max_blocks_per_seq=1 << 13)])
 def test_unsupported_shapes_are_errors(bad):
     assert call(shape(**bad)) == 2
 
@@ -114,3 +118,19 @@ def test_status_strings():
     for code in range(7):
         assert lib.pa_status_str(code)
     assert lib.pa_status_str(99) == b"unknown status"
+
+
+def test_balanced_split_shapes_pass_validation():
+    # Valid balanced shapes pass validation; without a GPU the call stops at
+    # the device query (PA_ERR_HIP, nothing launched) and the workspace size
+    # is unknown (0). Where a GPU is present this call would launch on the
+    # fake pointers, so it is left to the GPU tests.
+    import torch
+    if torch.cuda.device_count() > 0:
+        pytest.skip("a GPU is present: valid shapes would launch")
+    lib = _lib.load_library()
+    for kw in (dict(batch=4096), dict(batch=1, max_blocks_per_seq=8192),
+               dict(batch=32, num_q_heads=28, num_kv_heads=4, max_blocks_per_seq=256)):
+        s = shape(partition_size=-1, **kw)
+        assert call(s, ws=FAKE, wsb=1 << 30) == 6, kw
+        assert lib.pa_decode_workspace_bytes(ctypes.byref(s)) == 0
