@@ -135,6 +135,22 @@ __device__ __forceinline__ float ld_agent(const float* p) {
   return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// 16-byte agent-coherent accesses through a buffer resource (base must be
+// wave-uniform): the SC1 cache-policy bit, the same one the agent-scope
+// atomics above carry, on a dwordx4 buffer load/store. One such access moves
+// a float4 where four scalar ones would each cost a memory transaction.
+constexpr int kCpolSc1 = 16;
+typedef __amdgpu_buffer_rsrc_t brsrc;
+__device__ __forceinline__ brsrc buffer_rsrc(const float* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ f32x4 ld_agent4(brsrc r, uint32_t off) {
+  return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kCpolSc1));
+}
+__device__ __forceinline__ void st_agent4(brsrc r, uint32_t off, f32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, 0, kCpolSc1);
+}
+
 // ---------------------------------------------------------------------------
 // Matrix-core operand types.
 //
@@ -191,6 +207,12 @@ struct Op16<BF16> {
 //   kKoff / kVoff: per-lane byte offsets inside a K / V page (loop constants)
 //   load_k()/load_v(): issue the page's K / V loads;  scores(): S^T for the page;
 //   pvt(): the V^T operand of tile t (4 tokens of row 16*t + r).
+// load_q() reads the query row the caller points it at. Lanes whose head
+// column r lies past the group (r >= G) are pointed at the group's first row:
+// an MFMA output column depends only on its own B column, so those columns
+// hold finite duplicates that are never stored, and the query operand needs
+// no masking after its load (a select there would make the compiler wait for
+// the load at once).
 // ---------------------------------------------------------------------------
 
 // q/out f16 or bf16 with a cache of the same type.
@@ -217,11 +239,10 @@ struct Tile16 {
   };
   static __device__ __forceinline__ uint32_t koff(int lane) { return lane * 16; }
   static __device__ __forceinline__ uint32_t voff(int lane) { return (lane & 15) * 32 + (lane >> 4) * 8; }
-  static __device__ __forceinline__ void load_q(Q& q, gptr qrow, int jj, bool ok) {
+  static __device__ __forceinline__ void load_q(Q& q, gptr qrow, int jj) {
 #pragma unroll
     for (int c = 0; c < kK; ++c) {
-      u32x4 raw = ld<u32x4>(qrow, 16 * (jj + 4 * c));   // head-dim 8*(jj + 4c) .. +7
-      if (!ok) raw = u32x4{0u, 0u, 0u, 0u};
+      const u32x4 raw = ld<u32x4>(qrow, 16 * (jj + 4 * c));   // head-dim 8*(jj + 4c) .. +7
       q.c[c] = __builtin_bit_cast(A8, raw);
     }
   }
@@ -279,12 +300,11 @@ struct Tile8 {
   };
   static __device__ __forceinline__ uint32_t koff(int lane) { return lane * 16; }
   static __device__ __forceinline__ uint32_t voff(int lane) { return (lane & 15) * 16 + (lane >> 4) * 4; }
-  static __device__ __forceinline__ void load_q(Q& q, gptr qrow, int jj, bool ok) {
+  static __device__ __forceinline__ void load_q(Q& q, gptr qrow, int jj) {
 #pragma unroll
     for (int c = 0; c < 2 * kK; ++c) {
       // head-dim 16*(jj + 4*(c/2)) + 8*(c%2) .. +7
-      u32x4 raw = ld<u32x4>(qrow, 2 * (16 * (jj + 4 * (c / 2)) + 8 * (c % 2)));
-      if (!ok) raw = u32x4{0u, 0u, 0u, 0u};
+      const u32x4 raw = ld<u32x4>(qrow, 2 * (16 * (jj + 4 * (c / 2)) + 8 * (c % 2)));
       q.c[c] = __builtin_bit_cast(A8, raw);
     }
   }
@@ -340,11 +360,10 @@ struct Tile32 {
   };
   static __device__ __forceinline__ uint32_t koff(int lane) { return lane * 16; }
   static __device__ __forceinline__ uint32_t voff(int lane) { return (lane & 15) * 64 + (lane >> 4) * 16; }
-  static __device__ __forceinline__ void load_q(Q& q, gptr qrow, int jj, bool ok) {
+  static __device__ __forceinline__ void load_q(Q& q, gptr qrow, int jj) {
 #pragma unroll
     for (int c = 0; c < kK; ++c) {
-      const f32x4 raw = ld<f32x4>(qrow, 16 * (jj + 4 * c));   // head-dim 4*(jj + 4c) .. +3
-      q.c[c] = ok ? raw : f32x4{0.f, 0.f, 0.f, 0.f};
+      q.c[c] = ld<f32x4>(qrow, 16 * (jj + 4 * c));   // head-dim 4*(jj + 4c) .. +3
     }
   }
   static __device__ __forceinline__ void load_k(KRegs& r, gptr kp, uint32_t ko) {
@@ -407,6 +426,23 @@ __device__ __forceinline__ void store_out<BF16>(uint8_t* out, size_t idx, float 
   reinterpret_cast<__bf16*>(out)[idx] = (__bf16)x;
 }
 
+template <typename IO>
+__device__ __forceinline__ void store_out4(uint8_t* out, size_t idx, f32x4 v);
+template <>
+__device__ __forceinline__ void store_out4<F32>(uint8_t* out, size_t idx, f32x4 v) {
+  *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(out) + idx) = v;
+}
+template <>
+__device__ __forceinline__ void store_out4<F16>(uint8_t* out, size_t idx, f32x4 v) {
+  *reinterpret_cast<f16x4*>(reinterpret_cast<_Float16*>(out) + idx) =
+      f16x4{(_Float16)v[0], (_Float16)v[1], (_Float16)v[2], (_Float16)v[3]};
+}
+template <>
+__device__ __forceinline__ void store_out4<BF16>(uint8_t* out, size_t idx, f32x4 v) {
+  *reinterpret_cast<bf16x4*>(reinterpret_cast<__bf16*>(out) + idx) =
+      bf16x4{(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
+}
+
 template <typename T> struct ElemSize { static constexpr int v = 2; };
 template <> struct ElemSize<F32> { static constexpr int v = 4; };
 template <> struct ElemSize<FP8> { static constexpr int v = 1; };
@@ -434,13 +470,16 @@ struct Smem {
 // s takes p = s, s + S, ...). Every thread issues the loads of 8 partitions before
 // folding them with a running max, and slices are combined in order 0, 1, ...,
 // so the result does not depend on which workgroup finished last.
+// red: LDS scratch of at least kMergeScratch floats.
+constexpr int kMergeScratch = 6 * kThreads;
 template <typename IO, int D>
-__device__ void merge_partitions(const Params& a, Smem<D>& sm, int b, int g, int slot0, int nparts) {
+__device__ __forceinline__ void merge_partitions(const Params& a, float* red, int b, int g, int slot0, int nparts) {
   constexpr int kQuads = D / 4;
   constexpr int kBatch = 8;
   const int tid = threadIdx.x;
   const int npair = a.group * kQuads;
   const int S = npair >= kThreads ? 1 : kThreads / npair;
+  const size_t slot_floats = (size_t)a.group * D;
   for (int base = 0; base < npair * S; base += kThreads) {
     const int idx = base + tid;
     const bool active = idx < npair * S;
@@ -448,38 +487,38 @@ __device__ void merge_partitions(const Params& a, Smem<D>& sm, int b, int g, int
     const int h = pair / kQuads, dq = pair % kQuads;
     const size_t row = (size_t)b * a.num_q_heads + g * a.group + h;
     const float* lse = a.ws_lse + (size_t)slot0 * a.group + h;
-    const float* o = a.ws_o + ((size_t)slot0 * a.group + h) * D + 4 * dq;
-    const size_t lse_step = a.group, o_step = (size_t)a.group * D;   // per slot
     float mr = -INFINITY, wr = 0.f;
     f32x4 ar = {0.f, 0.f, 0.f, 0.f};
-    if (active) {
-      for (int p0 = sl; p0 < nparts; p0 += kBatch * S) {
-        float lp[kBatch];
-        f32x4 ov[kBatch];
+    // batches of kBatch * S slots, each read through a resource based at the
+    // batch's first slot (offsets stay small whatever nparts is)
+    for (int p0 = 0; p0 < nparts; p0 += kBatch * S) {
+      const int nb = min(kBatch * S, nparts - p0);
+      const brsrc r = buffer_rsrc(a.ws_o + ((size_t)slot0 + p0) * slot_floats,
+                                  (uint32_t)(nb * slot_floats * sizeof(float)));
+      float lp[kBatch];
+      f32x4 ov[kBatch];
 #pragma unroll
-        for (int u = 0; u < kBatch; ++u) {
-          const int p = p0 + u * S;
-          if (p < nparts) {
-            const float* op = o + (size_t)p * o_step;
-            lp[u] = ld_agent(lse + (size_t)p * lse_step);
-            ov[u] = f32x4{ld_agent(op), ld_agent(op + 1), ld_agent(op + 2), ld_agent(op + 3)};
-          }
+      for (int u = 0; u < kBatch; ++u) {
+        const int q = sl + u * S;   // slot within the batch
+        if (active && q < nb) {
+          lp[u] = ld_agent(lse + (size_t)(p0 + q) * a.group);
+          ov[u] = ld_agent4(r, (uint32_t)((q * slot_floats + h * D + 4 * dq) * sizeof(float)));
         }
+      }
 #pragma unroll
-        for (int u = 0; u < kBatch; ++u) {
-          if (p0 + u * S < nparts) {
-            const float mn = fmaxf(mr, lp[u]);
-            const float sa = exp2_fast(mr - mn), sb = exp2_fast(lp[u] - mn);
-            ar = ar * sa + ov[u] * sb;
-            wr = wr * sa + sb;
-            mr = mn;
-          }
+      for (int u = 0; u < kBatch; ++u) {
+        if (active && sl + u * S < nb) {
+          const float mn = fmaxf(mr, lp[u]);
+          const float sa = exp2_fast(mr - mn), sb = exp2_fast(lp[u] - mn);
+          ar = ar * sa + ov[u] * sb;
+          wr = wr * sa + sb;
+          mr = mn;
         }
       }
     }
     if (S > 1) {
       // npair * S <= kThreads: one pass, every thread is here.
-      float* red = &sm.acc[0][0][0];   // [S][npair] quads, then m, then w
+      // red: [S][npair] quads, then m, then w
       float* redm = red + 4 * npair * S;
       float* redw = redm + npair * S;
       if (active) {
@@ -505,8 +544,7 @@ __device__ void merge_partitions(const Params& a, Smem<D>& sm, int b, int g, int
       }
     }
     if (active && sl == 0) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) store_out<IO>(a.out, row * D + 4 * dq + e, ar[e] / wr);
+      store_out4<IO>(a.out, row * D + 4 * dq, f32x4{ar[0] / wr, ar[1] / wr, ar[2] / wr, ar[3] / wr});
       if (dq == 0 && a.lse_out) a.lse_out[row] = (mr + log2_fast(wr)) * kLn2;
     }
   }
@@ -559,7 +597,7 @@ __device__ __forceinline__ void decode_piece(const Params& a, Smem<D>& sm, const
   int bt_cur = fetch_bt(0);
   typename T::Q qop;
   T::load_q(qop, (gptr)(a.q + ((size_t)b * a.num_q_heads + hq0 + (head_ok ? rr : 0)) * D * ElemSize<IO>::v),
-            jj, head_ok);
+            jj);
 
   const Piece pc = resolve();
   if (pc.nparts == 0) return;
@@ -608,10 +646,14 @@ __device__ __forceinline__ void decode_piece(const Params& a, Smem<D>& sm, const
   typename T::VRegs ring_v[kVS];
   size_t poff[kKS];
 
-  auto issue_k = [&](int slot, int i) {
-    if (i > 0 && (i & 63) == 0) {
-      bt_cur = bt_next;
-      if (nmine > i + 64) bt_next = fetch_bt((i >> 6) + 1);
+  // kRefresh: the wave has more than 64 pages, so block ids are re-fetched
+  // every 64 pages inside the loop (see run_ring below).
+  auto issue_k = [&](int slot, int i, auto refresh_tag) {
+    if constexpr (decltype(refresh_tag)::value) {
+      if (i > 0 && (i & 63) == 0) {
+        bt_cur = bt_next;
+        if (nmine > i + 64) bt_next = fetch_bt((i >> 6) + 1);
+      }
     }
     int phys = __builtin_amdgcn_readlane(bt_cur, i & 63);
     if ((unsigned)phys >= (unsigned)a.num_blocks) {
@@ -670,30 +712,40 @@ __device__ __forceinline__ void decode_piece(const Params& a, Smem<D>& sm, const
   // and never holds a wave's last page (the only one that can be partial);
   // the peeled remainder issues and masks as needed.
   constexpr int kU = kKS * kVS / gcd_c(kKS, kVS);
+  // Two copies of the loop: with no block-id fetch inside it (at most 64
+  // pages per wave, the usual case) the compiler's wait counts for the ring
+  // stay exact; a fetch inside the loop makes them conservative (it then
+  // waits for nearly every load in flight at the top of each iteration).
+  auto run_ring = [&](auto refresh_tag) {
 #pragma unroll
-  for (int j = 0; j < dK; ++j)
-    if (j < nmine) issue_k(j, j);
+    for (int j = 0; j < dK; ++j)
+      if (j < nmine) issue_k(j, j, refresh_tag);
 #pragma unroll
-  for (int j = 0; j < dV; ++j)
-    if (j < nmine) issue_v(j, j);
-  int i0 = 0;
-  for (; i0 + kU - 1 + kAhead < nmine; i0 += kU) {
+    for (int j = 0; j < dV; ++j)
+      if (j < nmine) issue_v(j, j);
+    int i0 = 0;
+    for (; i0 + kU - 1 + kAhead < nmine; i0 += kU) {
 #pragma unroll
-    for (int u = 0; u < kU; ++u) {
-      issue_k((u + dK) % kKS, i0 + u + dK);
-      issue_v((u + dV) % kVS, (u + dV) % kKS);
-      compute(u % kKS, u % kVS, i0 + u, Full{});
+      for (int u = 0; u < kU; ++u) {
+        issue_k((u + dK) % kKS, i0 + u + dK, refresh_tag);
+        issue_v((u + dV) % kVS, (u + dV) % kKS);
+        compute(u % kKS, u % kVS, i0 + u, Full{});
+      }
     }
-  }
 #pragma unroll
-  for (int u = 0; u < kU + kAhead; ++u) {
-    const int i = i0 + u;
-    if (i < nmine) {
-      if (i + dK < nmine) issue_k((u + dK) % kKS, i + dK);
-      if (i + dV < nmine) issue_v((u + dV) % kVS, (u + dV) % kKS);
-      compute(u % kKS, u % kVS, i, Tail{});
+    for (int u = 0; u < kU + kAhead; ++u) {
+      const int i = i0 + u;
+      if (i < nmine) {
+        if (i + dK < nmine) issue_k((u + dK) % kKS, i + dK, refresh_tag);
+        if (i + dV < nmine) issue_v((u + dV) % kVS, (u + dV) % kKS);
+        compute(u % kKS, u % kVS, i, Tail{});
+      }
     }
-  }
+  };
+  if (nmine > 64)
+    run_ring(std::integral_constant<bool, true>{});
+  else
+    run_ring(std::integral_constant<bool, false>{});
 
   // ---- merge the waves through LDS --------------------------------------
   lsum = wave_sum_rows(lsum);
@@ -714,27 +766,32 @@ __device__ __forceinline__ void decode_piece(const Params& a, Smem<D>& sm, const
 
   const bool split = pc.nparts > 1;
   const size_t slot = (size_t)pc.slot0 + pc.k;
-  for (int i = tid; i < G * D; i += kThreads) {
-    const int h = i / D, d = i - h * D;
+  const brsrc wr_slot = buffer_rsrc(a.ws_o + slot * G * D, (uint32_t)(G * D * sizeof(float)));
+  for (int i = tid; i < G * (D / 4); i += kThreads) {   // (head, 4-float quad)
+    const int h = i / (D / 4), d = 4 * (i - h * (D / 4));
     float M = -INFINITY;
 #pragma unroll
     for (int ww = 0; ww < kWaves; ++ww) M = fmaxf(M, sm.m[ww][h]);
-    float W = 0.f, o = 0.f;
+    float W = 0.f;
+    f32x4 o = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ww = 0; ww < kWaves; ++ww) {
       const float e = exp2_fast(sm.m[ww][h] - M);
       W += e * sm.l[ww][h];
-      o += e * sm.acc[ww][h][d];
+      o += e * *reinterpret_cast<const f32x4*>(&sm.acc[ww][h][d]);
     }
-    float val = o / W * vmul;
+    f32x4 val = {o[0] / W * vmul, o[1] / W * vmul, o[2] / W * vmul, o[3] / W * vmul};
     float lse2 = M + log2_fast(W);
-    if (bad) val = lse2 = __builtin_nanf("");
+    if (bad) {
+      val = f32x4{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
+      lse2 = __builtin_nanf("");
+    }
     const size_t row = (size_t)b * a.num_q_heads + hq0 + h;
     if (!split) {
-      store_out<IO>(a.out, row * D + d, val);
+      store_out4<IO>(a.out, row * D + d, val);
       if (d == 0 && a.lse_out) a.lse_out[row] = lse2 * kLn2;
     } else {
-      st_agent(a.ws_o + (slot * G + h) * D + d, val);
+      st_agent4(wr_slot, (uint32_t)((h * D + d) * sizeof(float)), val);
       if (d == 0) st_agent(a.ws_lse + slot * G + h, lse2);
     }
   }
@@ -752,7 +809,8 @@ __device__ __forceinline__ void decode_piece(const Params& a, Smem<D>& sm, const
   }
   __syncthreads();
   if (!__builtin_amdgcn_readfirstlane(sm.last)) return;   // uniform: a scalar branch
-  merge_partitions<IO, D>(a, sm, b, g, pc.slot0, pc.nparts);
+  static_assert(sizeof(sm.acc) >= kMergeScratch * sizeof(float), "merge scratch");
+  merge_partitions<IO, D>(a, &sm.acc[0][0][0], b, g, pc.slot0, pc.nparts);
   if (tid == 0) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
@@ -787,31 +845,471 @@ pa_decode_kernel(const Params a) {
   });
 }
 
-// Balanced schedule: the work line (pa_schedule.h) is cut into gridDim.x
-// equal shares, one per workgroup; the grid (kWgPerCu workgroups per CU) is
-// resident all at once, so every CU gets the same number of pages. Each workgroup first sums
-// the line positions of all sequences (an exclusive scan over the workgroup,
-// batch <= kThreads * kScanPerThread), finds the sequence holding its share's
-// start, then decodes the share's pieces in line order.
+// ---------------------------------------------------------------------------
+// Balanced schedule.
+//
+// The work line (pa_schedule.h) is cut into gridDim.x equal shares, one per
+// workgroup; the grid (kWgPerCu workgroups per CU) is resident all at once,
+// so every CU gets the same number of pages. Each workgroup first loads the
+// context lengths into LDS with the exclusive prefix sums of their line
+// positions (a scan over the workgroup, batch <= kThreads * kScanPerThread);
+// every later lookup of "which sequence holds line position x" is a binary
+// search there. Wave w then takes the contiguous quarter [y_w, y_w+1) of the
+// share and streams its pages through one register ring from the first to
+// the last, across all the (sequence, KV head) pairs the quarter touches:
+//   - block ids and per-position facts (tokens in the page, KV head, "last
+//     position of its piece") are fetched 64 positions at a time, one chunk
+//     ahead;
+//   - the query rows (and fp8 scales) of the next pair are loaded while the
+//     current pair is computed;
+//   - at a pair's last position in the quarter the wave flushes its softmax
+//     state: a pair that lies whole inside the quarter gets its output
+//     written by the wave; any other piece (it continues into a neighbouring
+//     quarter or share) goes to one of the wave's two LDS slots, slot 0 for
+//     the piece that starts the quarter, slot 1 for the one that ends it.
+// After its quarter, the workgroup merges, for every piece of the share that
+// went through LDS, the slots of the waves holding it, and writes the output
+// (pair inside the share) or a partial result, handed on to the last-finisher
+// merge of the pair as in the fixed schedule.
+// ---------------------------------------------------------------------------
 constexpr int kScanPerThread = 16;
+constexpr int kBalancedMaxBatch = kThreads * kScanPerThread;
 static_assert(kMinSharePages >= kWaves, "a share gives every wave a page");
 
+// Per-position facts in a lane's meta word.
+constexpr int kMetaValid = 31;     // tokens of the page; 0: placeholder position
+constexpr int kMetaEnd = 32;       // last position of its piece in the quarter
+constexpr int kMetaBad = 64;       // block id outside the pool
+constexpr int kMetaHeadShift = 8;  // KV head in bits 8..23
+
+// Dynamic LDS of the balanced kernel, sized by group G, head_dim D, batch B.
+// Pieces of one share that go through the LDS merge, at most: the share's
+// first and last piece and one piece across each of the three quarter
+// boundaries.
+constexpr int kMaxSplit = 8;
+
+struct BalLayout {
+  uint32_t acc, m, l, bad, red, len, pre, misc, split, total;   // byte offsets
+};
+__host__ __device__ inline uint32_t lds_align(uint32_t x) { return (x + 15u) & ~15u; }
+__host__ __device__ inline BalLayout bal_layout(int G, int D, int B) {
+  BalLayout o;
+  uint32_t p = 0;
+  o.acc = p;  p = lds_align(p + 4u * kWaves * 2 * G * (D + 4));   // [kWaves][2][G][D + 4]
+  o.m = p;    p = lds_align(p + 4u * kWaves * 2 * G);             // [kWaves][2][G]
+  o.l = p;    p = lds_align(p + 4u * kWaves * 2 * G);
+  o.bad = p;  p = lds_align(p + 4u * kWaves * 2);                 // [kWaves][2]
+  o.red = p;  p = lds_align(p + 4u * kMergeScratch);
+  o.len = p;  p = lds_align(p + 4u * B);                          // [B]
+  o.pre = p;  p = lds_align(p + 4u * (B + 1));                    // [B + 1]
+  o.misc = p; p = lds_align(p + 4u * kWaves);                     // wsum[kWaves]
+  o.split = p; p = lds_align(p + 4u * 5 * kMaxSplit);             // split pieces, their flags
+  o.total = p;
+  return o;
+}
+
+extern __shared__ __attribute__((aligned(16))) uint8_t bal_lds[];
+
+template <int D>
+struct BalSm {
+  float* acc;
+  float* m;
+  float* l;
+  int* bad;
+  float* red;
+  int* len;
+  int* pre;
+  int* misc;
+  int* split;   // [kMaxSplit][4] (b, g, nparts, slot0), then [kMaxSplit] "last" flags
+  int G;
+  __device__ BalSm(int G_, int B) : G(G_) {
+    const BalLayout o = bal_layout(G_, D, B);
+    acc = reinterpret_cast<float*>(bal_lds + o.acc);
+    m = reinterpret_cast<float*>(bal_lds + o.m);
+    l = reinterpret_cast<float*>(bal_lds + o.l);
+    bad = reinterpret_cast<int*>(bal_lds + o.bad);
+    red = reinterpret_cast<float*>(bal_lds + o.red);
+    len = reinterpret_cast<int*>(bal_lds + o.len);
+    pre = reinterpret_cast<int*>(bal_lds + o.pre);
+    misc = reinterpret_cast<int*>(bal_lds + o.misc);
+    split = reinterpret_cast<int*>(bal_lds + o.split);
+  }
+  __device__ float* acc_row(int w, int slot, int h) const { return acc + ((w * 2 + slot) * G + h) * (D + 4); }
+  __device__ int mi(int w, int slot, int h) const { return (w * 2 + slot) * G + h; }
+};
+
+// The sequence holding line position x: the largest b < B with H*pre[b] <= x.
+__device__ __forceinline__ int seq_of(const int* pre, int B, int H, int x) {
+  int lo = 0, hi = B;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (H * pre[mid] <= x) lo = mid; else hi = mid;
+  }
+  return lo;
+}
+__device__ __forceinline__ int seq_of_uniform(const int* pre, int B, int H, int x) {
+  int lo = 0, hi = B;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (H * __builtin_amdgcn_readfirstlane(pre[mid]) <= x) lo = mid; else hi = mid;
+  }
+  return lo;
+}
+
+// A uniform cursor on one piece of a quarter [., y1): the pair (b, g) and the
+// pages pg_lo .. pg_hi - 1 of it that lie in the quarter.
+struct QCursor {
+  int b, L;
+  int g, pg_lo, pg_hi;
+  int pair_first, pair_end;  // the pair's line positions
+};
+
+// The piece at line position x (uniform).
+template <int D>
+__device__ __forceinline__ void qcursor_at(QCursor& c, const Params& a, const BalSm<D>& sm, int x,
+                                           int y1) {
+  const int H = a.num_kv_heads;
+  c.b = seq_of_uniform(sm.pre, a.batch, H, x);
+  c.L = __builtin_amdgcn_readfirstlane(sm.len[c.b]);
+  const int cb = line_pages(c.L, a.max_blocks_per_seq);
+  const int sf = H * __builtin_amdgcn_readfirstlane(sm.pre[c.b]);
+  c.g = (x - sf) / cb;
+  c.pg_lo = x - sf - c.g * cb;
+  c.pair_first = sf + c.g * cb;
+  c.pair_end = c.pair_first + cb;
+  c.pg_hi = c.pg_lo + (min(y1, c.pair_end) - x);
+}
+
+// One wave's quarter [y0, y1) of a share.
 template <typename IO, typename KV, int D>
-__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3)))
+__device__ __forceinline__ void decode_quarter(const Params& a, const BalSm<D>& sm, const int y0,
+                                               const int y1) {
+  using T = typename TileOf<IO, KV, D>::type;
+  constexpr bool kFp8 = std::is_same<KV, FP8>::value;
+  constexpr size_t kPageBytes = (size_t)kBlock * D * ElemSize<KV>::v;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int G = a.group, H = a.num_kv_heads, mbs = a.max_blocks_per_seq, B = a.batch;
+  const int rr = lane & 15, jj = lane >> 4;
+  const bool head_ok = rr < G;
+  const int n = y1 - y0;
+
+  // ---- block ids and position facts, 64 positions per chunk ---------------
+  auto fetch_chunk = [&](int c0, int& blk, int& meta) {
+    const int xp = y0 + c0 + lane;
+    blk = 0;
+    meta = 0;
+    if (xp < y1) {
+      const int bl = seq_of(sm.pre, B, H, xp);
+      const int L = sm.len[bl];
+      const int cb = line_pages(L, mbs);
+      const int sf = H * sm.pre[bl];
+      const int g = (xp - sf) / cb;
+      const int page = xp - sf - g * cb;
+      const int pair_end = sf + (g + 1) * cb;
+      const bool valid = L > 0 && L <= mbs * kBlock;
+      if (valid) blk = a.block_table[(size_t)bl * mbs + page];
+      meta = (valid ? min(kBlock, L - page * kBlock) : 0) | (xp + 1 == min(y1, pair_end) ? kMetaEnd : 0) |
+             (g << kMetaHeadShift);
+    }
+  };
+  int bt_cur, meta_cur, bt_nxt = 0, meta_nxt = 0;
+  fetch_chunk(0, bt_cur, meta_cur);
+  if (n > 64) fetch_chunk(64, bt_nxt, meta_nxt);
+
+  // ---- the pieces, in order: the current one and the next ----------------
+  QCursor cur, nxt;
+  qcursor_at(cur, a, sm, y0, y1);
+  bool has_nxt = cur.pair_end < y1;
+  if (has_nxt) qcursor_at(nxt, a, sm, cur.pair_end, y1);
+  auto q_row = [&](const QCursor& c) {
+    return (gptr)(a.q + ((size_t)c.b * a.num_q_heads + c.g * G + (head_ok ? rr : 0)) * D * ElemSize<IO>::v);
+  };
+  typename T::Q q_cur, q_nxt;
+  T::load_q(q_cur, q_row(cur), jj);
+  if (has_nxt) T::load_q(q_nxt, q_row(nxt), jj);
+  float kmul_cur = a.scale * kLog2e, kmul_nxt = kmul_cur, vmul_cur = 1.0f, vmul_nxt = 1.0f;
+  if constexpr (kFp8) {
+    const float s0 = kmul_cur;
+    kmul_cur = s0 * a.k_scale[cur.g];
+    vmul_cur = a.v_scale[cur.g];
+    if (has_nxt) {
+      kmul_nxt = s0 * a.k_scale[nxt.g];
+      vmul_nxt = a.v_scale[nxt.g];
+    }
+  }
+
+  const gptr kbase = uniform_ptr(a.k);
+  const gptr vbase = uniform_ptr(a.v);
+  const uint32_t ko = T::koff(lane), vo = T::voff(lane);
+
+  constexpr int kKS = T::kKStages, kVS = T::kVStages;
+  constexpr int dK = kKS - 1, dV = kVS - 1;
+  static_assert(kKS >= 1 && kVS >= 1 && dV <= dK, "ring depths");
+  constexpr int kAhead = dK > 1 ? dK : 1;
+  typename T::KRegs ring_k[kKS];
+  typename T::VRegs ring_v[kVS];
+  size_t poff[kKS];
+  int meta_k[kKS];
+
+  auto issue_k = [&](int slot, int i, auto refresh_tag) {
+    if constexpr (decltype(refresh_tag)::value) {
+      if (i > 0 && (i & 63) == 0) {
+        bt_cur = bt_nxt;
+        meta_cur = meta_nxt;
+        if (n > i + 64) fetch_chunk(i + 64, bt_nxt, meta_nxt);
+      }
+    }
+    // Loads are issued for every position, placeholders included (they read
+    // block 0 and are never used): a load under a branch would make the
+    // compiler's wait counts for the whole ring conservative.
+    int mk = __builtin_amdgcn_readlane(meta_cur, i & 63);
+    int phys = __builtin_amdgcn_readlane(bt_cur, i & 63);
+    if (!(mk & kMetaValid)) phys = 0;
+    if ((unsigned)phys >= (unsigned)a.num_blocks) {
+      mk |= kMetaBad;
+      phys = 0;
+    }
+    const int g = (mk >> kMetaHeadShift) & 0xffff;
+    poff[slot] = ((size_t)phys * H + g) * kPageBytes;
+    T::load_k(ring_k[slot], kbase + poff[slot], ko);
+    meta_k[slot] = mk;
+  };
+  auto issue_v = [&](int vslot, int kslot) { T::load_v(ring_v[vslot], vbase + poff[kslot], vo); };
+
+  float m = -INFINITY, lsum = 0.f;
+  bool bad = false;
+  f32x4 acc[D / 16];
+#pragma unroll
+  for (int t = 0; t < D / 16; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // One page of the online softmax (as in the fixed schedule).
+  auto page_math = [&](int kslot, int vslot, int nvalid, auto masked_tag) {
+    constexpr bool kMasked = decltype(masked_tag)::value;
+    const f32x4 s = T::scores(ring_k[kslot], q_cur);
+    float sc[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) sc[e] = (!kMasked || 4 * jj + e < nvalid) ? s[e] * kmul_cur : -INFINITY;
+    const float mx = wave_max_rows(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])));
+    const float mnew = fmaxf(m, mx);
+    const float alpha = exp2_fast(m - mnew);
+    float pr[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) pr[e] = exp2_fast(sc[e] - mnew);
+    const typename T::P pk = T::pack(pr);
+    lsum = lsum * alpha + T::psum(pk);
+    m = mnew;
+    if (__any(alpha != 1.0f)) {
+#pragma unroll
+      for (int t = 0; t < D / 16; ++t) acc[t] *= alpha;
+    }
+#pragma unroll
+    for (int t = 0; t < D / 16; ++t) {
+      typename T::A4 va = T::pvt(ring_v[vslot], t);
+      if constexpr (kMasked) va = T::zero_tail(va, jj, nvalid);
+      acc[t] = T::pv(va, pk, acc[t]);
+    }
+  };
+
+  // End of the current piece: flush the state, move to the next piece.
+  auto flush = [&]() {
+    const float l = wave_sum_rows(lsum);
+    const bool direct = cur.pair_first >= y0 && cur.pair_end <= y1;
+    if (direct) {
+      const size_t row0 = (size_t)cur.b * a.num_q_heads + (size_t)cur.g * G;
+      const bool bad_len = cur.L < 0 || cur.L > mbs * kBlock;
+      if (bad_len || cur.L == 0) {
+        const float fill = bad_len ? __builtin_nanf("") : 0.f;
+        for (int i = lane; i < G * D; i += 64) store_out<IO>(a.out, row0 * D + i, fill);
+        if (a.lse_out && lane < G) a.lse_out[row0 + lane] = bad_len ? fill : -INFINITY;
+      } else if (head_ok) {
+        const float inv = bad ? __builtin_nanf("") : vmul_cur / l;
+#pragma unroll
+        for (int t = 0; t < D / 16; ++t)
+          store_out4<IO>(a.out, (row0 + rr) * D + 16 * t + 4 * jj, acc[t] * inv);
+        if (jj == 0 && a.lse_out)
+          a.lse_out[row0 + rr] = bad ? __builtin_nanf("") : (m + log2_fast(l)) * kLn2;
+      }
+    } else {
+      const int slot = cur.pair_first <= y0 ? 0 : 1;
+      if (head_ok) {
+        float* row = sm.acc_row(w, slot, rr);
+#pragma unroll
+        for (int t = 0; t < D / 16; ++t) *reinterpret_cast<f32x4*>(row + 16 * t + 4 * jj) = acc[t];
+        if (jj == 0) {
+          sm.m[sm.mi(w, slot, rr)] = m;
+          sm.l[sm.mi(w, slot, rr)] = l;
+        }
+      }
+      if (lane == 0) sm.bad[w * 2 + slot] = bad ? 1 : 0;
+    }
+    m = -INFINITY;
+    lsum = 0.f;
+    bad = false;
+#pragma unroll
+    for (int t = 0; t < D / 16; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (has_nxt) {
+      cur = nxt;
+      q_cur = q_nxt;
+      kmul_cur = kmul_nxt;
+      vmul_cur = vmul_nxt;
+      has_nxt = cur.pair_end < y1;
+      if (has_nxt) {
+        qcursor_at(nxt, a, sm, cur.pair_end, y1);
+        T::load_q(q_nxt, q_row(nxt), jj);
+        if constexpr (kFp8) {
+          kmul_nxt = a.scale * kLog2e * a.k_scale[nxt.g];
+          vmul_nxt = a.v_scale[nxt.g];
+        }
+      }
+    }
+  };
+
+  auto compute = [&](int kslot, int vslot) {
+    const int mk = meta_k[kslot];
+    const int nvalid = mk & kMetaValid;
+    if (nvalid != 0) {
+      if (mk & kMetaBad) bad = true;
+      if (nvalid == kBlock)
+        page_math(kslot, vslot, nvalid, std::integral_constant<bool, false>{});
+      else
+        page_math(kslot, vslot, nvalid, std::integral_constant<bool, true>{});
+    }
+    if (mk & kMetaEnd) flush();
+  };
+
+  // The ring, as in the fixed schedule: a steady-state block of kU positions
+  // that issues unconditionally, then a peeled remainder.
+  constexpr int kU = kKS * kVS / gcd_c(kKS, kVS);
+  // Two copies of the loop, as in the fixed schedule: without a chunk fetch
+  // inside it (quarters of at most 64 positions) the ring's wait counts stay
+  // exact.
+  auto run_ring = [&](auto refresh_tag) {
+#pragma unroll
+    for (int j = 0; j < dK; ++j)
+      if (j < n) issue_k(j, j, refresh_tag);
+#pragma unroll
+    for (int j = 0; j < dV; ++j)
+      if (j < n) issue_v(j, j);
+    int i0 = 0;
+    for (; i0 + kU - 1 + kAhead < n; i0 += kU) {
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        issue_k((u + dK) % kKS, i0 + u + dK, refresh_tag);
+        issue_v((u + dV) % kVS, (u + dV) % kKS);
+        compute(u % kKS, u % kVS);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kU + kAhead; ++u) {
+      const int i = i0 + u;
+      if (i < n) {
+        if (i + dK < n) issue_k((u + dK) % kKS, i + dK, refresh_tag);
+        if (i + dV < n) issue_v((u + dV) % kVS, (u + dV) % kKS);
+        compute(u % kKS, u % kVS);
+      }
+    }
+  };
+  if (n > 64)
+    run_ring(std::integral_constant<bool, true>{});
+  else
+    run_ring(std::integral_constant<bool, false>{});
+}
+
+// Workgroup barrier that orders LDS only: each wave waits for its own LDS
+// operations, not for its global stores (which __syncthreads() would wait
+// for as well).
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// Combine the LDS slots of waves wa .. wb that hold one piece of the share
+// (pair (b, g) starting at line position pair_first) and write the output
+// (nparts == 1) or the piece's partial result (slot slot0 + k). yq(ww): the
+// quarter starts.
+template <typename IO, typename KV, int D, typename YQ>
+__device__ __forceinline__ void combine_slots(const Params& a, const BalSm<D>& sm, int b, int g, int pair_first,
+                              int wa, int wb, int k, int nparts, int slot0, YQ yq) {
+  const int tid = threadIdx.x;
+  const int G = a.group;
+  const int hq0 = g * G;
+  // per wave: does it hold the piece, and in which slot
+  bool on[kWaves];
+  int sl[kWaves];
+  int bad = 0;
+#pragma unroll
+  for (int ww = 0; ww < kWaves; ++ww) {
+    on[ww] = ww >= wa && ww <= wb;
+    sl[ww] = on[ww] && pair_first > yq(ww) ? 1 : 0;
+    if (on[ww]) bad |= sm.bad[ww * 2 + sl[ww]];
+  }
+  float vmul = 1.0f;
+  if constexpr (std::is_same<KV, FP8>::value) vmul = a.v_scale[g];
+  const bool split = nparts > 1;
+  const size_t slot = (size_t)slot0 + k;
+  const brsrc wr_slot = buffer_rsrc(a.ws_o + slot * G * D, (uint32_t)(G * D * sizeof(float)));
+  for (int i = tid; i < G * (D / 4); i += kThreads) {   // (head, 4-float quad)
+    const int h = i / (D / 4), d = 4 * (i - h * (D / 4));
+    float mv[kWaves], lv[kWaves];
+    f32x4 av[kWaves];
+#pragma unroll
+    for (int ww = 0; ww < kWaves; ++ww) {   // all reads first, then the arithmetic
+      mv[ww] = sm.m[sm.mi(ww, sl[ww], h)];
+      lv[ww] = sm.l[sm.mi(ww, sl[ww], h)];
+      av[ww] = *reinterpret_cast<const f32x4*>(sm.acc_row(ww, sl[ww], h) + d);
+    }
+    float M = -INFINITY;
+#pragma unroll
+    for (int ww = 0; ww < kWaves; ++ww)
+      if (on[ww]) M = fmaxf(M, mv[ww]);
+    float W = 0.f;
+    f32x4 o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ww = 0; ww < kWaves; ++ww) {
+      if (on[ww]) {
+        const float e = exp2_fast(mv[ww] - M);
+        W += e * lv[ww];
+        o += e * av[ww];
+      }
+    }
+    f32x4 val = {o[0] / W * vmul, o[1] / W * vmul, o[2] / W * vmul, o[3] / W * vmul};
+    float lse2 = M + log2_fast(W);
+    if (bad) {
+      val = f32x4{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
+      lse2 = __builtin_nanf("");
+    }
+    const size_t row = (size_t)b * a.num_q_heads + hq0 + h;
+    if (!split) {
+      store_out4<IO>(a.out, row * D + d, val);
+      if (d == 0 && a.lse_out) a.lse_out[row] = lse2 * kLn2;
+    } else {
+      st_agent4(wr_slot, (uint32_t)((h * D + d) * sizeof(float)), val);
+      if (d == 0) st_agent(a.ws_lse + slot * G + h, lse2);
+    }
+  }
+}
+
+template <typename IO, typename KV, int D>
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 pa_decode_balanced_kernel(const Params a) {
-  __shared__ Smem<D> sm;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = tid >> 6;
   const int B = a.batch, H = a.num_kv_heads, mbs = a.max_blocks_per_seq;
+  const BalSm<D> sm(a.group, B);
 
-  // line positions of this thread's sequences [bbeg, bbeg + per)
+  // lengths of this thread's sequences [bbeg, bbeg + per) into LDS, and the
+  // exclusive prefix sums of their line positions
   const int per = (B + kThreads - 1) / kThreads;
   const int bbeg = tid * per;
   int mine = 0;
   for (int i = 0; i < per; ++i) {
     const int bb = bbeg + i;
-    if (bb < B) mine += line_pages(a.context_lens[bb], mbs);
+    if (bb < B) {
+      const int L = a.context_lens[bb];
+      sm.len[bb] = L;
+      mine += line_pages(L, mbs);
+    }
   }
   int incl = mine;
 #pragma unroll
@@ -819,17 +1317,24 @@ pa_decode_balanced_kernel(const Params a) {
     const int y = __shfl_up(incl, d);
     if (lane >= d) incl += y;
   }
-  if (lane == 63) sm.wsum[w] = incl;
-  if (tid == 0) sm.b0 = sm.pre0 = 0;
+  if (lane == 63) sm.misc[w] = incl;
   __syncthreads();
-  int before = 0, total = 0;
+  int before = 0;
 #pragma unroll
-  for (int ww = 0; ww < kWaves; ++ww) {
-    const int v = sm.wsum[ww];
-    total += v;
-    if (ww < w) before += v;
+  for (int ww = 0; ww < kWaves; ++ww)
+    if (ww < w) before += sm.misc[ww];
+  int pre = before + incl - mine;
+  for (int i = 0; i < per; ++i) {
+    const int bb = bbeg + i;
+    if (bb < B) {
+      sm.pre[bb] = pre;
+      pre += line_pages(sm.len[bb], mbs);
+    }
   }
-  total = __builtin_amdgcn_readfirstlane(total);
+  if (tid == kThreads - 1) sm.pre[B] = before + incl;
+  __syncthreads();
+
+  const int total = __builtin_amdgcn_readfirstlane(sm.pre[B]);
   const int N = total * H;
   const int S = share_count(N, (int)gridDim.x);
   const int wg = blockIdx.x;
@@ -837,34 +1342,65 @@ pa_decode_balanced_kernel(const Params a) {
   const int x0 = share_start(wg, N, S);
   const int x1 = share_start(wg + 1, N, S);
 
-  // the sequence whose pairs hold line position x0
-  int pre = before + incl - mine;
-  for (int i = 0; i < per; ++i) {
-    const int bb = bbeg + i;
-    if (bb < B) {
-      const int cb = line_pages(a.context_lens[bb], mbs);
-      if (H * pre <= x0 && x0 < H * (pre + cb)) {
-        sm.b0 = bb;
-        sm.pre0 = pre;
-      }
-      pre += cb;
-    }
-  }
+  // this wave's quarter of the share
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+  auto yq = [&](int ww) { return x0 + share_start(ww, x1 - x0, kWaves); };
+  decode_quarter<IO, KV, D>(a, sm, yq(wu), yq(wu + 1));
   __syncthreads();
-  const int b0 = __builtin_amdgcn_readfirstlane(sm.b0);
-  const int pre0 = __builtin_amdgcn_readfirstlane(sm.pre0);
 
-  bool first = true;
+  // Pieces of the share whose state went through LDS, in three steps:
+  // 1. combine each one's wave slots; write the output of whole pairs and the
+  //    partial result of split ones (remembered in LDS);
+  // 2. once those stores are complete, count every split piece in on its
+  //    pair's counter (one thread per piece, all at once);
+  // 3. merge the pairs whose count this workgroup completed.
+  const int b0 = seq_of_uniform(sm.pre, B, H, x0);
+  const int pre0 = __builtin_amdgcn_readfirstlane(sm.pre[b0]);
+  int nsplit = 0;
   walk_share(
       wg, x0, x1, b0, pre0, B, H, N, S, mbs,
-      [&](int bb) { return __builtin_amdgcn_readfirstlane(a.context_lens[bb]); },
+      [&](int bb) { return __builtin_amdgcn_readfirstlane(sm.len[bb]); },
       [&](int bb, int L, const LinePiece& lp) {
-        if (!first) __syncthreads();   // the previous piece's LDS reads are done
-        first = false;
-        decode_piece<IO, KV, D>(a, sm, bb, lp.g, lp.pg_lo, [&]() {
-          return Piece{L, lp.pg_hi, lp.k, lp.nparts, lp.slot0};
-        });
+        const int cb = line_pages(L, mbs);
+        const int s0 = lp.x_end - (lp.pg_hi - lp.pg_lo);
+        const int pair_first = s0 - lp.pg_lo;
+        const int pair_end = pair_first + cb;
+        const int wa = share_of(s0 - x0, x1 - x0, kWaves);
+        const int wb = share_of(lp.x_end - 1 - x0, x1 - x0, kWaves);
+        if (wa == wb && pair_first >= yq(wa) && pair_end <= yq(wa + 1)) return;   // written by wave wa
+        combine_slots<IO, KV, D>(a, sm, bb, lp.g, pair_first, wa, wb, lp.k, lp.nparts, lp.slot0, yq);
+        if (lp.nparts > 1) {
+          if (tid == 0) {
+            int* e = sm.split + 4 * nsplit;
+            e[0] = bb;
+            e[1] = lp.g;
+            e[2] = lp.nparts;
+            e[3] = lp.slot0;
+          }
+          ++nsplit;
+        }
       });
+  if (nsplit == 0) return;   // uniform
+  __builtin_amdgcn_s_waitcnt(0);   // this wave's partial stores are complete
+  __syncthreads();
+  if (tid < nsplit) {
+    const int* e = sm.split + 4 * tid;
+    uint32_t* cnt = a.ws_cnt + (size_t)e[0] * H + e[1];
+    const uint32_t done = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    sm.split[4 * kMaxSplit + tid] = done == (uint32_t)(e[2] - 1);
+  }
+  lds_barrier();
+  for (int i = 0; i < nsplit; ++i) {
+    if (!__builtin_amdgcn_readfirstlane(sm.split[4 * kMaxSplit + i])) continue;   // uniform
+    const int bb = __builtin_amdgcn_readfirstlane(sm.split[4 * i]);
+    const int g = __builtin_amdgcn_readfirstlane(sm.split[4 * i + 1]);
+    const int np = __builtin_amdgcn_readfirstlane(sm.split[4 * i + 2]);
+    const int slot0 = __builtin_amdgcn_readfirstlane(sm.split[4 * i + 3]);
+    merge_partitions<IO, D>(a, sm.red, bb, g, slot0, np);
+    if (tid == 0)
+      __hip_atomic_store(a.ws_cnt + (size_t)bb * H + g, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    lds_barrier();   // the merge scratch is reused by the next pair
+  }
 }
 
 __global__ void fill_zero_kernel(uint8_t* p, size_t n) {
@@ -885,14 +1421,13 @@ struct WsLayout {
 
 static inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-// Shares of the balanced split per CU. The register budget lets a CU hold
-// three workgroups, but two larger shares per CU measure faster on MI355X
-// than three (and one per CU as fast on f16/bf16 caches, slower on fp8):
-// every share pays a fixed latency at its start (lengths, block ids, first
-// pages) and end (partial store and hand-off), so fewer, longer shares stream
-// a larger part of the time, while two workgroups still keep enough loads in
-// flight per CU.
-constexpr int kWgPerCu = 2;
+// Shares of the balanced split per CU. One share (one workgroup of four
+// waves with deep register rings) per CU measured as fast as two or three on
+// MI355X at streaming and faster overall: every share pays a fixed cost at
+// its start (lengths, block ids, first pages) and at its end (combining the
+// waves, partial results, the hand-off to the pair's merge), and fewer,
+// longer shares cut pairs into fewer pieces.
+constexpr int kWgPerCu = 1;
 
 // Shares of the balanced split on the current device, or -1.
 static int balanced_shares() {
@@ -915,7 +1450,7 @@ static bool shape_ok(const pa_shape* s) {
   if (s->num_blocks < 1) return false;
   if (s->partition_size == PA_SPLIT_BALANCED) {
     // the workgroup-wide scan covers the batch, and line positions fit int32
-    if (s->batch > kThreads * kScanPerThread) return false;
+    if (s->batch > kBalancedMaxBatch) return false;
     const long long line = (long long)s->batch * s->num_kv_heads * s->max_blocks_per_seq;
     return line + 4096LL * 3 < 0x7fffffffLL;   // + shares (4096 CUs at most, 3 per CU)
   }
@@ -953,7 +1488,8 @@ static WsLayout ws_layout(const pa_shape* s, int shares) {
 template <typename IO, typename KV, int D>
 static hipError_t launch(const Params& prm, dim3 grid, bool balanced, hipStream_t stream) {
   if (balanced)
-    hipLaunchKernelGGL((pa_decode_balanced_kernel<IO, KV, D>), grid, dim3(kThreads), 0, stream, prm);
+    hipLaunchKernelGGL((pa_decode_balanced_kernel<IO, KV, D>), grid, dim3(kThreads),
+                       bal_layout(prm.group, D, prm.batch).total, stream, prm);
   else
     hipLaunchKernelGGL((pa_decode_kernel<IO, KV, D>), grid, dim3(kThreads), 0, stream, prm);
   return hipGetLastError();
