@@ -60,6 +60,9 @@ def parse():
                     help="minimum host time spent timing the oracle")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-stream-ceiling", action="store_true")
+    ap.add_argument("--op", choices=["decode", "append"], default="decode",
+                    help="decode: the attention call (default); append: the paged KV "
+                         "append of one new token per sequence on the same workload")
     ap.add_argument("--pmc-pass", action="store_true",
                     help="run a 1 GiB device copy and 20 decode calls, print nothing else "
                          "(for rocprofv3 --pmc counter passes)")
@@ -156,6 +159,81 @@ def cpu_baseline(wl, gpu_out_f64, min_seconds):
     }
 
 
+def bench_append(args, torch, np, pkd, W):
+    """Time pa_kv_append (one new token per sequence, written at its context
+    length) on the workload's shape; bytes = rows read + cache bytes written."""
+    import oracle
+    spec = W.SPECS[args.workload]
+    wl = W.make_workload(spec)
+    dev = torch.device("cuda:0")
+    t = W.to_device(wl, dev)
+    B, H, D = spec.batch, spec.num_kv_heads, spec.head_dim
+    src = spec.io_dtype
+    rng = np.random.default_rng(1000 + args.workload)
+    with np.errstate(over="ignore"):
+        k_new = W._to_storage(rng.standard_normal((B, H, D)).astype(np.float32), src)
+        v_new = W._to_storage(rng.standard_normal((B, H, D)).astype(np.float32), src)
+    pos = np.minimum(wl.context_lens.astype(np.int32), 16 * spec.max_blocks_per_seq - 1)
+    kn = W.storage_tensor(k_new, src).to(dev)
+    vn = W.storage_tensor(v_new, src).to(dev)
+    pt = torch.from_numpy(pos).to(dev)
+    pool_bytes = t["k_cache"].numel() * t["k_cache"].element_size() * 2
+    reps = max(1, math.ceil(3 * MALL_BYTES / pool_bytes))
+    kcs = [t["k_cache"]] + [t["k_cache"].clone() for _ in range(reps - 1)]
+    vcs = [t["v_cache"]] + [t["v_cache"].clone() for _ in range(reps - 1)]
+    stream = torch.cuda.current_stream()
+
+    from paged_kv_decode_05_amd._lib import prepare_append
+    calls = [prepare_append(kn, vn, pt, t["block_table"], kcs[i], vcs[i], k_scale=t["k_scale"],
+                            v_scale=t["v_scale"], stream=stream) for i in range(reps)]
+
+    def call(i):
+        calls[i % reps]()
+
+    for i in range(args.warmup):
+        call(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(args.steps):
+        call(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    s_src = oracle.ELEM_BYTES[src]
+    s_kv = oracle.ELEM_BYTES[spec.kv_dtype]
+    moved = B * H * D * 2 * (s_src + s_kv) + B * 4 * 2
+    gbps = moved / (ms / 1e3) / 1e9
+    rec = {
+        "metric": "paged KV append GB/s (new K/V rows read + cache bytes written)",
+        "value": round(gbps, 3), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 6), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None,
+        "dtype": src + ("" if spec.kv_dtype == src else "->fp8_e4m3"),
+        "data": "synthetic (seeded N(0,1) rows, the workload's block table)",
+        "config": {"workload": spec.name, "op": "kv_append", "batch": B, "kv_heads": H,
+                   "head_dim": D, "bytes_per_step": moved},
+        "roofline": {"bound": "hbm", "achieved": round(gbps, 3), "peak": PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(gbps / PEAK_GBPS, 6), "traffic": None},
+        "note": "one token per sequence: a few hundred KB per call, so the call is "
+                "launch-latency bound, not bandwidth bound",
+    }
+    if not args.no_cpu_baseline:
+        reps_c, t0 = 0, time.perf_counter()
+        while True:
+            oracle.kv_append_ref(wl.k_cache, wl.v_cache, k_new, v_new, wl.block_table, pos, src,
+                                 spec.kv_dtype, wl.k_scale, wl.v_scale)
+            reps_c += 1
+            el = time.perf_counter() - t0
+            if el >= min(args.cpu_seconds, 5.0):
+                break
+        rec["cpu_baseline"] = {"value": round(moved / (el / reps_c) / 1e9, 6), "unit": "GB/s",
+                               "cores": 1, "kind": "oracle",
+                               "sample": f"the whole call ({B} sequences), {reps_c} oracle passes "
+                                         f"in {el:.1f} s (pure Python loop, one thread)"}
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -169,6 +247,9 @@ def main():
 
     import paged_kv_decode_05_amd as pkd
     from paged_kv_decode_05_amd import workloads as W
+
+    if args.op == "append":
+        return bench_append(args, torch, np, pkd, W)
 
     spec = W.SPECS[args.workload]
     wl = W.make_workload(spec)

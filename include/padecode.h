@@ -141,6 +141,37 @@ pa_status pa_decode(const pa_shape* shape, const void* q, const void* k_cache,
                     size_t workspace_bytes, void* out, float* lse_out,
                     void* stream);
 
+/* Paged KV append: write each sequence's new token K and V rows into its
+ * block and slot of the caches, as the decode step does right before
+ * attention ("rvLLM: High-performance LLM inference in Rust", section "Kernel
+ * Compiler Stack", per-layer decode steps: the KV cache write follows RoPE and
+ * precedes attention), into an f16/bf16/f32 or FP8 cache ("rvLLM", sections
+ * "What's Inside" and "Optional Features"; "Litellama", section "Features").
+ *   shape        batch, num_kv_heads, head_dim, block_size (16),
+ *                max_blocks_per_seq, num_blocks as for pa_decode
+ *                (num_q_heads and partition_size are not used)
+ *   k_new, v_new [batch][num_kv_heads][head_dim] in src_dtype
+ *                (PA_F32, PA_F16 or PA_BF16), device memory
+ *   positions    int32 [batch]: the token position p to write (for a decode
+ *                step, the context length before the token); p < 0 skips
+ *                the sequence
+ *   block_table  int32 [batch][max_blocks_per_seq], as for pa_decode
+ *   kv_dtype     src_dtype (the bits are copied) or PA_FP8_E4M3: the code is
+ *                round-to-nearest-even of clamp(x / scale, -448, 448) with
+ *                the division in float32 and scale = k_scale[g] (v_scale[g]),
+ *                NaN becoming 0x7F
+ *   k_cache, v_cache  written in place, layouts as for pa_decode
+ * Row p of sequence b goes to block block_table[b][p / 16], slot p % 16. A
+ * position at or past 16 * max_blocks_per_seq, or a block id outside the
+ * pool, writes nothing (never outside the caches). Two sequences must not
+ * name the same (block, slot). Enqueued on `stream`; errors as for
+ * pa_decode. */
+pa_status pa_kv_append(const pa_shape* shape, const void* k_new, const void* v_new,
+                       const int32_t* positions, const int32_t* block_table,
+                       pa_dtype src_dtype, pa_dtype kv_dtype, const float* k_scale,
+                       const float* v_scale, void* k_cache, void* v_cache,
+                       void* stream);
+
 /* Zero-fill a workspace on `stream` with a fill kernel (safe to capture in a
  * HIP graph). */
 pa_status pa_workspace_reset(void* workspace, size_t workspace_bytes,

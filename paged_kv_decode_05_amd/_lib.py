@@ -14,8 +14,8 @@ PA_F32, PA_F16, PA_BF16, PA_FP8_E4M3 = 0, 1, 2, 3
 SPLIT_BALANCED = -1   # partition_size value of the balanced split (PA_SPLIT_BALANCED)
 DTYPE_CODE = {"f32": PA_F32, "f16": PA_F16, "bf16": PA_BF16, "fp8_e4m3": PA_FP8_E4M3}
 
-EXPORTED = ("pa_decode", "pa_decode_workspace_bytes", "pa_workspace_reset",
-            "pa_status_str")
+EXPORTED = ("pa_decode", "pa_decode_workspace_bytes", "pa_kv_append",
+            "pa_workspace_reset", "pa_status_str")
 
 
 class PaError(RuntimeError):
@@ -54,6 +54,9 @@ def load_library(path=None):
                               ctypes.c_int, ctypes.c_int, vp, vp, vp, ctypes.c_size_t, vp,
                               vp, vp]
     lib.pa_decode.restype = ctypes.c_int
+    lib.pa_kv_append.argtypes = [ctypes.POINTER(PaShape), vp, vp, vp, vp, ctypes.c_int,
+                                 ctypes.c_int, vp, vp, vp, vp, vp]
+    lib.pa_kv_append.restype = ctypes.c_int
     lib.pa_workspace_reset.argtypes = [vp, ctypes.c_size_t, vp]
     lib.pa_workspace_reset.restype = ctypes.c_int
     lib.pa_status_str.argtypes = [ctypes.c_int]
@@ -173,3 +176,64 @@ def prepare(q, k_cache, v_cache, block_table, context_lens, scale, *, k_scale=No
     keep = (shape, q, k_cache, v_cache, block_table, context_lens, k_scale, v_scale,
             workspace, out, lse_out)
     return Prepared(lib, args, out, keep)
+
+
+def kv_append(k_new, v_new, positions, block_table, k_cache, v_cache, *, k_scale=None,
+              v_scale=None, stream=None):
+    """Write k_new / v_new [B, Hkv, D] (float32 | float16 | bfloat16) into the
+    caches at token positions[b] (int32 [B]; < 0 skips) through block_table,
+    in place; an fp8 cache (float8_e4m3fn / uint8) quantises with the float32
+    per-KV-head k_scale / v_scale. Returns (k_cache, v_cache)."""
+    prepare_append(k_new, v_new, positions, block_table, k_cache, v_cache, k_scale=k_scale,
+                   v_scale=v_scale, stream=stream)()
+    return k_cache, v_cache
+
+
+class PreparedAppend:
+    """A pa_kv_append call with its arguments marshalled once."""
+
+    def __init__(self, lib, args, keep):
+        self._fn = lib.pa_kv_append
+        self._args = args
+        self._keep = keep
+
+    def __call__(self):
+        _check(self._fn(*self._args))
+
+
+def prepare_append(k_new, v_new, positions, block_table, k_cache, v_cache, *, k_scale=None,
+                   v_scale=None, stream=None):
+    """Validate and marshal a kv_append call; calling the result enqueues it."""
+    import torch
+    lib = load_library()
+    src = _torch_dtype_name(k_new)
+    kv = _torch_dtype_name(k_cache)
+    if (src not in ("f32", "f16", "bf16") or _torch_dtype_name(v_new) != src or kv is None
+            or _torch_dtype_name(v_cache) != kv):
+        raise PaError(3, f"unsupported dtypes k_new={k_new.dtype} k_cache={k_cache.dtype}")
+    for name, t in (("k_new", k_new), ("v_new", v_new), ("positions", positions),
+                    ("block_table", block_table), ("k_cache", k_cache), ("v_cache", v_cache)):
+        if not t.is_cuda or not t.is_contiguous():
+            raise PaError(2, f"{name} must be a contiguous device tensor")
+    if positions.dtype != torch.int32 or block_table.dtype != torch.int32:
+        raise PaError(3, "positions and block_table must be int32")
+    if k_new.dim() != 3 or tuple(v_new.shape) != tuple(k_new.shape) or k_cache.dim() != 5:
+        raise PaError(2, "expected k_new, v_new [B,Hkv,D] and caches in the decode layout")
+    B, H, D = k_new.shape
+    nb = k_cache.shape[0]
+    if (k_cache.shape[1] != H or k_cache.shape[2] * k_cache.shape[4] != D
+            or tuple(v_cache.shape) != (nb, H, D, k_cache.shape[3])
+            or tuple(positions.shape) != (B,) or block_table.dim() != 2
+            or block_table.shape[0] != B):
+        raise PaError(2, "inconsistent tensor shapes")
+    shape = PaShape(batch=B, num_q_heads=H, num_kv_heads=H, head_dim=D,
+                    block_size=k_cache.shape[3], max_blocks_per_seq=block_table.shape[1],
+                    num_blocks=nb, partition_size=0)
+    s = stream if stream is not None else torch.cuda.current_stream()
+    args = (ctypes.byref(shape), k_new.data_ptr(), v_new.data_ptr(), positions.data_ptr(),
+            block_table.data_ptr(), DTYPE_CODE[src], DTYPE_CODE[kv],
+            k_scale.data_ptr() if k_scale is not None else None,
+            v_scale.data_ptr() if v_scale is not None else None,
+            k_cache.data_ptr(), v_cache.data_ptr(), s.cuda_stream)
+    keep = (shape, k_new, v_new, positions, block_table, k_cache, v_cache, k_scale, v_scale)
+    return PreparedAppend(lib, args, keep)

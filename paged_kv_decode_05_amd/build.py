@@ -22,21 +22,24 @@ COMMON = [
 ]
 
 TARGETS = [
-    (os.path.join(HERE, "csrc", "pa_decode.hip"), os.path.join(HERE, "libpadecode.so")),
-    (os.path.join(ROOT, "tests", "probes", "probes.hip"),
+    ([os.path.join(HERE, "csrc", "pa_decode.hip"), os.path.join(HERE, "csrc", "pa_append.hip")],
+     os.path.join(HERE, "libpadecode.so")),
+    ([os.path.join(ROOT, "tests", "probes", "probes.hip")],
      os.path.join(ROOT, "tests", "probes", "libpaprobes.so")),
 ]
 
 
-def build_one(src, dst, verbose=False):
+def build_one(srcs, dst, verbose=False):
+    if isinstance(srcs, str):
+        srcs = [srcs]
     tmp = dst + ".tmp"
-    cmd = [HIPCC, *COMMON, src, "-o", tmp]
+    cmd = [HIPCC, *COMMON, *srcs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
     out = "\n".join(l for l in res.stdout.splitlines() if "packed-fp32-ops" not in l)
     if res.returncode != 0:
-        raise RuntimeError(f"hipcc failed for {src}:\n{out}")
+        raise RuntimeError(f"hipcc failed for {srcs}:\n{out}")
     if verbose and out.strip():
         print(out)
     os.replace(tmp, dst)

@@ -134,3 +134,27 @@ def test_balanced_split_shapes_pass_validation():
         s = shape(partition_size=-1, **kw)
         assert call(s, ws=FAKE, wsb=1 << 30) == 6, kw
         assert lib.pa_decode_workspace_bytes(ctypes.byref(s)) == 0
+
+
+def call_append(s, src=1, kv=1, ks=None, vs=None, kn=FAKE, vn=FAKE, pos=FAKE, bt=FAKE,
+                kc=FAKE, vc=FAKE):
+    lib = _lib.load_library()
+    sp = ctypes.byref(s) if s is not None else None
+    return lib.pa_kv_append(sp, kn, vn, pos, bt, src, kv, ks, vs, kc, vc, None)
+
+
+def test_append_rejects_bad_arguments_before_any_launch():
+    assert call_append(None) == 1
+    for kw in ("kn", "vn", "pos", "bt", "kc", "vc"):
+        assert call_append(shape(), **{kw: None}) == 1, kw
+    assert call_append(shape(), src=1, kv=3) == 1                  # fp8 without scales
+    assert call_append(shape(head_dim=96)) == 2
+    assert call_append(shape(block_size=8)) == 2
+    assert call_append(shape(num_kv_heads=0)) == 2
+    assert call_append(shape(max_blocks_per_seq=0)) == 2
+    assert call_append(shape(), src=1, kv=2) == 3                  # f16 rows into a bf16 cache
+    assert call_append(shape(), src=3, kv=3, ks=FAKE, vs=FAKE) == 3   # fp8 rows
+    assert call_append(shape(), kn=FAKE + 1) == 5
+    assert call_append(shape(), kc=FAKE + 8) == 5
+    assert call_append(shape(), pos=FAKE + 2) == 5
+    assert call_append(shape(batch=0)) == 0                         # empty batch: no-op
