@@ -60,9 +60,11 @@ def parse():
                     help="minimum host time spent timing the oracle")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-stream-ceiling", action="store_true")
-    ap.add_argument("--op", choices=["decode", "append"], default="decode",
+    ap.add_argument("--op", choices=["decode", "append", "merge"], default="decode",
                     help="decode: the attention call (default); append: the paged KV "
-                         "append of one new token per sequence on the same workload")
+                         "append of one new token per sequence on the same workload; "
+                         "merge: the log-sum-exp merge of --shards position shards")
+    ap.add_argument("--shards", type=int, default=8, help="shards for --op merge")
     ap.add_argument("--pmc-pass", action="store_true",
                     help="run a 1 GiB device copy and 20 decode calls, print nothing else "
                          "(for rocprofv3 --pmc counter passes)")
@@ -234,6 +236,66 @@ def bench_append(args, torch, np, pkd, W):
     print(json.dumps(rec), flush=True)
 
 
+def bench_merge(args, torch, np, pkd, W):
+    """Time pa_lse_merge of --shards per-shard results on the workload's
+    (sequence, query head) rows; bytes = shard outputs and lse read + output
+    written."""
+    import oracle
+    spec = W.SPECS[args.workload]
+    B, Hq, D = spec.batch, spec.num_q_heads, spec.head_dim
+    S, rows, dt = args.shards, B * Hq, spec.io_dtype
+    rng = np.random.default_rng(2000 + args.workload)
+    o = W._to_storage(rng.standard_normal((S, rows, D)).astype(np.float32), dt)
+    lse = (rng.standard_normal((S, rows)) * 3).astype(np.float32)
+    dev = torch.device("cuda:0")
+    ot = W.storage_tensor(o, dt).to(dev)
+    lt = torch.from_numpy(lse).to(dev)
+    out = torch.empty((rows, D), dtype=ot.dtype, device=dev)
+    lout = torch.empty(rows, device=dev)
+    stream = torch.cuda.current_stream()
+    lib = pkd.load_library()
+    from paged_kv_decode_05_amd._lib import DTYPE_CODE
+    args_c = (S, rows, D, ot.data_ptr(), lt.data_ptr(), DTYPE_CODE[dt], out.data_ptr(),
+              lout.data_ptr(), stream.cuda_stream)
+    for _ in range(args.warmup):
+        assert lib.pa_lse_merge(*args_c) == 0
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        lib.pa_lse_merge(*args_c)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    es = oracle.ELEM_BYTES[dt]
+    moved = S * rows * (D * es + 4) + rows * (D * es + 4)
+    gbps = moved / (ms / 1e3) / 1e9
+    rec = {
+        "metric": "log-sum-exp shard merge GB/s (shard outputs + lse read, output written)",
+        "value": round(gbps, 3), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 6), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": dt,
+        "data": "synthetic (seeded N(0,1) shard outputs, N(0,9) lse)",
+        "config": {"workload": spec.name, "op": "lse_merge", "shards": S, "rows": rows,
+                   "head_dim": D, "bytes_per_step": moved},
+        "roofline": {"bound": "hbm", "achieved": round(gbps, 3), "peak": PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(gbps / PEAK_GBPS, 6), "traffic": None},
+        "note": "decode-sized rows: under 1 MB per call, so the call is launch-latency bound",
+    }
+    if not args.no_cpu_baseline:
+        reps_c, t0 = 0, time.perf_counter()
+        while True:
+            oracle.shard_merge_ref(o, lse, dt)
+            reps_c += 1
+            el = time.perf_counter() - t0
+            if el >= min(args.cpu_seconds, 5.0):
+                break
+        rec["cpu_baseline"] = {"value": round(moved / (el / reps_c) / 1e9, 6), "unit": "GB/s",
+                               "cores": 1, "kind": "oracle",
+                               "sample": f"the whole call, {reps_c} oracle passes in {el:.1f} s"}
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -250,6 +312,8 @@ def main():
 
     if args.op == "append":
         return bench_append(args, torch, np, pkd, W)
+    if args.op == "merge":
+        return bench_merge(args, torch, np, pkd, W)
 
     spec = W.SPECS[args.workload]
     wl = W.make_workload(spec)

@@ -172,6 +172,27 @@ pa_status pa_kv_append(const pa_shape* shape, const void* k_new, const void* v_n
                        const float* v_scale, void* k_cache, void* v_cache,
                        void* stream);
 
+/* Merge decode-attention results computed on disjoint position shards of
+ * every sequence (decode context parallelism: "RapidLLM", feature table, row
+ * "Decode context parallelism": partial attention over disjoint KV ranges is
+ * combined by log-sum-exp). For each row r (a (sequence, query head) pair):
+ *     M = max_s lse_s[r],  w_s = exp(lse_s[r] - M),
+ *     out[r] = sum_s w_s * shard_out[s][r] / sum_s w_s,
+ *     lse_out[r] = M + log sum_s w_s                       (natural log)
+ * summed over s = 0 .. num_shards-1 in that order.
+ *   shard_out  [num_shards][rows][head_dim] in dtype (F32, F16 or BF16),
+ *              e.g. the out of one pa_decode call per shard
+ *   shard_lse  float32 [num_shards][rows], natural log (pa_decode's lse_out)
+ *   out        [rows][head_dim] in dtype;  lse_out float32 [rows] or NULL
+ * A shard whose lse is -inf (no tokens) contributes nothing; a row with no
+ * contributing shard gets out = 0 and lse = -inf; a NaN lse in any shard
+ * makes that row's out and lse NaN. head_dim: a multiple of 4, 4 .. 1024;
+ * shard_out and out 16-byte aligned. Enqueued on `stream`; errors as for
+ * pa_decode. */
+pa_status pa_lse_merge(int32_t num_shards, int32_t rows, int32_t head_dim,
+                       const void* shard_out, const float* shard_lse, pa_dtype dtype,
+                       void* out, float* lse_out, void* stream);
+
 /* Zero-fill a workspace on `stream` with a fill kernel (safe to capture in a
  * HIP graph). */
 pa_status pa_workspace_reset(void* workspace, size_t workspace_bytes,

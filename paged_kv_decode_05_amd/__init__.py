@@ -5,7 +5,7 @@ Python side only marshals torch tensors into its C ABI. Importing this package
 does not load the library; `decode()` does, and raises if it is missing.
 """
 from ._lib import (SPLIT_BALANCED, PaError, Prepared, decode, kv_append, library_path,
-                   load_library, prepare, reset_workspace, workspace_bytes)
+                   load_library, lse_merge, prepare, reset_workspace, workspace_bytes)
 
 __all__ = ["SPLIT_BALANCED", "PaError", "Prepared", "decode", "kv_append", "library_path",
-           "load_library", "prepare", "reset_workspace", "workspace_bytes"]
+           "load_library", "lse_merge", "prepare", "reset_workspace", "workspace_bytes"]

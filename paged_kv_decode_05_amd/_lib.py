@@ -14,7 +14,7 @@ PA_F32, PA_F16, PA_BF16, PA_FP8_E4M3 = 0, 1, 2, 3
 SPLIT_BALANCED = -1   # partition_size value of the balanced split (PA_SPLIT_BALANCED)
 DTYPE_CODE = {"f32": PA_F32, "f16": PA_F16, "bf16": PA_BF16, "fp8_e4m3": PA_FP8_E4M3}
 
-EXPORTED = ("pa_decode", "pa_decode_workspace_bytes", "pa_kv_append",
+EXPORTED = ("pa_decode", "pa_decode_workspace_bytes", "pa_kv_append", "pa_lse_merge",
             "pa_workspace_reset", "pa_status_str")
 
 
@@ -57,6 +57,9 @@ def load_library(path=None):
     lib.pa_kv_append.argtypes = [ctypes.POINTER(PaShape), vp, vp, vp, vp, ctypes.c_int,
                                  ctypes.c_int, vp, vp, vp, vp, vp]
     lib.pa_kv_append.restype = ctypes.c_int
+    lib.pa_lse_merge.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, vp, vp,
+                                 ctypes.c_int, vp, vp, vp]
+    lib.pa_lse_merge.restype = ctypes.c_int
     lib.pa_workspace_reset.argtypes = [vp, ctypes.c_size_t, vp]
     lib.pa_workspace_reset.restype = ctypes.c_int
     lib.pa_status_str.argtypes = [ctypes.c_int]
@@ -237,3 +240,28 @@ def prepare_append(k_new, v_new, positions, block_table, k_cache, v_cache, *, k_
             k_cache.data_ptr(), v_cache.data_ptr(), s.cuda_stream)
     keep = (shape, k_new, v_new, positions, block_table, k_cache, v_cache, k_scale, v_scale)
     return PreparedAppend(lib, args, keep)
+
+
+def lse_merge(shard_out, shard_lse, *, out=None, lse_out=None, stream=None):
+    """Merge per-shard decode results: shard_out [S, ..., D] (float32 | float16 |
+    bfloat16), shard_lse float32 [S, ...] (natural log) -> out [..., D] (and
+    lse_out [...] if given). Returns out."""
+    import torch
+    lib = load_library()
+    dt = _torch_dtype_name(shard_out)
+    if dt not in ("f32", "f16", "bf16") or shard_lse.dtype != torch.float32:
+        raise PaError(3, f"unsupported dtypes {shard_out.dtype}, {shard_lse.dtype}")
+    for name, t in (("shard_out", shard_out), ("shard_lse", shard_lse)):
+        if not t.is_cuda or not t.is_contiguous():
+            raise PaError(2, f"{name} must be a contiguous device tensor")
+    if shard_out.dim() < 2 or tuple(shard_lse.shape) != tuple(shard_out.shape[:-1]):
+        raise PaError(2, "expected shard_out [S, ..., D] and shard_lse [S, ...]")
+    S, D = shard_out.shape[0], shard_out.shape[-1]
+    rows = shard_lse[0].numel()
+    if out is None:
+        out = torch.empty(shard_out.shape[1:], dtype=shard_out.dtype, device=shard_out.device)
+    s = stream if stream is not None else torch.cuda.current_stream()
+    _check(lib.pa_lse_merge(S, rows, D, shard_out.data_ptr(), shard_lse.data_ptr(),
+                            DTYPE_CODE[dt], out.data_ptr(),
+                            lse_out.data_ptr() if lse_out is not None else None, s.cuda_stream))
+    return out

@@ -158,3 +158,19 @@ def test_append_rejects_bad_arguments_before_any_launch():
     assert call_append(shape(), kc=FAKE + 8) == 5
     assert call_append(shape(), pos=FAKE + 2) == 5
     assert call_append(shape(batch=0)) == 0                         # empty batch: no-op
+
+
+def test_lse_merge_rejects_bad_arguments_before_any_launch():
+    lib = _lib.load_library()
+    m = lib.pa_lse_merge
+    assert m(0, 4, 128, FAKE, FAKE, 1, FAKE, None, None) == 2        # no shards
+    assert m(2, -1, 128, FAKE, FAKE, 1, FAKE, None, None) == 2
+    assert m(2, 4, 6, FAKE, FAKE, 1, FAKE, None, None) == 2          # head_dim % 4
+    assert m(2, 4, 2048, FAKE, FAKE, 1, FAKE, None, None) == 2
+    assert m(2, 4, 128, None, FAKE, 1, FAKE, None, None) == 1
+    assert m(2, 4, 128, FAKE, None, 1, FAKE, None, None) == 1
+    assert m(2, 4, 128, FAKE, FAKE, 1, None, None, None) == 1
+    assert m(2, 4, 128, FAKE, FAKE, 3, FAKE, None, None) == 3        # fp8 outputs
+    assert m(2, 4, 128, FAKE + 8, FAKE, 1, FAKE, None, None) == 5
+    assert m(2, 4, 128, FAKE, FAKE + 2, 1, FAKE, None, None) == 5
+    assert m(2, 0, 128, FAKE, FAKE, 1, FAKE, None, None) == 0        # no rows: no-op
