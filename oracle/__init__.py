@@ -14,11 +14,12 @@ from .paged_decode import (BLOCK_SIZE, attend, gather_kv, lse_merge, page_x,
                            paged_decode_ref, paged_decode_split_ref)
 from .kv_append import e4m3_encode, kv_append_ref, quantize_e4m3, widen_to_f32
 from .shard_merge import shard_merge_ref
+from .block_pool import BlockPoolRef, PoolError, chain_hash, fnv1a64
 
 __all__ = [
     "E4M3_TABLE", "ELEM_BYTES", "STORAGE", "decode", "decode_bf16",
     "decode_e4m3", "decode_f16", "decode_f32", "e4m3_value", "BLOCK_SIZE",
     "attend", "gather_kv", "lse_merge", "page_x", "paged_decode_ref",
     "paged_decode_split_ref", "e4m3_encode", "kv_append_ref", "quantize_e4m3",
-    "widen_to_f32", "shard_merge_ref",
+    "widen_to_f32", "shard_merge_ref", "BlockPoolRef", "PoolError", "chain_hash", "fnv1a64",
 ]
