@@ -60,10 +60,12 @@ def parse():
                     help="minimum host time spent timing the oracle")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-stream-ceiling", action="store_true")
-    ap.add_argument("--op", choices=["decode", "append", "merge"], default="decode",
+    ap.add_argument("--op", choices=["decode", "append", "merge", "pool"], default="decode",
                     help="decode: the attention call (default); append: the paged KV "
                          "append of one new token per sequence on the same workload; "
-                         "merge: the log-sum-exp merge of --shards position shards")
+                         "merge: the log-sum-exp merge of --shards position shards; "
+                         "pool: the host block pool's bookkeeping for the workload's "
+                         "requests behind a shared prompt prefix")
     ap.add_argument("--shards", type=int, default=8, help="shards for --op merge")
     ap.add_argument("--pmc-pass", action="store_true",
                     help="run a 1 GiB device copy and 20 decode calls, print nothing else "
@@ -296,6 +298,97 @@ def bench_merge(args, torch, np, pkd, W):
     print(json.dumps(rec), flush=True)
 
 
+def pool_requests(np, W, spec):
+    """Token ids of the workload's requests: the shared prompt prefix (the
+    workload's shared_prefix_tokens) followed by a random tail, each request
+    as long as the workload's drawn context length, and longer than the
+    prefix."""
+    rng = np.random.default_rng(3000 + spec.seed)
+    lens = W.draw_lens(spec, np.random.default_rng(spec.seed))
+    pre_n = spec.shared_prefix_tokens
+    prefix = rng.integers(0, 128000, pre_n, dtype=np.int32)
+    reqs = []
+    for L in lens:
+        tail = rng.integers(0, 128000, max(int(L) - pre_n, 1), dtype=np.int32)
+        reqs.append(np.concatenate([prefix, tail])[: max(int(L), pre_n + 1)])
+    return reqs
+
+
+def bench_pool(args, np, pkd, W):
+    """Time the host block pool (pa_pool_*) on the workload's requests: one
+    episode admits every request (prefix lookup, hashing of every full block,
+    block hand-out), then runs --steps decode steps (one appended token per
+    request and the batch's block-table export), then frees every request.
+    `value` is decode steps per second; admission is reported beside it."""
+    import oracle
+    spec = W.SPECS[args.workload]
+    if not spec.shared_prefix_tokens:      # the long-context workload is the one with a prefix
+        spec = W.SPECS[5]
+    reqs = pool_requests(np, W, spec)
+    B, mbs = len(reqs), spec.max_blocks_per_seq
+    need = sum(-(-len(r) // 16) + args.steps // 16 + 2 for r in reqs)
+    nb = int(need * 1.2)
+    steps = args.steps
+
+    def episode(make, tables):
+        p = make()
+        t0 = time.perf_counter()
+        hits = [p.add_sequence(i, r) for i, r in enumerate(reqs)]
+        t1 = time.perf_counter()
+        for k in range(steps):
+            for i in range(B):
+                p.append_token(i, k)
+            tables(p)
+        t2 = time.perf_counter()
+        for i in range(B):
+            p.free_sequence(i)
+        return t1 - t0, t2 - t1, hits
+
+    nat_tables = lambda p: p.block_table(list(range(B)), mbs, 0)
+    for _ in range(max(1, args.warmup // 25)):
+        episode(lambda: pkd.BlockPool(nb, 1), nat_tables)
+    reps, adm, run = 5, [], []
+    for _ in range(reps):
+        a, r, hits = episode(lambda: pkd.BlockPool(nb, 1), nat_tables)
+        adm.append(a)
+        run.append(r)
+    prompt_tokens = int(sum(len(r) for r in reqs))
+    step_s = min(run) / steps
+    rec = {
+        "metric": "host block pool decode-step bookkeeping (appends + block-table export)",
+        "value": round(1.0 / step_s, 3), "unit": "steps/s", "n_gpus": 1, "steps": steps,
+        "warmup": args.warmup, "ms_per_step": round(step_s * 1e3, 6),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "int32",
+        "data": "synthetic (seeded token ids: shared prompt prefix + random tails)",
+        "config": {"workload": spec.name, "op": "block_pool", "requests": B,
+                   "prompt_tokens": prompt_tokens, "prefix_tokens_reused": int(sum(hits)),
+                   "pool_blocks": nb, "max_blocks_per_seq": mbs,
+                   "admit_ms": round(min(adm) * 1e3, 3),
+                   "admit_prompt_tokens_per_s": round(prompt_tokens / min(adm), 1)},
+        "roofline": None,
+        "note": "host code with no GPU kernel: no roofline; best of 5 episodes",
+    }
+    if not args.no_cpu_baseline:
+        ref_steps = max(1, min(steps, 50))
+        t0 = time.perf_counter()
+        p = oracle.BlockPoolRef(nb, 1)
+        for i, r in enumerate(reqs):
+            p.add_sequence(i, r.tolist())
+        ta = time.perf_counter() - t0
+        t1 = time.perf_counter()
+        for k in range(ref_steps):
+            for i in range(B):
+                p.append_token(i, k)
+            p.block_table(list(range(B)), mbs, 0)
+        tr = time.perf_counter() - t1
+        rec["cpu_baseline"] = {"value": round(ref_steps / tr, 3), "unit": "steps/s", "cores": 1,
+                               "kind": "oracle",
+                               "sample": f"one admission ({ta:.1f} s, "
+                                         f"{prompt_tokens / ta:.0f} prompt tokens/s) "
+                                         f"then {ref_steps} decode steps"}
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -314,6 +407,8 @@ def main():
         return bench_append(args, torch, np, pkd, W)
     if args.op == "merge":
         return bench_merge(args, torch, np, pkd, W)
+    if args.op == "pool":
+        return bench_pool(args, np, pkd, W)
 
     spec = W.SPECS[args.workload]
     wl = W.make_workload(spec)

@@ -79,7 +79,9 @@ typedef enum {
   PA_ERR_DTYPE = 3,     /* unsupported io/kv dtype combination */
   PA_ERR_WORKSPACE = 4, /* workspace missing or smaller than required */
   PA_ERR_ALIGN = 5,     /* a tensor pointer is not 16-byte aligned */
-  PA_ERR_HIP = 6        /* the HIP runtime refused the launch */
+  PA_ERR_HIP = 6,       /* the HIP runtime refused the launch */
+  PA_ERR_CAPACITY = 7,  /* block pool: not enough free blocks (or host memory) */
+  PA_ERR_STATE = 8      /* block pool: sequence id unknown, or already present */
 } pa_status;
 
 typedef struct {
@@ -192,6 +194,66 @@ pa_status pa_kv_append(const pa_shape* shape, const void* k_new, const void* v_n
 pa_status pa_lse_merge(int32_t num_shards, int32_t rows, int32_t head_dim,
                        const void* shard_out, const float* shard_lse, pa_dtype dtype,
                        void* out, float* lse_out, void* stream);
+
+/* ---- Host block pool with hash-chained prefix reuse --------------------
+ * The block manager of a paged KV cache ("rvLLM: High-performance LLM
+ * inference in Rust", architecture diagram, "Block Manager (paged KV)") with
+ * prefix caching ("Litellama", section "Features", Prefix Caching): block ids
+ * for the block tables pa_decode and pa_kv_append read, handed out so that
+ * sequences whose leading 16-token blocks hold the same tokens share the
+ * same physical blocks, and blocks no sequence uses stay cached until the
+ * pool needs them.
+ *   * A full block is keyed by FNV-1a-64 over the 8 little-endian bytes of
+ *     its parent key (the pool seed for a sequence's first block) followed
+ *     by its 16 token ids as 4-byte little-endian integers. A lookup also
+ *     compares parent key and tokens, so a hash collision never shares.
+ *   * The free queue holds every block no sequence uses, least recently
+ *     released first; initially all blocks, in id order. Taking a block from
+ *     it drops the cache entry the block carried (eviction).
+ * Host memory only; the pool is not thread-safe (one caller at a time).
+ * Every call returns PA_ERR_NULL for a NULL pool or required pointer. */
+typedef struct pa_block_pool pa_block_pool;
+
+/* A pool of num_blocks (>= 1) block ids 0 .. num_blocks-1; *pool receives the
+ * handle (NULL on error). PA_ERR_CAPACITY if host memory runs out. */
+pa_status pa_pool_create(int32_t num_blocks, uint64_t seed, pa_block_pool** pool);
+
+/* Frees the pool and everything it holds; NULL is a no-op. */
+void pa_pool_destroy(pa_block_pool* pool);
+
+/* Registers sequence seq_id with its num_tokens (>= 0) prompt tokens. The
+ * longest run of leading full blocks found in the cache is shared (their
+ * reference counts rise; cached blocks in the free queue leave it); the
+ * remaining full blocks and a partial last block are taken from the free
+ * queue, and the new full blocks enter the cache unless it already holds
+ * that key. *cached_tokens (if not NULL) receives 16 x the blocks shared.
+ * PA_ERR_STATE if seq_id exists; PA_ERR_CAPACITY, changing nothing, if the
+ * free queue cannot supply every block the call needs. */
+pa_status pa_pool_add_sequence(pa_block_pool* pool, int64_t seq_id, const int32_t* tokens,
+                               int32_t num_tokens, int32_t* cached_tokens);
+
+/* Appends one generated token: a token that starts a new block takes one
+ * from the free queue (PA_ERR_CAPACITY, changing nothing, if it is empty);
+ * a token that completes a block enters that block in the cache.
+ * PA_ERR_STATE for an unknown seq_id. */
+pa_status pa_pool_append_token(pa_block_pool* pool, int64_t seq_id, int32_t token);
+
+/* Releases the sequence's blocks, last block first: a block whose reference
+ * count reaches zero joins the back of the free queue, still cached.
+ * PA_ERR_STATE for an unknown seq_id. */
+pa_status pa_pool_free_sequence(pa_block_pool* pool, int64_t seq_id);
+
+/* Number of blocks in the free queue; -1 for a NULL pool. */
+int32_t pa_pool_num_free(const pa_block_pool* pool);
+
+/* Writes the block tables of num_seqs sequences (host memory):
+ * block_table[i][j] = j-th block of seq_ids[i], pad_block past its blocks,
+ * int32 [num_seqs][max_blocks_per_seq]; context_lens[i] (if not NULL) = its
+ * token count. PA_ERR_STATE for an unknown id, PA_ERR_SHAPE if a sequence
+ * has more than max_blocks_per_seq blocks; nothing is written on error. */
+pa_status pa_pool_block_table(const pa_block_pool* pool, const int64_t* seq_ids,
+                              int32_t num_seqs, int32_t max_blocks_per_seq, int32_t pad_block,
+                              int32_t* block_table, int32_t* context_lens);
 
 /* Zero-fill a workspace on `stream` with a fill kernel (safe to capture in a
  * HIP graph). */

@@ -15,7 +15,10 @@ SPLIT_BALANCED = -1   # partition_size value of the balanced split (PA_SPLIT_BAL
 DTYPE_CODE = {"f32": PA_F32, "f16": PA_F16, "bf16": PA_BF16, "fp8_e4m3": PA_FP8_E4M3}
 
 EXPORTED = ("pa_decode", "pa_decode_workspace_bytes", "pa_kv_append", "pa_lse_merge",
-            "pa_workspace_reset", "pa_status_str")
+            "pa_workspace_reset", "pa_status_str", "pa_pool_create", "pa_pool_destroy",
+            "pa_pool_add_sequence", "pa_pool_append_token", "pa_pool_free_sequence",
+            "pa_pool_num_free", "pa_pool_block_table")
+PA_ERR_CAPACITY, PA_ERR_STATE = 7, 8
 
 
 class PaError(RuntimeError):
@@ -64,6 +67,21 @@ def load_library(path=None):
     lib.pa_workspace_reset.restype = ctypes.c_int
     lib.pa_status_str.argtypes = [ctypes.c_int]
     lib.pa_status_str.restype = ctypes.c_char_p
+    i32, i64 = ctypes.c_int32, ctypes.c_int64
+    lib.pa_pool_create.argtypes = [i32, ctypes.c_uint64, ctypes.POINTER(vp)]
+    lib.pa_pool_create.restype = ctypes.c_int
+    lib.pa_pool_destroy.argtypes = [vp]
+    lib.pa_pool_destroy.restype = None
+    lib.pa_pool_add_sequence.argtypes = [vp, i64, vp, i32, ctypes.POINTER(i32)]
+    lib.pa_pool_add_sequence.restype = ctypes.c_int
+    lib.pa_pool_append_token.argtypes = [vp, i64, i32]
+    lib.pa_pool_append_token.restype = ctypes.c_int
+    lib.pa_pool_free_sequence.argtypes = [vp, i64]
+    lib.pa_pool_free_sequence.restype = ctypes.c_int
+    lib.pa_pool_num_free.argtypes = [vp]
+    lib.pa_pool_num_free.restype = i32
+    lib.pa_pool_block_table.argtypes = [vp, vp, i32, i32, i32, vp, vp]
+    lib.pa_pool_block_table.restype = ctypes.c_int
     if path is None:
         _lib = lib
     return lib
@@ -265,3 +283,55 @@ def lse_merge(shard_out, shard_lse, *, out=None, lse_out=None, stream=None):
                             DTYPE_CODE[dt], out.data_ptr(),
                             lse_out.data_ptr() if lse_out is not None else None, s.cuda_stream))
     return out
+
+
+class BlockPool:
+    """Host block pool with hash-chained prefix reuse (pa_pool_* in the C ABI):
+    hands out the block ids of the tables `decode` and `kv_append` read.
+    Token lists are int32; tables come back as numpy int32 arrays."""
+
+    def __init__(self, num_blocks, seed=0):
+        self._lib = load_library()
+        h = ctypes.c_void_p()
+        _check(self._lib.pa_pool_create(int(num_blocks), int(seed) & (2**64 - 1),
+                                        ctypes.byref(h)))
+        self._h = h
+
+    def close(self):
+        if self._h:
+            self._lib.pa_pool_destroy(self._h)
+            self._h = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def add_sequence(self, seq_id, tokens):
+        """Register a sequence's prompt; returns the leading tokens found cached."""
+        import numpy as np
+        t = np.ascontiguousarray(tokens, dtype=np.int32).reshape(-1)
+        got = ctypes.c_int32(0)
+        _check(self._lib.pa_pool_add_sequence(self._h, int(seq_id), t.ctypes.data, t.size,
+                                              ctypes.byref(got)))
+        return got.value
+
+    def append_token(self, seq_id, token):
+        _check(self._lib.pa_pool_append_token(self._h, int(seq_id), int(token)))
+
+    def free_sequence(self, seq_id):
+        _check(self._lib.pa_pool_free_sequence(self._h, int(seq_id)))
+
+    def num_free(self):
+        return self._lib.pa_pool_num_free(self._h)
+
+    def block_table(self, seq_ids, max_blocks, pad=0):
+        """-> (int32 [len(seq_ids), max_blocks] block table, int32 context lengths)."""
+        import numpy as np
+        ids = np.ascontiguousarray(seq_ids, dtype=np.int64).reshape(-1)
+        table = np.empty((ids.size, int(max_blocks)), dtype=np.int32)
+        lens = np.empty(ids.size, dtype=np.int32)
+        _check(self._lib.pa_pool_block_table(self._h, ids.ctypes.data, ids.size, int(max_blocks),
+                                             int(pad), table.ctypes.data, lens.ctypes.data))
+        return table, lens

@@ -1614,6 +1614,8 @@ const char* pa_status_str(pa_status status) {
     case PA_ERR_WORKSPACE: return "workspace missing or too small";
     case PA_ERR_ALIGN: return "a tensor pointer is not suitably aligned";
     case PA_ERR_HIP: return "the HIP runtime refused the launch";
+    case PA_ERR_CAPACITY: return "not enough free blocks in the pool";
+    case PA_ERR_STATE: return "unknown or already present sequence id";
   }
   return "unknown status";
 }

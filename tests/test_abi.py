@@ -115,7 +115,7 @@ def test_workspace_size_arithmetic():
 
 def test_status_strings():
     lib = _lib.load_library()
-    for code in range(7):
+    for code in range(9):
         assert lib.pa_status_str(code)
     assert lib.pa_status_str(99) == b"unknown status"
 
