@@ -15,6 +15,7 @@ from .paged_decode import (BLOCK_SIZE, attend, gather_kv, lse_merge, page_x,
 from .kv_append import e4m3_encode, kv_append_ref, quantize_e4m3, widen_to_f32
 from .shard_merge import shard_merge_ref
 from .block_pool import BlockPoolRef, PoolError, chain_hash, fnv1a64
+from .multi_query import multi_query_ref
 
 __all__ = [
     "E4M3_TABLE", "ELEM_BYTES", "STORAGE", "decode", "decode_bf16",
@@ -22,4 +23,5 @@ __all__ = [
     "attend", "gather_kv", "lse_merge", "page_x", "paged_decode_ref",
     "paged_decode_split_ref", "e4m3_encode", "kv_append_ref", "quantize_e4m3",
     "widen_to_f32", "shard_merge_ref", "BlockPoolRef", "PoolError", "chain_hash", "fnv1a64",
+    "multi_query_ref",
 ]

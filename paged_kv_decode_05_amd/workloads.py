@@ -219,6 +219,16 @@ def make_workload(spec, seed=None, poison=True):
                     scale=np.float32(1.0 / math.sqrt(D)), k_scale=k_scale, v_scale=v_scale)
 
 
+def multi_query(wl, q_len, seed=None):
+    """Query rows for q_len new tokens per sequence: storage [B][q_len][Hq][D]
+    in the workload's io dtype, standard normal from a Generator seeded with
+    (seed or the workload's seed) + 7919 * q_len. The workload's context
+    lengths count the new tokens (their K/V are already in the cache)."""
+    s = wl.spec
+    rng = np.random.default_rng((s.seed if seed is None else seed) + 7919 * q_len)
+    return _to_storage(_normal(rng, (s.batch, q_len, s.num_q_heads, s.head_dim)), s.io_dtype)
+
+
 def small_variant(spec, batch, lens, max_blocks_per_seq=None, name_suffix="small"):
     """Same head shape and dtypes with a smaller batch and length mix."""
     mbs = max_blocks_per_seq
