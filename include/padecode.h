@@ -143,6 +143,35 @@ pa_status pa_decode(const pa_shape* shape, const void* q, const void* k_cache,
                     size_t workspace_bytes, void* out, float* lse_out,
                     void* stream);
 
+/* Attention of q_len new tokens per sequence over the paged cache, causal
+ * among the new tokens: the attention step of chunked prefill ("Litellama",
+ * section "Features", Chunked Prefill) and of speculative verification
+ * ("rvLLM: High-performance LLM inference in Rust", speculative decoding:
+ * several drafted tokens checked in one target step). The new tokens' K and V
+ * are already in the cache (pa_kv_append), so context_lens[b] = L counts
+ * them; new token t (0 .. q_len-1) sits at position L - q_len + t and
+ * attends to positions 0 .. L - q_len + t:
+ *     out[b][t][h] = softmax(scale * q[b][t][h] . K^T) V   over those positions
+ * A new token with no visible position (L < q_len) gets out = 0 and
+ * lse = -inf; q_len = 1 is pa_decode.
+ *   q, out      [batch][q_len][num_q_heads][head_dim] in io_dtype
+ *   lse_out     float32 [batch][q_len][num_q_heads] (natural log) or NULL
+ *   q_len       1 .. 16
+ *   shape       as for pa_decode; partition_size 0 or a positive multiple of
+ *               16 (PA_SPLIT_BALANCED is not supported here)
+ *   workspace   pa_decode_multi_workspace_bytes(shape, q_len) bytes when
+ *               partition_size > 0; same counter-first contract as
+ *               pa_decode, with ceil(ceil(G*q_len/16)/2) counters per
+ *               (sequence, KV head), G = num_q_heads / num_kv_heads
+ * Everything else (dtypes, scales, alignment, errors) as for pa_decode. */
+size_t pa_decode_multi_workspace_bytes(const pa_shape* shape, int32_t q_len);
+pa_status pa_decode_multi(const pa_shape* shape, int32_t q_len, const void* q,
+                          const void* k_cache, const void* v_cache,
+                          const int32_t* block_table, const int32_t* context_lens,
+                          float scale, pa_dtype io_dtype, pa_dtype kv_dtype,
+                          const float* k_scale, const float* v_scale, void* workspace,
+                          size_t workspace_bytes, void* out, float* lse_out, void* stream);
+
 /* Paged KV append: write each sequence's new token K and V rows into its
  * block and slot of the caches, as the decode step does right before
  * attention ("rvLLM: High-performance LLM inference in Rust", section "Kernel

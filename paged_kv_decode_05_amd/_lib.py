@@ -14,7 +14,8 @@ PA_F32, PA_F16, PA_BF16, PA_FP8_E4M3 = 0, 1, 2, 3
 SPLIT_BALANCED = -1   # partition_size value of the balanced split (PA_SPLIT_BALANCED)
 DTYPE_CODE = {"f32": PA_F32, "f16": PA_F16, "bf16": PA_BF16, "fp8_e4m3": PA_FP8_E4M3}
 
-EXPORTED = ("pa_decode", "pa_decode_workspace_bytes", "pa_kv_append", "pa_lse_merge",
+EXPORTED = ("pa_decode", "pa_decode_workspace_bytes", "pa_decode_multi",
+            "pa_decode_multi_workspace_bytes", "pa_kv_append", "pa_lse_merge",
             "pa_workspace_reset", "pa_status_str", "pa_pool_create", "pa_pool_destroy",
             "pa_pool_add_sequence", "pa_pool_append_token", "pa_pool_free_sequence",
             "pa_pool_num_free", "pa_pool_block_table")
@@ -57,6 +58,12 @@ def load_library(path=None):
                               ctypes.c_int, ctypes.c_int, vp, vp, vp, ctypes.c_size_t, vp,
                               vp, vp]
     lib.pa_decode.restype = ctypes.c_int
+    lib.pa_decode_multi_workspace_bytes.argtypes = [ctypes.POINTER(PaShape), ctypes.c_int32]
+    lib.pa_decode_multi_workspace_bytes.restype = ctypes.c_size_t
+    lib.pa_decode_multi.argtypes = [ctypes.POINTER(PaShape), ctypes.c_int32, vp, vp, vp, vp, vp,
+                                    ctypes.c_float, ctypes.c_int, ctypes.c_int, vp, vp, vp,
+                                    ctypes.c_size_t, vp, vp, vp]
+    lib.pa_decode_multi.restype = ctypes.c_int
     lib.pa_kv_append.argtypes = [ctypes.POINTER(PaShape), vp, vp, vp, vp, ctypes.c_int,
                                  ctypes.c_int, vp, vp, vp, vp, vp]
     lib.pa_kv_append.restype = ctypes.c_int
@@ -103,15 +110,19 @@ def _torch_dtype_name(t):
 
 
 def make_shape(q, k_cache, block_table, partition_size):
-    B, Hq, D = q.shape
+    B, Hq, D = q.shape[0], q.shape[-2], q.shape[-1]
     return PaShape(batch=B, num_q_heads=Hq, num_kv_heads=k_cache.shape[1], head_dim=D,
                    block_size=k_cache.shape[3], max_blocks_per_seq=block_table.shape[1],
                    num_blocks=k_cache.shape[0], partition_size=partition_size)
 
 
 def workspace_bytes(q, k_cache, block_table, partition_size):
+    """Workspace bytes for a decode (q [B, Hq, D]) or multi-token (q [B, T, Hq, D]) call."""
     shape = make_shape(q, k_cache, block_table, partition_size)
-    return int(load_library().pa_decode_workspace_bytes(ctypes.byref(shape)))
+    lib = load_library()
+    if q.dim() == 4:
+        return int(lib.pa_decode_multi_workspace_bytes(ctypes.byref(shape), q.shape[1]))
+    return int(lib.pa_decode_workspace_bytes(ctypes.byref(shape)))
 
 
 def reset_workspace(workspace, stream=None):
@@ -133,8 +144,8 @@ class Prepared:
     """A pa_decode call with its arguments marshalled once; calling it enqueues
     the decode again on the same buffers (their contents may change)."""
 
-    def __init__(self, lib, args, out, keep):
-        self._fn = lib.pa_decode
+    def __init__(self, fn, args, out, keep):
+        self._fn = fn
         self._args = args
         self.out = out
         self._keep = keep
@@ -157,6 +168,10 @@ def prepare(q, k_cache, v_cache, block_table, context_lens, scale, *, k_scale=No
     SPLIT_BALANCED = equal page shares per workgroup. `workspace` (uint8,
     zero-filled once) is used when partition_size != 0; `workspace_bytes`
     gives its size.
+
+    q [B, T, Hq, D] selects the multi-token call (pa_decode_multi): T new
+    tokens per sequence whose K/V are already in the cache, new token t seeing
+    positions 0 .. L-T+t; out [B, T, Hq, D], lse_out [B, T, Hq].
     """
     import torch
     lib = load_library()
@@ -170,9 +185,11 @@ def prepare(q, k_cache, v_cache, block_table, context_lens, scale, *, k_scale=No
             raise PaError(2, f"{name} must be a contiguous device tensor")
     if block_table.dtype != torch.int32 or context_lens.dtype != torch.int32:
         raise PaError(3, "block_table and context_lens must be int32")
-    if q.dim() != 3 or k_cache.dim() != 5 or v_cache.dim() != 4 or block_table.dim() != 2:
-        raise PaError(2, "expected q [B,Hq,D], k_cache [nb,Hkv,D/X,16,X], v_cache [nb,Hkv,D,16]")
-    B, Hq, D = q.shape
+    if q.dim() not in (3, 4) or k_cache.dim() != 5 or v_cache.dim() != 4 or block_table.dim() != 2:
+        raise PaError(2, "expected q [B,Hq,D] or [B,T,Hq,D], k_cache [nb,Hkv,D/X,16,X], "
+                         "v_cache [nb,Hkv,D,16]")
+    multi = q.dim() == 4
+    B, Hq, D = q.shape[0], q.shape[-2], q.shape[-1]
     nb, Hkv = k_cache.shape[0], k_cache.shape[1]
     if (tuple(v_cache.shape) != (nb, Hkv, D, k_cache.shape[3])
             or k_cache.shape[2] * k_cache.shape[4] != D
@@ -180,23 +197,29 @@ def prepare(q, k_cache, v_cache, block_table, context_lens, scale, *, k_scale=No
         raise PaError(2, "inconsistent tensor shapes")
     if out is None:
         out = torch.empty_like(q)
+    if lse_out is not None and tuple(lse_out.shape) != tuple(q.shape[:-1]):
+        raise PaError(2, "lse_out must have q's shape without the head dimension")
     shape = make_shape(q, k_cache, block_table, partition_size)
     ws_ptr, ws_bytes = None, 0
     if partition_size:
-        need = int(lib.pa_decode_workspace_bytes(ctypes.byref(shape)))
+        need = workspace_bytes(q, k_cache, block_table, partition_size)
         if workspace is None:
             workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
         ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
     ks = k_scale.data_ptr() if k_scale is not None else None
     vs = v_scale.data_ptr() if v_scale is not None else None
     s = stream if stream is not None else torch.cuda.current_stream()
-    args = (ctypes.byref(shape), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+    tail = (q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
             block_table.data_ptr(), context_lens.data_ptr(), float(scale), DTYPE_CODE[io],
             DTYPE_CODE[kv], ks, vs, ws_ptr, ws_bytes, out.data_ptr(),
             lse_out.data_ptr() if lse_out is not None else None, s.cuda_stream)
+    if multi:
+        fn, args = lib.pa_decode_multi, (ctypes.byref(shape), q.shape[1]) + tail
+    else:
+        fn, args = lib.pa_decode, (ctypes.byref(shape),) + tail
     keep = (shape, q, k_cache, v_cache, block_table, context_lens, k_scale, v_scale,
             workspace, out, lse_out)
-    return Prepared(lib, args, out, keep)
+    return Prepared(fn, args, out, keep)
 
 
 def kv_append(k_new, v_new, positions, block_table, k_cache, v_cache, *, k_scale=None,

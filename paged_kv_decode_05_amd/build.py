@@ -22,7 +22,7 @@ COMMON = [
 ]
 
 TARGETS = [
-    ([os.path.join(HERE, "csrc", n) for n in ("pa_decode.hip", "pa_append.hip", "pa_merge.hip",
+    ([os.path.join(HERE, "csrc", n) for n in ("pa_decode.hip", "pa_multi.hip", "pa_append.hip", "pa_merge.hip",
                                                      "block_pool.cpp")],
      os.path.join(HERE, "libpadecode.so")),
     ([os.path.join(ROOT, "tests", "probes", "probes.hip")],

@@ -1,0 +1,556 @@
+// Attention of several new query tokens per sequence over the paged KV cache,
+// causal among the new tokens, for gfx950 (MI355X): the attention step of
+// chunked prefill ("Litellama", section "Features": Chunked Prefill, prompts
+// split into 512-token chunks that interleave with decode requests) and of
+// speculative verification ("rvLLM: High-performance LLM inference in Rust",
+// speculative decoding: the target model checks several drafted tokens in one
+// step). The new tokens' K and V are already in the cache, so a sequence's
+// length L counts them; new token t (0 .. T-1) sees positions 0 .. L-T+t.
+//
+// Same building blocks and cache layouts as single-token decode. A workgroup
+// of four waves owns one (sequence b, KV head g, partition p, row chunk c)
+// unit. The query rows of a (b, g) pair are its G*T (new token, head) pairs,
+// row = t*G + h, cut into chunks of NT matrix-core column tiles of 16 rows
+// (NT = 1 or 2; a pair has ceil(G*T/16) tiles, so ceil(tiles/2) chunks: four
+// tiles of accumulators do not fit in the registers at head_dim 128). Every
+// wave keeps NT sets of accumulators, so one K/V page loaded into registers
+// feeds all NT*16 rows, and the matrix-core work per byte grows with T. The
+// chunks of one (b, g, p) are launched nbg workgroups apart, which keeps them
+// on one XCD (workgroups go to the XCDs round-robin; nbg = B * Hkv is
+// usually a multiple of 8) and close in time, so the second chunk's K/V reads
+// mostly hit that XCD's L2. The chunk's query operand
+// sits in LDS in lane order (one 16-byte read per lane per operand chunk),
+// which keeps the registers for the accumulators. Pages go to the waves
+// round-robin through the same register rings as decode; a page whose tokens
+// reach past L - T (only a sequence's last two pages, always the last page of
+// its wave in the unit) is masked per column: token j is visible to row
+// (t, h) iff j <= L - T + t. A column with nothing visible yet keeps a zero
+// state (the running max stays -inf, exponentials are taken against 0).
+// Waves merge through LDS one column tile at a time; split-K partials go to
+// the workspace and the last partition of each (b, g, chunk) to finish merges
+// them, as for decode. Rows with no visible token get out = 0, lse = -inf.
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+#include "padecode.h"
+#include "pa_tiles.h"
+
+namespace pa_mq {
+using namespace pa;
+
+constexpr int kMaxQLen = 16;
+
+struct Params {
+  const uint8_t* q;          // [B][T][Hq][D]
+  const uint8_t* k;
+  const uint8_t* v;
+  const int32_t* block_table;
+  const int32_t* context_lens;
+  const float* k_scale;
+  const float* v_scale;
+  uint8_t* out;              // [B][T][Hq][D]
+  float* lse_out;            // [B][T][Hq] or null
+  float* ws_o;               // [slot][R][D]  partial outputs, normalised
+  float* ws_lse;             // [slot][R]     base 2, in units of the scaled scores
+  uint32_t* ws_cnt;          // [B][Hkv][chunks]
+  float scale;
+  int32_t batch;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t group;             // G = Hq / Hkv
+  int32_t q_len;             // T
+  int32_t rows;              // R = G * T
+  int32_t chunks;
+  int32_t max_blocks_per_seq;
+  int32_t num_blocks;
+  int32_t part_tokens;
+  int32_t p_max;
+};
+
+template <typename QC, int NT, int KQ, int D>
+struct MqSmem {
+  QC q[NT][KQ][64];            // query operand chunks, lane order
+  float acc[kWaves][16][D + 4];
+  float m[kWaves][16];
+  float l[kWaves][16];
+  int bad;
+  int last;
+};
+
+template <typename IO, typename KV, int D, int NT>
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
+pa_multi_kernel(const Params a) {
+  using T = typename TileOf<IO, KV, D>::type;
+  using QC = typename T::QC;
+  constexpr int KQ = T::kQ;
+  constexpr bool kFp8 = std::is_same<KV, FP8>::value;
+  constexpr size_t kPageBytes = (size_t)kBlock * D * ElemSize<KV>::v;
+  constexpr int kRowsC = NT * 16;
+  __shared__ MqSmem<QC, NT, KQ, D> sm;
+
+  const int H = a.num_kv_heads;
+  const int nbg = a.batch * H;
+  const int pc = blockIdx.x / nbg;          // p * chunks + c: partition-major
+  const int bg = blockIdx.x - pc * nbg;
+  const int p = pc / a.chunks;
+  const int c = pc - p * a.chunks;
+  const int b = bg / H;
+  const int g = bg - b * H;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int rr = lane & 15, jj = lane >> 4;
+  const int G = a.group, TQ = a.q_len, R = a.rows;
+  const int PT = a.part_tokens;
+  const int page0 = PT > 0 ? p * (PT / kBlock) : 0;
+  const int row0 = c * kRowsC;
+
+  // Block ids of this wave's first 64 pages (indices clamped into the row).
+  const int32_t* bt = a.block_table + (size_t)b * a.max_blocks_per_seq + w;
+  const int bt_last = a.max_blocks_per_seq - 1 - w;
+  auto fetch_bt = [&](int chunk) {
+    return bt[min(page0 + kWaves * (chunk * 64 + lane), bt_last)];
+  };
+  int bt_cur = fetch_bt(0);
+
+  // The chunk's query operand into LDS. Rows past R repeat row R-1: their
+  // columns hold finite duplicates that are never stored.
+  for (int i = tid; i < NT * KQ * 64; i += kThreads) {
+    const int j = i / (KQ * 64);
+    const int rem = i - j * (KQ * 64);
+    const int cc = rem >> 6, ln = rem & 63;
+    const int rho = min(row0 + 16 * j + (ln & 15), R - 1);
+    const int t = rho / G, h = rho - t * G;
+    const uint8_t* qrow =
+        a.q + (((size_t)b * TQ + t) * a.num_q_heads + (size_t)g * G + h) * D * ElemSize<IO>::v;
+    sm.q[j][cc][ln] = __builtin_bit_cast(QC, *reinterpret_cast<const u32x4*>(qrow + T::qoff(cc, ln >> 4)));
+  }
+
+  const int L = a.context_lens[b];
+  const bool bad_len = L < 0 || L > a.max_blocks_per_seq * kBlock;
+  const int nparts = (bad_len || L == 0) ? 1 : (PT > 0 ? (L + PT - 1) / PT : 1);
+  if (p >= nparts) return;
+  const int rows_c = min(kRowsC, R - row0);   // rows this chunk stores
+  if (bad_len || L == 0) {
+    const float fill = bad_len ? __builtin_nanf("") : 0.f;
+    for (int i = tid; i < rows_c * D; i += kThreads) {
+      const int rho = row0 + i / D, t = rho / G, h = rho - t * G;
+      store_out<IO>(a.out, (((size_t)b * TQ + t) * a.num_q_heads + (size_t)g * G + h) * D + i % D, fill);
+    }
+    if (a.lse_out && tid < rows_c) {
+      const int rho = row0 + tid, t = rho / G, h = rho - t * G;
+      a.lse_out[((size_t)b * TQ + t) * a.num_q_heads + (size_t)g * G + h] = bad_len ? fill : -INFINITY;
+    }
+    return;
+  }
+
+  // Last visible position of each of the lane's columns.
+  int lim[NT];
+#pragma unroll
+  for (int j = 0; j < NT; ++j) lim[j] = L - TQ + min(row0 + 16 * j + rr, R - 1) / G;
+
+  const int t0 = page0 * kBlock;
+  const int pg_hi = PT > 0 ? page0 + PT / kBlock : a.max_blocks_per_seq;
+  const int t1 = min(pg_hi * kBlock, L);
+  const int npages = (t1 - t0 + kBlock - 1) / kBlock;
+  const int nmine = npages > w ? (npages - w + kWaves - 1) / kWaves : 0;
+
+  float kmul = a.scale * kLog2e;
+  float vmul = 1.0f;
+  if constexpr (kFp8) {
+    kmul *= a.k_scale[g];
+    vmul = a.v_scale[g];
+  }
+  int bt_next = nmine > 64 ? fetch_bt(1) : 0;
+
+  const gptr kbase = uniform_ptr(a.k + (size_t)g * kPageBytes);
+  const gptr vbase = uniform_ptr(a.v + (size_t)g * kPageBytes);
+  const size_t block_stride = (size_t)a.num_kv_heads * kPageBytes;
+  const uint32_t ko = T::koff(lane), vo = T::voff(lane);
+  bool bad_blk = false;
+
+  constexpr int kKS = T::kKStages, kVS = T::kVStages;
+  constexpr int dK = kKS - 1, dV = kVS - 1;
+  constexpr int kAhead = dK > 1 ? dK : 1;
+  typename T::KRegs ring_k[kKS];
+  typename T::VRegs ring_v[kVS];
+  size_t poff[kKS];
+
+  auto issue_k = [&](int slot, int i, auto refresh_tag) __attribute__((always_inline)) {
+    if constexpr (decltype(refresh_tag)::value) {
+      if (i > 0 && (i & 63) == 0) {
+        bt_cur = bt_next;
+        if (nmine > i + 64) bt_next = fetch_bt((i >> 6) + 1);
+      }
+    }
+    int phys = __builtin_amdgcn_readlane(bt_cur, i & 63);
+    if ((unsigned)phys >= (unsigned)a.num_blocks) {
+      bad_blk = true;
+      phys = 0;
+    }
+    poff[slot] = (size_t)phys * block_stride;
+    T::load_k(ring_k[slot], kbase + poff[slot], ko);
+  };
+  auto issue_v = [&](int vslot, int kslot) __attribute__((always_inline)) { T::load_v(ring_v[vslot], vbase + poff[kslot], vo); };
+
+  float mrow[NT], lrow[NT];
+  f32x4 acc[NT][D / 16];
+#pragma unroll
+  for (int j = 0; j < NT; ++j) {
+    mrow[j] = -INFINITY;
+    lrow[j] = 0.f;
+#pragma unroll
+    for (int t = 0; t < D / 16; ++t) acc[j][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  // One page for all NT column tiles. kMasked: the page may hold tokens at
+  // or past the unit's end, or tokens some column must not see.
+  auto compute = [&](int kslot, int vslot, int i, auto masked_tag) __attribute__((always_inline)) {
+    constexpr bool kMasked = decltype(masked_tag)::value;
+    const int pstart = t0 + (w + kWaves * i) * kBlock;
+    typename T::A4 va[D / 16];
+#pragma unroll
+    for (int t = 0; t < D / 16; ++t) {
+      va[t] = T::pvt(ring_v[vslot], t);
+      if constexpr (kMasked) va[t] = T::zero_tail(va[t], jj, t1 - pstart);
+    }
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+      typename T::Q qop;
+#pragma unroll
+      for (int cc = 0; cc < KQ; ++cc) qop.c[cc] = sm.q[j][cc][lane];
+      const f32x4 s = T::scores(ring_k[kslot], qop);
+      float sc[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if constexpr (kMasked) {
+          const int tok = pstart + 4 * jj + e;
+          sc[e] = (tok <= lim[j] && tok < t1) ? s[e] * kmul : -INFINITY;
+        } else {
+          sc[e] = s[e] * kmul;
+        }
+      }
+      const float mx = wave_max_rows(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])));
+      const float mnew = fmaxf(mrow[j], mx);
+      float msafe = mnew;
+      if constexpr (kMasked) msafe = mnew == -INFINITY ? 0.f : mnew;
+      const float alpha = exp2_fast(mrow[j] - msafe);
+      float pr[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) pr[e] = exp2_fast(sc[e] - msafe);
+      const typename T::P pk = T::pack(pr);
+      lrow[j] = lrow[j] * alpha + T::psum(pk);
+      mrow[j] = mnew;
+      if (__any(alpha != 1.0f)) {
+#pragma unroll
+        for (int t = 0; t < D / 16; ++t) acc[j][t] *= alpha;
+      }
+#pragma unroll
+      for (int t = 0; t < D / 16; ++t) acc[j][t] = T::pv(va[t], pk, acc[j][t]);
+    }
+  };
+  using Full = std::integral_constant<bool, false>;
+  using Tail = std::integral_constant<bool, true>;
+
+  // Steady blocks never hold a wave's last kAhead pages; every page a mask
+  // can touch is the last page of its wave, so it runs in the peeled tail.
+  constexpr int kU = kKS * kVS / gcd_c(kKS, kVS);
+  __syncthreads();   // query operand in LDS
+  auto run_ring = [&](auto refresh_tag) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < dK; ++j)
+      if (j < nmine) issue_k(j, j, refresh_tag);
+#pragma unroll
+    for (int j = 0; j < dV; ++j)
+      if (j < nmine) issue_v(j, j);
+    int i0 = 0;
+    for (; i0 + kU - 1 + kAhead < nmine; i0 += kU) {
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        issue_k((u + dK) % kKS, i0 + u + dK, refresh_tag);
+        issue_v((u + dV) % kVS, (u + dV) % kKS);
+        compute(u % kKS, u % kVS, i0 + u, Full{});
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kU + kAhead; ++u) {
+      const int i = i0 + u;
+      if (i < nmine) {
+        if (i + dK < nmine) issue_k((u + dK) % kKS, i + dK, refresh_tag);
+        if (i + dV < nmine) issue_v((u + dV) % kVS, (u + dV) % kKS);
+        compute(u % kKS, u % kVS, i, Tail{});
+      }
+    }
+  };
+  if (nmine > 64)
+    run_ring(std::integral_constant<bool, true>{});
+  else
+    run_ring(std::integral_constant<bool, false>{});
+
+  // ---- merge the waves through LDS, one column tile at a time -------------
+  if (tid == 0) sm.bad = 0;
+  __syncthreads();
+  if (bad_blk) sm.bad = 1;
+  const bool split = nparts > 1;
+  const size_t slot = (size_t)bg * a.p_max + p;
+  const brsrc wr_slot = buffer_rsrc(a.ws_o + slot * R * D, (uint32_t)(R * D * sizeof(float)));
+  bool bad = false;
+#pragma unroll
+  for (int j = 0; j < NT; ++j) {
+    const float lsum = wave_sum_rows(lrow[j]);
+    if (j > 0) __syncthreads();   // the previous tile's readers are done
+    if (jj == 0) {
+      sm.m[w][rr] = mrow[j];
+      sm.l[w][rr] = lsum;
+    }
+#pragma unroll
+    for (int t = 0; t < D / 16; ++t)
+      *reinterpret_cast<f32x4*>(&sm.acc[w][rr][16 * t + 4 * jj]) = acc[j][t];
+    __syncthreads();
+    if (j == 0) bad = sm.bad != 0;
+    for (int i = tid; i < 16 * (D / 4); i += kThreads) {   // (row, 4-float quad)
+      const int r2 = i / (D / 4), d = 4 * (i - r2 * (D / 4));
+      const int rho = row0 + 16 * j + r2;
+      if (rho >= R) continue;
+      float M = -INFINITY;
+#pragma unroll
+      for (int ww = 0; ww < kWaves; ++ww) M = fmaxf(M, sm.m[ww][r2]);
+      float W = 0.f;
+      f32x4 o = {0.f, 0.f, 0.f, 0.f};
+      if (M > -INFINITY) {
+#pragma unroll
+        for (int ww = 0; ww < kWaves; ++ww) {
+          const float e = exp2_fast(sm.m[ww][r2] - M);
+          W += e * sm.l[ww][r2];
+          o += e * *reinterpret_cast<const f32x4*>(&sm.acc[ww][r2][d]);
+        }
+      }
+      f32x4 val = {0.f, 0.f, 0.f, 0.f};
+      float lse2 = -INFINITY;
+      if (W > 0.f) {
+        val = f32x4{o[0] / W * vmul, o[1] / W * vmul, o[2] / W * vmul, o[3] / W * vmul};
+        lse2 = M + log2_fast(W);
+      }
+      if (bad) {
+        val = f32x4{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
+        lse2 = __builtin_nanf("");
+      }
+      if (!split) {
+        const int t = rho / G, h = rho - t * G;
+        const size_t orow = ((size_t)b * TQ + t) * a.num_q_heads + (size_t)g * G + h;
+        store_out4<IO>(a.out, orow * D + d, val);
+        if (d == 0 && a.lse_out) a.lse_out[orow] = lse2 * kLn2;
+      } else {
+        st_agent4(wr_slot, (uint32_t)(((size_t)rho * D + d) * sizeof(float)), val);
+        if (d == 0) st_agent(a.ws_lse + slot * R + rho, lse2);
+      }
+    }
+  }
+  if (!split) return;
+
+  // ---- split-K: the last partition of (b, g, c) to finish merges ----------
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  uint32_t* cnt = a.ws_cnt + (size_t)bg * a.chunks + c;
+  if (tid == 0) {
+    const uint32_t done = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    sm.last = done == (uint32_t)(nparts - 1);
+  }
+  __syncthreads();
+  if (!__builtin_amdgcn_readfirstlane(sm.last)) return;
+  constexpr int kBatch = 8;
+  const size_t slot0 = (size_t)bg * a.p_max;
+  for (int i = tid; i < rows_c * (D / 4); i += kThreads) {
+    const int r2 = i / (D / 4), d = 4 * (i - r2 * (D / 4));
+    const int rho = row0 + r2;
+    float mr = -INFINITY, wr = 0.f;
+    f32x4 ar = {0.f, 0.f, 0.f, 0.f};
+    bool nan = false;
+    for (int q0 = 0; q0 < nparts; q0 += kBatch) {
+      const int nb = min(kBatch, nparts - q0);
+      const brsrc r = buffer_rsrc(a.ws_o + (slot0 + q0) * R * D, (uint32_t)(nb * R * D * sizeof(float)));
+      float lp[kBatch];
+      f32x4 ov[kBatch];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        if (u < nb) {
+          lp[u] = ld_agent(a.ws_lse + (slot0 + q0 + u) * R + rho);
+          ov[u] = ld_agent4(r, (uint32_t)((((size_t)u * R + rho) * D + d) * sizeof(float)));
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        if (u < nb) {
+          if (lp[u] != lp[u]) nan = true;
+          if (lp[u] > -INFINITY) {   // a partition this row sees nothing of adds nothing
+            const float mn = fmaxf(mr, lp[u]);
+            const float sa = exp2_fast(mr - mn), sb = exp2_fast(lp[u] - mn);
+            ar = ar * sa + ov[u] * sb;
+            wr = wr * sa + sb;
+            mr = mn;
+          }
+        }
+      }
+    }
+    f32x4 val = {0.f, 0.f, 0.f, 0.f};
+    float lse = -INFINITY;
+    if (nan) {
+      val = f32x4{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
+      lse = __builtin_nanf("");
+    } else if (wr > 0.f) {
+      val = f32x4{ar[0] / wr, ar[1] / wr, ar[2] / wr, ar[3] / wr};
+      lse = (mr + log2_fast(wr)) * kLn2;
+    }
+    const int t = rho / G, h = rho - t * G;
+    const size_t orow = ((size_t)b * TQ + t) * a.num_q_heads + (size_t)g * G + h;
+    store_out4<IO>(a.out, orow * D + d, val);
+    if (d == 0 && a.lse_out) a.lse_out[orow] = lse;
+  }
+  if (tid == 0) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// ---------------------------------------------------------------------------
+// Host side.
+// ---------------------------------------------------------------------------
+struct Plan {
+  int rows, tiles, chunks, nt, p_max;
+  size_t cnt_off, o_off, lse_off, total;
+};
+
+static inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+static bool plan(const pa_shape* s, int q_len, Plan* out) {
+  if (!s) return false;
+  if (q_len < 1 || q_len > kMaxQLen) return false;
+  if (s->batch < 0 || s->batch > 65535) return false;
+  if (s->num_kv_heads < 1 || s->num_kv_heads > 65535) return false;
+  if (s->num_q_heads < 1 || s->num_q_heads % s->num_kv_heads != 0) return false;
+  const int G = s->num_q_heads / s->num_kv_heads;
+  if (G > kMaxGroup) return false;
+  if ((long long)s->batch * q_len * s->num_q_heads > 0x7fffffffLL) return false;
+  if (s->head_dim != 64 && s->head_dim != 128) return false;
+  if (s->block_size != kBlock) return false;
+  if (s->max_blocks_per_seq < 1 || s->max_blocks_per_seq > (1 << 26)) return false;
+  if (s->num_blocks < 1) return false;
+  if (s->partition_size < 0 || s->partition_size % kBlock != 0) return false;
+  Plan p;
+  p.rows = G * q_len;
+  p.tiles = (p.rows + 15) / 16;
+  p.nt = p.tiles == 1 ? 1 : 2;
+  p.chunks = (p.tiles + p.nt - 1) / p.nt;
+  const long long tokens = (long long)s->max_blocks_per_seq * kBlock;
+  p.p_max = s->partition_size ? (int)((tokens + s->partition_size - 1) / s->partition_size) : 1;
+  const long long units = (long long)s->batch * s->num_kv_heads * p.chunks * p.p_max;
+  if (units > 0x7fffffffLL) return false;
+  p.cnt_off = p.o_off = p.lse_off = p.total = 0;
+  if (s->partition_size) {
+    const size_t slots = (size_t)s->batch * s->num_kv_heads * p.p_max;
+    p.o_off = align_up((size_t)s->batch * s->num_kv_heads * p.chunks * sizeof(uint32_t), 256);
+    p.lse_off = p.o_off + align_up(slots * p.rows * s->head_dim * sizeof(float), 256);
+    p.total = p.lse_off + align_up(slots * p.rows * sizeof(float), 256);
+  }
+  *out = p;
+  return true;
+}
+
+template <typename IO, typename KV, int D>
+static hipError_t launch_nt(int nt, const Params& prm, dim3 grid, hipStream_t st) {
+  if (nt == 1)
+    hipLaunchKernelGGL((pa_multi_kernel<IO, KV, D, 1>), grid, dim3(kThreads), 0, st, prm);
+  else
+    hipLaunchKernelGGL((pa_multi_kernel<IO, KV, D, 2>), grid, dim3(kThreads), 0, st, prm);
+  return hipGetLastError();
+}
+
+template <typename IO, typename KV>
+static hipError_t launch_d(int D, int nt, const Params& prm, dim3 grid, hipStream_t st) {
+  return D == 64 ? launch_nt<IO, KV, 64>(nt, prm, grid, st) : launch_nt<IO, KV, 128>(nt, prm, grid, st);
+}
+
+static inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+}  // namespace pa_mq
+
+extern "C" {
+
+size_t pa_decode_multi_workspace_bytes(const pa_shape* shape, int32_t q_len) {
+  pa_mq::Plan p;
+  if (!pa_mq::plan(shape, q_len, &p)) return 0;
+  return p.total;
+}
+
+pa_status pa_decode_multi(const pa_shape* shape, int32_t q_len, const void* q, const void* k_cache,
+                          const void* v_cache, const int32_t* block_table,
+                          const int32_t* context_lens, float scale, pa_dtype io_dtype,
+                          pa_dtype kv_dtype, const float* k_scale, const float* v_scale,
+                          void* workspace, size_t workspace_bytes, void* out, float* lse_out,
+                          void* stream) {
+  using namespace pa_mq;
+  if (!shape) return PA_ERR_NULL;
+  Plan pl;
+  if (!plan(shape, q_len, &pl)) return PA_ERR_SHAPE;
+  if (!q || !k_cache || !v_cache || !block_table || !context_lens || !out) return PA_ERR_NULL;
+  const bool io_ok = io_dtype == PA_F32 || io_dtype == PA_F16 || io_dtype == PA_BF16;
+  const bool kv_ok = kv_dtype == io_dtype || (kv_dtype == PA_FP8_E4M3 && io_dtype != PA_F32);
+  if (!io_ok || !kv_ok) return PA_ERR_DTYPE;
+  if (kv_dtype == PA_FP8_E4M3 && (!k_scale || !v_scale)) return PA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out))
+    return PA_ERR_ALIGN;
+  if (((uintptr_t)block_table & 3u) || ((uintptr_t)context_lens & 3u) ||
+      ((uintptr_t)lse_out & 3u))
+    return PA_ERR_ALIGN;
+  if (shape->partition_size != 0) {
+    if (!workspace || workspace_bytes < pl.total) return PA_ERR_WORKSPACE;
+    if ((uintptr_t)workspace & 255u) return PA_ERR_ALIGN;
+  }
+  if (shape->batch == 0) return PA_OK;
+
+  Params prm;
+  prm.q = static_cast<const uint8_t*>(q);
+  prm.k = static_cast<const uint8_t*>(k_cache);
+  prm.v = static_cast<const uint8_t*>(v_cache);
+  prm.block_table = block_table;
+  prm.context_lens = context_lens;
+  prm.k_scale = k_scale;
+  prm.v_scale = v_scale;
+  prm.out = static_cast<uint8_t*>(out);
+  prm.lse_out = lse_out;
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  const bool split = shape->partition_size != 0;
+  prm.ws_o = split ? reinterpret_cast<float*>(ws + pl.o_off) : nullptr;
+  prm.ws_lse = split ? reinterpret_cast<float*>(ws + pl.lse_off) : nullptr;
+  prm.ws_cnt = split ? reinterpret_cast<uint32_t*>(ws + pl.cnt_off) : nullptr;
+  prm.scale = scale;
+  prm.batch = shape->batch;
+  prm.num_q_heads = shape->num_q_heads;
+  prm.num_kv_heads = shape->num_kv_heads;
+  prm.group = shape->num_q_heads / shape->num_kv_heads;
+  prm.q_len = q_len;
+  prm.rows = pl.rows;
+  prm.chunks = pl.chunks;
+  prm.max_blocks_per_seq = shape->max_blocks_per_seq;
+  prm.num_blocks = shape->num_blocks;
+  prm.part_tokens = shape->partition_size;
+  prm.p_max = pl.p_max;
+
+  const long long units = (long long)shape->batch * shape->num_kv_heads * pl.chunks * pl.p_max;
+  const dim3 grid((unsigned)units, 1, 1);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int D = shape->head_dim;
+  hipError_t e;
+  if (io_dtype == PA_F32)
+    e = launch_d<F32, F32>(D, pl.nt, prm, grid, st);
+  else if (io_dtype == PA_F16)
+    e = kv_dtype == PA_FP8_E4M3 ? launch_d<F16, FP8>(D, pl.nt, prm, grid, st)
+                                : launch_d<F16, F16>(D, pl.nt, prm, grid, st);
+  else
+    e = kv_dtype == PA_FP8_E4M3 ? launch_d<BF16, FP8>(D, pl.nt, prm, grid, st)
+                                : launch_d<BF16, BF16>(D, pl.nt, prm, grid, st);
+  return e == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+}  // extern "C"

@@ -174,17 +174,19 @@ struct Tile16 {
   struct VRegs {
     u32x2 v[kT];
   };
+  typedef A8 QC;                           // one 16-byte chunk of the query operand
+  static constexpr int kQ = kK;            // chunks per lane
   struct Q {
-    A8 c[kK];
+    QC c[kQ];
   };
   static __device__ __forceinline__ uint32_t koff(int lane) { return lane * 16; }
   static __device__ __forceinline__ uint32_t voff(int lane) { return (lane & 15) * 32 + (lane >> 4) * 8; }
+  // byte offset in the query row of chunk c of lane group jj:
+  // head-dim 8*(jj + 4c) .. +7
+  static __device__ __forceinline__ uint32_t qoff(int c, int jj) { return 16 * (jj + 4 * c); }
   static __device__ __forceinline__ void load_q(Q& q, gptr qrow, int jj) {
 #pragma unroll
-    for (int c = 0; c < kK; ++c) {
-      const u32x4 raw = ld<u32x4>(qrow, 16 * (jj + 4 * c));   // head-dim 8*(jj + 4c) .. +7
-      q.c[c] = __builtin_bit_cast(A8, raw);
-    }
+    for (int c = 0; c < kQ; ++c) q.c[c] = __builtin_bit_cast(QC, ld<u32x4>(qrow, qoff(c, jj)));
   }
   static __device__ __forceinline__ void load_k(KRegs& r, gptr kp, uint32_t ko) {
 #pragma unroll
@@ -235,18 +237,20 @@ struct Tile8 {
   struct VRegs {
     uint32_t v[kT];
   };
+  typedef A8 QC;
+  static constexpr int kQ = 2 * kK;
   struct Q {
-    A8 c[2 * kK];
+    QC c[kQ];
   };
   static __device__ __forceinline__ uint32_t koff(int lane) { return lane * 16; }
   static __device__ __forceinline__ uint32_t voff(int lane) { return (lane & 15) * 16 + (lane >> 4) * 4; }
+  // head-dim 16*(jj + 4*(c/2)) + 8*(c%2) .. +7
+  static __device__ __forceinline__ uint32_t qoff(int c, int jj) {
+    return 2 * (16 * (jj + 4 * (c / 2)) + 8 * (c % 2));
+  }
   static __device__ __forceinline__ void load_q(Q& q, gptr qrow, int jj) {
 #pragma unroll
-    for (int c = 0; c < 2 * kK; ++c) {
-      // head-dim 16*(jj + 4*(c/2)) + 8*(c%2) .. +7
-      const u32x4 raw = ld<u32x4>(qrow, 2 * (16 * (jj + 4 * (c / 2)) + 8 * (c % 2)));
-      q.c[c] = __builtin_bit_cast(A8, raw);
-    }
+    for (int c = 0; c < kQ; ++c) q.c[c] = __builtin_bit_cast(QC, ld<u32x4>(qrow, qoff(c, jj)));
   }
   static __device__ __forceinline__ void load_k(KRegs& r, gptr kp, uint32_t ko) {
 #pragma unroll
@@ -295,16 +299,18 @@ struct Tile32 {
   struct VRegs {
     f32x4 v[kT];
   };
+  typedef f32x4 QC;
+  static constexpr int kQ = kK;
   struct Q {
-    f32x4 c[kK];
+    QC c[kQ];
   };
   static __device__ __forceinline__ uint32_t koff(int lane) { return lane * 16; }
   static __device__ __forceinline__ uint32_t voff(int lane) { return (lane & 15) * 64 + (lane >> 4) * 16; }
+  // head-dim 4*(jj + 4c) .. +3
+  static __device__ __forceinline__ uint32_t qoff(int c, int jj) { return 16 * (jj + 4 * c); }
   static __device__ __forceinline__ void load_q(Q& q, gptr qrow, int jj) {
 #pragma unroll
-    for (int c = 0; c < kK; ++c) {
-      q.c[c] = ld<f32x4>(qrow, 16 * (jj + 4 * c));   // head-dim 4*(jj + 4c) .. +3
-    }
+    for (int c = 0; c < kQ; ++c) q.c[c] = ld<f32x4>(qrow, qoff(c, jj));
   }
   static __device__ __forceinline__ void load_k(KRegs& r, gptr kp, uint32_t ko) {
 #pragma unroll

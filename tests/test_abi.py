@@ -174,3 +174,57 @@ def test_lse_merge_rejects_bad_arguments_before_any_launch():
     assert m(2, 4, 128, FAKE + 8, FAKE, 1, FAKE, None, None) == 5
     assert m(2, 4, 128, FAKE, FAKE + 2, 1, FAKE, None, None) == 5
     assert m(2, 0, 128, FAKE, FAKE, 1, FAKE, None, None) == 0        # no rows: no-op
+
+
+def call_multi(s, q_len=4, io=1, kv=1, ks=None, vs=None, ws=None, wsb=0, out=FAKE, q=FAKE,
+               k=FAKE, v=FAKE, bt=FAKE, cl=FAKE, lse=None):
+    lib = _lib.load_library()
+    sp = ctypes.byref(s) if s is not None else None
+    return lib.pa_decode_multi(sp, q_len, q, k, v, bt, cl, 0.1, io, kv, ks, vs, ws, wsb, out,
+                               lse, None)
+
+
+def test_multi_token_call_rejects_bad_arguments_before_any_launch():
+    assert call_multi(None) == 1
+    for kw in ("q", "k", "v", "bt", "cl", "out"):
+        assert call_multi(shape(), **{kw: None}) == 1, kw
+    for T in (0, 17, -1):
+        assert call_multi(shape(), q_len=T) == 2
+    assert call_multi(shape(partition_size=-1)) == 2             # no balanced split here
+    assert call_multi(shape(partition_size=24)) == 2
+    assert call_multi(shape(num_q_heads=40, num_kv_heads=2)) == 2
+    assert call_multi(shape(), io=0, kv=3, ks=FAKE, vs=FAKE) == 3
+    assert call_multi(shape(), io=1, kv=3) == 1
+    assert call_multi(shape(), q=FAKE + 8) == 5
+    s = shape(partition_size=512)
+    need = _lib.load_library().pa_decode_multi_workspace_bytes(ctypes.byref(s), 4)
+    assert call_multi(s) == 4
+    assert call_multi(s, ws=FAKE, wsb=need - 1) == 4
+    assert call_multi(s, ws=FAKE + 16, wsb=need) == 5
+    assert call_multi(shape(batch=0, partition_size=512), ws=FAKE, wsb=need) == 0
+
+
+def test_multi_token_workspace_size_arithmetic():
+    lib = _lib.load_library()
+
+    def ws(T, **kw):
+        return lib.pa_decode_multi_workspace_bytes(ctypes.byref(shape(**kw)), T)
+
+    def up(x):
+        return (x + 255) // 256 * 256
+
+    assert ws(4) == 0 and ws(0, partition_size=512) == 0 and ws(17, partition_size=512) == 0
+    assert lib.pa_decode_multi_workspace_bytes(None, 4) == 0
+    # B=32, Hq=28, Hkv=4 (G=7), T=8 -> 56 rows = 4 column tiles = 2 chunks;
+    # MBS=256, partition 512 -> 8 partitions
+    b, hkv, d, p, rows, chunks = 32, 4, 128, 8, 56, 2
+    expect = up(b * hkv * chunks * 4) + up(b * hkv * p * rows * d * 4) + up(b * hkv * p * rows * 4)
+    assert ws(8, batch=b, num_q_heads=28, num_kv_heads=hkv, max_blocks_per_seq=256,
+              partition_size=512) == expect
+    # G=16, T=16: 256 rows, 8 chunks; one partition of 16 tokens per block
+    expect = up(2 * 1 * 8 * 4) + up(2 * 1 * 32 * 256 * 64 * 4) + up(2 * 1 * 32 * 256 * 4)
+    assert ws(16, batch=2, num_q_heads=16, num_kv_heads=1, head_dim=64,
+              partition_size=16) == expect
+    # one new token: the same rows as decode, one counter per (sequence, KV head)
+    s = shape(partition_size=512)
+    assert ws(1, partition_size=512) == lib.pa_decode_workspace_bytes(ctypes.byref(s))
