@@ -41,7 +41,10 @@ if ROOT not in sys.path:
 METRIC = "paged decode attention KV-read GB/s (% of HBM peak) and seqs·tokens/sec"
 PEAK_GBPS = 8000.0            # MI355X HBM3E, published
 MALL_BYTES = 256 << 20        # Infinity Cache
-KERNEL_SRC = os.path.join(ROOT, "paged_kv_decode_05_amd", "csrc", "pa_decode.hip")
+CSRC = os.path.join(ROOT, "paged_kv_decode_05_amd", "csrc")
+# the sources each kernel is compiled from (its file and the headers it includes)
+KERNEL_SRCS = {"decode": ("pa_decode.hip", "pa_tiles.h", "pa_schedule.h"),
+               "multi": ("pa_multi.hip", "pa_tiles.h")}
 PROBES = os.path.join(ROOT, "tests", "probes", "libpaprobes.so")
 
 
@@ -60,32 +63,40 @@ def parse():
                     help="minimum host time spent timing the oracle")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-stream-ceiling", action="store_true")
-    ap.add_argument("--op", choices=["decode", "append", "merge", "pool"], default="decode",
+    ap.add_argument("--op", choices=["decode", "multi", "append", "merge", "pool"],
+                    default="decode",
                     help="decode: the attention call (default); append: the paged KV "
                          "append of one new token per sequence on the same workload; "
+                         "multi: --qlen new tokens per sequence, causal among them "
+                         "(pa_decode_multi); "
                          "merge: the log-sum-exp merge of --shards position shards; "
                          "pool: the host block pool's bookkeeping for the workload's "
                          "requests behind a shared prompt prefix")
     ap.add_argument("--shards", type=int, default=8, help="shards for --op merge")
+    ap.add_argument("--qlen", type=int, default=8, help="new tokens per sequence for --op multi")
     ap.add_argument("--pmc-pass", action="store_true",
                     help="run a 1 GiB device copy and 20 decode calls, print nothing else "
                          "(for rocprofv3 --pmc counter passes)")
     return ap.parse_args()
 
 
-def kernel_sha256():
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+def kernel_sha256(kernel="decode"):
+    h = hashlib.sha256()
+    for name in KERNEL_SRCS[kernel]:
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def mode_name(ps):
     return {0: "one_pass", -1: "balanced"}.get(ps, f"partition{ps}")
 
 
-def traffic_from_profile(wl_name, ps):
+def traffic_from_profile(wl_name, ps, kernel="decode", q_len=None):
     """HBM bytes per launch from the committed counter summary, if it was taken
-    on the current kernel source; else None."""
-    path = os.path.join(ROOT, "profiles", f"pmc_traffic_{wl_name}_{mode_name(ps)}.md")
+    on the current kernel sources; else None."""
+    tag = wl_name if q_len is None else f"multi_{wl_name}_T{q_len}"
+    path = os.path.join(ROOT, "profiles", f"pmc_traffic_{tag}_{mode_name(ps)}.md")
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -93,7 +104,7 @@ def traffic_from_profile(wl_name, ps):
             m = re.match(r"^machine:\s*(\{.*\})\s*$", line)
             if m:
                 rec = json.loads(m.group(1))
-                if rec.get("kernel_sha256") == kernel_sha256():
+                if rec.get("kernel_sha256") == kernel_sha256(kernel):
                     return rec.get("traffic_bytes_per_launch")
     return None
 
@@ -128,16 +139,21 @@ def stream_read_ceiling(torch):
     return best
 
 
+def blas_threads():
+    """Threads the oracle's numpy BLAS may use."""
+    try:
+        from threadpoolctl import threadpool_info
+        return max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        return 1
+
+
 def cpu_baseline(wl, gpu_out_f64, min_seconds):
     """Time the float64 oracle on the host over the whole workload (repeated
     until min_seconds have passed) and compare the GPU output with it."""
     import numpy as np
     import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        cores = 1
+    cores = blas_threads()
     s = wl.spec
     reps, t0 = 0, time.perf_counter()
     while True:
@@ -298,6 +314,121 @@ def bench_merge(args, torch, np, pkd, W):
     print(json.dumps(rec), flush=True)
 
 
+def bench_multi(args, torch, np, pkd, W):
+    """Time pa_decode_multi with --qlen new tokens per sequence on the
+    workload (their K/V counted in the context lengths, as after the append).
+    Bytes = the K/V of every attended (sequence, cached token, KV head), as
+    for decode, plus q read and out written; flops = 4 * D per visible
+    (query row, key) pair. Both the workload's partition size and the one-pass
+    split are timed; `value` is the faster."""
+    import oracle
+    spec = W.SPECS[args.workload]
+    T = args.qlen
+    wl = W.make_workload(spec)
+    q = W.multi_query(wl, T)
+    dev = torch.device("cuda:0")
+    t = W.to_device(wl, dev)
+    qt = W.storage_tensor(q, spec.io_dtype).to(dev)
+    pool_bytes = t["k_cache"].numel() * t["k_cache"].element_size() * 2
+    reps = max(1, math.ceil(3 * MALL_BYTES / pool_bytes))
+    kcs = [t["k_cache"]] + [t["k_cache"].clone() for _ in range(reps - 1)]
+    vcs = [t["v_cache"]] + [t["v_cache"].clone() for _ in range(reps - 1)]
+    out = torch.empty_like(qt)
+    stream = torch.cuda.current_stream()
+
+    def make_calls(ps):
+        ws = None
+        if ps:
+            ws = torch.empty(pkd.workspace_bytes(qt, t["k_cache"], t["block_table"], ps),
+                             dtype=torch.uint8, device=dev)
+            pkd.reset_workspace(ws)
+        return [pkd.prepare(qt, kcs[i], vcs[i], t["block_table"], t["context_lens"],
+                            float(wl.scale), k_scale=t["k_scale"], v_scale=t["v_scale"],
+                            partition_size=ps, out=out, workspace=ws, stream=stream)
+                for i in range(reps)]
+
+    modes = [args.partition_size] if args.partition_size is not None else \
+        [spec.partition_size, 0]
+    if args.pmc_pass:
+        calls = make_calls(modes[0])
+        src = torch.ones(1 << 28, dtype=torch.int32, device=dev)      # 1 GiB
+        torch.empty_like(src).copy_(src)
+        for i in range(20):
+            calls[i % reps]()
+        torch.cuda.synchronize()
+        return
+    timed = {}
+    for mode in modes:
+        calls = make_calls(mode)
+        for i in range(args.warmup):
+            calls[i % reps]()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(args.steps):
+            calls[i % reps]()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        timed[mode] = (e0.elapsed_time(e1) / args.steps,
+                       out.float().cpu().numpy().astype(np.float64))
+    ps = min(timed, key=lambda m: timed[m][0])
+    ms, gpu_out = timed[ps]
+    es = oracle.ELEM_BYTES[spec.io_dtype]
+    qo_bytes = 2 * spec.batch * T * spec.num_q_heads * spec.head_dim * es
+    moved = wl.kv_bytes_logical() + qo_bytes
+    L = wl.context_lens.astype(np.int64)
+    visible = int(sum(max(int(l) - T + i + 1, 0) for l in L for i in range(T)))
+    flops = 4 * spec.head_dim * spec.num_q_heads * visible
+    gbps = moved / (ms / 1e3) / 1e9
+    tflops = flops / (ms / 1e3) / 1e12
+    mfma_peak = {"f32": 157.3, "f16": 2500.0, "bf16": 2500.0}[spec.io_dtype]
+    rec = {
+        "metric": "multi-token paged attention bytes moved GB/s (KV read + q/out)",
+        "value": round(gbps, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 6), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None,
+        "dtype": spec.io_dtype + ("" if spec.kv_dtype == spec.io_dtype else "+fp8_e4m3_kv"),
+        "data": "synthetic (seeded N(0,1) q/K/V, seeded lengths and block permutation)",
+        "config": {"workload": spec.name, "op": "decode_multi", "q_len": T,
+                   "batch": spec.batch, "q_heads": spec.num_q_heads,
+                   "kv_heads": spec.num_kv_heads, "head_dim": spec.head_dim,
+                   "split": mode_name(ps), "bytes_per_step": moved,
+                   "kv_bytes_per_step": wl.kv_bytes_logical(), "flops_per_step": flops,
+                   "pool_copies_rotated": reps},
+        "roofline": {"bound": "hbm", "achieved": round(gbps, 2), "peak": PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(gbps / PEAK_GBPS, 4),
+                     "traffic": traffic_from_profile(spec.name, ps, "multi", T)},
+        "mfma": {"achieved_TFLOPs": round(tflops, 2), "peak_TFLOPs": mfma_peak,
+                 "frac": round(tflops / mfma_peak, 4)},
+        "modes": {mode_name(m): {"ms_per_step": round(v[0], 6),
+                                 "GBps": round(moved / (v[0] / 1e3) / 1e9, 2)}
+                  for m, v in timed.items()},
+    }
+    if not args.no_cpu_baseline:
+        # oracle on whole sequences, in order, until --cpu-seconds pass
+        seqs, t0, kvb = [], time.perf_counter(), 0
+        per_tok = 2 * spec.num_kv_heads * spec.head_dim * oracle.ELEM_BYTES[spec.kv_dtype]
+        while len(seqs) < spec.batch and time.perf_counter() - t0 < args.cpu_seconds:
+            b = len(seqs)
+            oracle.multi_query_ref(q, wl.k_cache, wl.v_cache, wl.block_table,
+                                   wl.context_lens, wl.scale, spec.io_dtype, spec.kv_dtype,
+                                   wl.k_scale, wl.v_scale, seqs=[b])
+            seqs.append(b)
+            kvb += int(L[b]) * per_tok
+        el = time.perf_counter() - t0
+        ref = oracle.multi_query_ref(q, wl.k_cache, wl.v_cache, wl.block_table,
+                                     wl.context_lens, wl.scale, spec.io_dtype, spec.kv_dtype,
+                                     wl.k_scale, wl.v_scale, seqs=seqs[:2])
+        err = np.abs(gpu_out[seqs[:2]] - ref[seqs[:2]])
+        rec["cpu_baseline"] = {"value": round(kvb / el / 1e9, 5), "unit": "GB/s",
+                               "cores": int(blas_threads()),
+                               "kind": "oracle",
+                               "sample": f"{len(seqs)} of {spec.batch} sequences in {el:.1f} s "
+                                         f"(KV bytes of those sequences / time)",
+                               "parity_vs_gpu": {"max_abs": float(err.max())}}
+    print(json.dumps(rec), flush=True)
+
+
 def pool_requests(np, W, spec):
     """Token ids of the workload's requests: the shared prompt prefix (the
     workload's shared_prefix_tokens) followed by a random tail, each request
@@ -405,6 +536,8 @@ def main():
 
     if args.op == "append":
         return bench_append(args, torch, np, pkd, W)
+    if args.op == "multi":
+        return bench_multi(args, torch, np, pkd, W)
     if args.op == "merge":
         return bench_merge(args, torch, np, pkd, W)
     if args.op == "pool":

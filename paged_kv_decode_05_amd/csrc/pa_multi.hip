@@ -175,6 +175,9 @@ pa_multi_kernel(const Params a) {
 
   constexpr int kKS = T::kKStages, kVS = T::kVStages;
   constexpr int dK = kKS - 1, dV = kVS - 1;
+  // a V load reuses the page offset its K load recorded, so V may not run
+  // ahead of K
+  static_assert(kKS >= 1 && kVS >= 1 && dV <= dK, "ring depths");
   constexpr int kAhead = dK > 1 ? dK : 1;
   typename T::KRegs ring_k[kKS];
   typename T::VRegs ring_v[kVS];
