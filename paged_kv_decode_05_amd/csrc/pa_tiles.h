@@ -40,17 +40,26 @@ constexpr int gcd_c(int x, int y) { return y == 0 ? x : gcd_c(y, x % y); }
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float log2_fast(float x) { return __builtin_amdgcn_logf(x); }
 
-// Lanes l, l^16, l^32, l^48 hold the same query head.
-__device__ __forceinline__ float wave_max_rows(float x) {
-  x = fmaxf(x, __shfl_xor(x, 16));
-  x = fmaxf(x, __shfl_xor(x, 32));
-  return x;
+// Lanes l, l^16, l^32, l^48 hold the same query head. The reductions use
+// gfx950's lane-swap instructions: with x in both operands,
+// v_permlane16_swap returns the pair {x[l], x[l^16]} (in some order) and
+// v_permlane32_swap the pair {x[l], x[l^32]}, in the vector ALU, without the
+// LDS round trip a bpermute makes. max and + are commutative, so every lane
+// of a head gets the same bits (and the same bits as the xor-shuffle form).
+__device__ __forceinline__ float pair_max(float x, bool wide) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  const auto r = wide ? __builtin_amdgcn_permlane32_swap(u, u, false, false)
+                      : __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  return fmaxf(__builtin_bit_cast(float, (uint32_t)r[0]), __builtin_bit_cast(float, (uint32_t)r[1]));
 }
-__device__ __forceinline__ float wave_sum_rows(float x) {
-  x += __shfl_xor(x, 16);
-  x += __shfl_xor(x, 32);
-  return x;
+__device__ __forceinline__ float pair_sum(float x, bool wide) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  const auto r = wide ? __builtin_amdgcn_permlane32_swap(u, u, false, false)
+                      : __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  return __builtin_bit_cast(float, (uint32_t)r[0]) + __builtin_bit_cast(float, (uint32_t)r[1]);
 }
+__device__ __forceinline__ float wave_max_rows(float x) { return pair_max(pair_max(x, false), true); }
+__device__ __forceinline__ float wave_sum_rows(float x) { return pair_sum(pair_sum(x, false), true); }
 
 // Global-memory pointer every lane agrees on, kept in scalar registers, so
 // loads take the saddr + 32-bit voffset form of global_load.

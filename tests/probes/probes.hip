@@ -2,7 +2,9 @@
 //  * the lane layout of the 16x16 MFMA operands and accumulator
 //    (A: lane l holds row l%16, B: lane l holds column l%16, both with the
 //    same per-lane k-slots; C: lane l holds rows 4*(l/16)+i of column l%16);
-//  * exactness of the E4M3 -> f16 / bf16 conversion instructions.
+//  * exactness of the E4M3 -> f16 / bf16 conversion instructions;
+//  * the lane pairs gfx950's v_permlane16_swap / v_permlane32_swap return
+//    when both operands hold the same register (the row reductions use them).
 // Each probe is one 64-thread workgroup over small, fully in-bounds buffers.
 // pa_probe_schedule runs the balanced split's work-line arithmetic (the same
 // header the kernel uses) on the host, so its coverage can be checked without
@@ -76,6 +78,25 @@ __global__ void fp8_probe_kernel(const uint32_t* codes, uint32_t* out16, uint32_
   bf16x2 bhi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true);
   outb[2 * l] = __builtin_bit_cast(uint32_t, blo);
   outb[2 * l + 1] = __builtin_bit_cast(uint32_t, bhi);
+}
+
+// in: 64 words; out: 4 words per lane -- the two results of the 16-lane
+// swap, then the two of the 32-lane swap, each with in[l] in both operands.
+__global__ void permlane_probe_kernel(const uint32_t* in, uint32_t* out) {
+  const int l = threadIdx.x;
+  const uint32_t x = in[l];
+  const auto a = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+  const auto b = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  out[4 * l + 0] = a[0];
+  out[4 * l + 1] = a[1];
+  out[4 * l + 2] = b[0];
+  out[4 * l + 3] = b[1];
+}
+
+extern "C" int pa_probe_permlane(const void* in, void* out, void* stream) {
+  hipLaunchKernelGGL(permlane_probe_kernel, dim3(1), dim3(64), 0, (hipStream_t)stream,
+                     (const uint32_t*)in, (uint32_t*)out);
+  return hipGetLastError() == hipSuccess ? 0 : 2;
 }
 
 extern "C" int pa_probe_mfma(int which, const void* A, const void* B, float* C, void* stream) {

@@ -21,6 +21,7 @@ def lib():
     L.pa_probe_mfma.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
                                 ctypes.c_void_p, ctypes.c_void_p]
     L.pa_probe_fp8.argtypes = [ctypes.c_void_p] * 4
+    L.pa_probe_permlane.argtypes = [ctypes.c_void_p] * 3
     return L
 
 
@@ -58,3 +59,19 @@ def test_fp8_widening_is_exact():
     assert np.array_equal(np.isnan(f16), nan) and np.array_equal(np.isnan(bf), nan)
     assert np.array_equal(f16[~nan], ref[~nan])
     assert np.array_equal(bf[~nan], ref[~nan])
+
+
+def test_permlane_swaps_pair_lanes_16_and_32_apart():
+    # with the same register in both operands, the 16-lane swap must hand
+    # lane l the values of lanes l and l^16, the 32-lane swap those of l and
+    # l^32 (the head reductions take max / sum of the pair)
+    print("probe permlane", flush=True)
+    vals = torch.arange(1000, 1064, dtype=torch.int32).cuda()
+    out = torch.zeros(256, dtype=torch.int32, device="cuda")
+    s = torch.cuda.current_stream()
+    assert lib().pa_probe_permlane(vals.data_ptr(), out.data_ptr(), s.cuda_stream) == 0
+    torch.cuda.synchronize()
+    o = out.cpu().numpy().reshape(64, 4)
+    for l in range(64):
+        assert sorted(o[l, :2]) == sorted([1000 + l, 1000 + (l ^ 16)]), (l, o[l])
+        assert sorted(o[l, 2:]) == sorted([1000 + l, 1000 + (l ^ 32)]), (l, o[l])
