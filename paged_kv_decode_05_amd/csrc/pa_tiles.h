@@ -82,6 +82,12 @@ template <typename V>
 __device__ __forceinline__ V ld_nt(gptr base, uint32_t off) {
   return __builtin_nontemporal_load((const __attribute__((address_space(1))) V*)(base + off));
 }
+// kKeep: an ordinary load, for pages that other workgroups read again soon
+template <bool kKeep, typename V>
+__device__ __forceinline__ V ld_page(gptr base, uint32_t off) {
+  if constexpr (kKeep) return ld<V>(base, off);
+  else return ld_nt<V>(base, off);
+}
 
 // Agent-coherent (write-through / cache-revalidating) float store and load.
 __device__ __forceinline__ void st_agent(float* p, float v) {
@@ -204,13 +210,15 @@ struct Tile16 {
 #pragma unroll
     for (int c = 0; c < kQ; ++c) q.c[c] = __builtin_bit_cast(QC, ld<u32x4>(qrow, qoff(c, jj)));
   }
+  template <bool kKeep = false>
   static __device__ __forceinline__ void load_k(KRegs& r, gptr kp, uint32_t ko) {
 #pragma unroll
-    for (int i = 0; i < kK; ++i) r.k[i] = ld_nt<u32x4>(kp, ko + i * 1024);
+    for (int i = 0; i < kK; ++i) r.k[i] = ld_page<kKeep, u32x4>(kp, ko + i * 1024);
   }
+  template <bool kKeep = false>
   static __device__ __forceinline__ void load_v(VRegs& r, gptr vp, uint32_t vo) {
 #pragma unroll
-    for (int t = 0; t < kT; ++t) r.v[t] = ld_nt<u32x2>(vp, vo + t * 512);
+    for (int t = 0; t < kT; ++t) r.v[t] = ld_page<kKeep, u32x2>(vp, vo + t * 512);
   }
   static __device__ __forceinline__ f32x4 scores(const KRegs& r, const Q& q) {
     f32x4 s = {0.f, 0.f, 0.f, 0.f};
@@ -268,13 +276,15 @@ struct Tile8 {
 #pragma unroll
     for (int c = 0; c < kQ; ++c) q.c[c] = __builtin_bit_cast(QC, ld<u32x4>(qrow, qoff(c, jj)));
   }
+  template <bool kKeep = false>
   static __device__ __forceinline__ void load_k(KRegs& r, gptr kp, uint32_t ko) {
 #pragma unroll
-    for (int i = 0; i < kK; ++i) r.k[i] = ld_nt<u32x4>(kp, ko + i * 1024);
+    for (int i = 0; i < kK; ++i) r.k[i] = ld_page<kKeep, u32x4>(kp, ko + i * 1024);
   }
+  template <bool kKeep = false>
   static __device__ __forceinline__ void load_v(VRegs& r, gptr vp, uint32_t vo) {
 #pragma unroll
-    for (int t = 0; t < kT; ++t) r.v[t] = ld_nt<uint32_t>(vp, vo + t * 256);
+    for (int t = 0; t < kT; ++t) r.v[t] = ld_page<kKeep, uint32_t>(vp, vo + t * 256);
   }
   static __device__ __forceinline__ f32x4 scores(const KRegs& r, const Q& q) {
     f32x4 s = {0.f, 0.f, 0.f, 0.f};
@@ -328,13 +338,15 @@ struct Tile32 {
 #pragma unroll
     for (int c = 0; c < kQ; ++c) q.c[c] = ld<f32x4>(qrow, qoff(c, jj));
   }
+  template <bool kKeep = false>
   static __device__ __forceinline__ void load_k(KRegs& r, gptr kp, uint32_t ko) {
 #pragma unroll
-    for (int i = 0; i < kK; ++i) r.k[i] = ld_nt<f32x4>(kp, ko + i * 1024);
+    for (int i = 0; i < kK; ++i) r.k[i] = ld_page<kKeep, f32x4>(kp, ko + i * 1024);
   }
+  template <bool kKeep = false>
   static __device__ __forceinline__ void load_v(VRegs& r, gptr vp, uint32_t vo) {
 #pragma unroll
-    for (int t = 0; t < kT; ++t) r.v[t] = ld_nt<f32x4>(vp, vo + t * 1024);
+    for (int t = 0; t < kT; ++t) r.v[t] = ld_page<kKeep, f32x4>(vp, vo + t * 1024);
   }
   static __device__ __forceinline__ f32x4 scores(const KRegs& r, const Q& q) {
     f32x4 s = {0.f, 0.f, 0.f, 0.f};
