@@ -205,3 +205,17 @@ def test_verify_step_append_then_attend(io, kv, ps):
     q = W.multi_query(wl, T)
     out = run_multi(wl, q, t=t, lens=torch.from_numpy(wl.context_lens).cuda())
     check(wl, to_f64(out), ref_multi(wl, q), label=spec.name)
+
+
+def test_largest_batch_and_rows_sampled():
+    # 2048 sequences of up to 40 tokens, 16 query heads on one KV head and 16
+    # new tokens: 256 rows (eight chunks) per pair, 16384 workgroups in one
+    # pass; the oracle checks a sample of sequences (all the short ones too)
+    spec = W.Spec("mq_large", 2048, 16, 1, 64, "bf16", "bf16", ("uniform", 0, 40), 3,
+                  ("ratio", 1.2), 0, 0, 41)
+    wl = W.make_workload(spec)
+    q = W.multi_query(wl, 16)
+    print(f"case {spec.name}", flush=True)
+    out = to_f64(run_multi(wl, q))
+    seqs = sorted(set([0, 1, 777, 2047] + [int(b) for b in np.nonzero(wl.context_lens < 16)[0][:8]]))
+    check(wl, out, ref_multi(wl, q, seqs=seqs), seqs=seqs, label="large")
