@@ -63,6 +63,8 @@ def parse():
                     help="minimum host time spent timing the oracle")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-stream-ceiling", action="store_true")
+    ap.add_argument("--no-flush-check", action="store_true",
+                    help="skip the cross-check that times single calls after evicting the caches")
     ap.add_argument("--op", choices=["decode", "multi", "append", "merge", "pool"],
                     default="decode",
                     help="decode: the attention call (default); append: the paged KV "
@@ -599,6 +601,26 @@ def main():
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / args.steps, out.float().cpu().numpy().astype(np.float64)
 
+    def flush_check(mode, n=40):
+        """Median time of single calls, each after a 1 GiB write that evicts
+        L2 and the Infinity Cache (events around the call only): a
+        cross-check of the rotated-pool timing."""
+        calls = make_calls(mode)
+        scratch = torch.empty(1 << 28, dtype=torch.int32, device=dev)
+        times = []
+        for i in range(n + 3):
+            scratch.fill_(i)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            calls[0]()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            if i >= 3:
+                times.append(e0.elapsed_time(e1) * 1e3)
+        del scratch
+        times.sort()
+        return times[len(times) // 2]
+
     timed = {}
     for mode in modes:
         timed[mode] = time_mode(mode)
@@ -611,6 +633,7 @@ def main():
     sum_tokens = int(wl.context_lens.astype(np.int64).sum())
     traffic = traffic_from_profile(spec.name, ps)
     ceiling = None if args.no_stream_ceiling else stream_read_ceiling(torch)
+    flushed_us = None if args.no_flush_check else flush_check(ps)
 
     rec = {
         "metric": METRIC,
@@ -643,6 +666,7 @@ def main():
         },
         "pct_hbm_peak": round(100.0 * gbps / PEAK_GBPS, 2),
         "seq_tokens_per_s": round(sum_tokens / (ms / 1e3), 1),
+        "seqs_per_s": round(spec.batch / (ms / 1e3), 1),
         "roofline": {
             "bound": "hbm",
             "achieved": round(gbps, 2),
@@ -652,6 +676,10 @@ def main():
             "traffic": traffic,
         },
         "stream_read_ceiling_GBps": None if ceiling is None else round(ceiling, 1),
+        "pct_stream_ceiling": None if ceiling is None else round(100.0 * gbps / ceiling, 2),
+        "flush_check": None if flushed_us is None else {
+            "us_median_single_call_after_cache_eviction": round(flushed_us, 2),
+            "GBps": round(kv_bytes / (flushed_us / 1e6) / 1e9, 2), "mode": mode_name(ps)},
         "modes": {mode_name(m): {"partition_size": m, "ms_per_step": round(v[0], 6),
                                  "GBps": round(kv_bytes / (v[0] / 1e3) / 1e9, 2),
                                  "max_abs_vs_value_mode": float(np.abs(v[1] - gpu_out).max())}
