@@ -116,3 +116,49 @@ def test_identical_keys_average_the_visible_values(L, T):
             assert abs(lse[0, t, h] - (s + math.log(n))) < 1e-12
             if n > 1:
                 assert not np.allclose(out[0, t, h], V[: n - 1].mean(axis=0), rtol=0, atol=1e-9)
+
+
+def _mutated_multi(kind):
+    """The oracle's definition with one plausible mistake planted."""
+    from oracle.formats import decode
+    from oracle.paged_decode import attend, gather_kv
+
+    def fn(q, k_cache, v_cache, block_table, context_lens, scale, io, kv):
+        qv = decode(q, io)
+        B, T, Hq, D = qv.shape
+        if kind == "layout":                       # q read as [B][Hq][T][D]
+            qv = qv.reshape(B, Hq, T, D).transpose(0, 2, 1, 3)
+        Hkv = k_cache.shape[1]
+        G = Hq // Hkv
+        out = np.zeros((B, T, Hq, D))
+        for b in range(B):
+            L = int(context_lens[b])
+            blocks = np.asarray(block_table[b, : -(-L // 16)], dtype=np.int64)
+            for g in range(Hkv):
+                kr, vr = gather_kv(k_cache, v_cache, blocks, g, L, kv)
+                for t in range(T):
+                    n = {"offset": L - T + t, "nocausal": L}.get(kind, L - T + t + 1)
+                    tq = T - 1 - t if kind == "reverse" else t
+                    n = max(n, 0)
+                    o, _ = attend(qv[b, tq, g * G:(g + 1) * G], kr[:n], vr[:n],
+                                  float(np.float32(scale)))
+                    out[b, t, g * G:(g + 1) * G] = o
+        return out
+    return fn
+
+
+@pytest.mark.parametrize("kind", ["offset", "nocausal", "reverse", "layout"])
+def test_pins_catch_planted_mistakes(kind):
+    spec = tiny_spec("f32", "f32", B=3, hq=4, hkv=2, D=16, lens=("fixed", [6, 16, 37]), seed=2)
+    wl = W.make_workload(spec)
+    T = 5
+    q = W.multi_query(wl, T)
+    args = (q, wl.k_cache, wl.v_cache, wl.block_table, wl.context_lens, wl.scale, "f32", "f32")
+    good = mq(wl, q)
+    brute = np.stack([brute_decode(np.ascontiguousarray(q[:, t]), wl.k_cache, wl.v_cache,
+                                   wl.block_table,
+                                   np.maximum(wl.context_lens.astype(np.int64) - T + t + 1, 0),
+                                   wl.scale, "f32", "f32")[0] for t in range(T)], axis=1)
+    np.testing.assert_allclose(good, brute, rtol=0, atol=1e-12)
+    bad = _mutated_multi(kind)(*args)
+    assert not np.allclose(bad, brute, rtol=0, atol=1e-6), kind
