@@ -575,6 +575,10 @@ def main():
         modes = [pkd.SPLIT_BALANCED, spec.partition_size]
     else:
         modes = [spec.partition_size, pkd.SPLIT_BALANCED]
+        if spec.partition_size == 0:
+            # one pass leaves a long sequence to one workgroup, which streams
+            # at a per-CU rate; 512-token partitions are timed beside it
+            modes.append(512)
     ps = modes[0]   # --pmc-pass profiles this one
 
     if args.pmc_pass:
