@@ -37,14 +37,24 @@ __host__ __device__ inline int share_count(int n, int shares) {
   return s > 1 ? s : 1;
 }
 
+// floor(a / b) for 0 <= a < 2^53, 0 < b < 2^31 and a quotient below 2^31,
+// through one correctly rounded double division instead of a 64-bit integer
+// division (which the GPU has no instruction for: it expands into a long
+// scalar routine). Exact: a / b = q + f/b with the integer q and 0 <= f < b,
+// so rounding can only lift it to q + 1 if 1/b <= ulp(a / b) / 2 <=
+// (a / b) * 2^-53, i.e. if a >= 2^53; every caller stays far below (a < 2^46).
+__host__ __device__ inline int floor_div(long long a, long long b) {
+  return (int)((double)a / (double)b);
+}
+
 // First line position of share w of s over n positions.
 __host__ __device__ inline int share_start(int w, int n, int s) {
-  return (int)((long long)w * n / s);
+  return floor_div((long long)w * n, s);
 }
 
 // The share holding line position x: the largest w with share_start(w) <= x.
 __host__ __device__ inline int share_of(int x, int n, int s) {
-  return (int)(((long long)(x + 1) * s - 1) / n);
+  return floor_div((long long)(x + 1) * s - 1, n);
 }
 
 struct LinePiece {
@@ -64,7 +74,7 @@ __host__ __device__ inline LinePiece line_piece(int x, int x1, int seq_first, in
                                                 int n, int s, int wg) {
   LinePiece p;
   const int rel = x - seq_first;
-  p.g = rel / cb;
+  p.g = floor_div(rel, cb);
   p.pg_lo = rel - p.g * cb;
   const int pair_first = seq_first + p.g * cb;
   const int pair_end = pair_first + cb;
