@@ -175,3 +175,9 @@ extern "C" int pa_probe_schedule(const int* lens, int B, int H, int max_blocks, 
   }
   return n;
 }
+
+// Host evaluation of the work line's exact division helper (pa_schedule.h),
+// element by element: out[i] = floor_div(a[i], b[i]).
+extern "C" void pa_probe_floor_div(const long long* a, const long long* b, int n, int* out) {
+  for (int i = 0; i < n; ++i) out[i] = pa::floor_div(a[i], b[i]);
+}

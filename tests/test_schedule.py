@@ -113,3 +113,34 @@ def test_headline_shape(lib):
     lens = rng.integers(512, 4097, size=32)
     rows = check(lib, lens, 4, 256, 768)
     assert rows[:, 0].max() == 767       # every workgroup gets a share
+
+
+def test_floor_div_is_exact_integer_division(lib):
+    """The work line divides through doubles (pa_schedule.h floor_div); it must
+    equal integer division on the whole range the schedule uses: quotients
+    just below an integer (a = k*b - 1), the largest products of a share
+    index and a line length, and divisors up to 2^31 - 1."""
+    lib.pa_probe_floor_div.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
+                                       ctypes.c_void_p]
+    lib.pa_probe_floor_div.restype = None
+    rng = np.random.default_rng(5)
+    a, b = [], []
+    for _ in range(20000):
+        bb = int(rng.integers(1, 2**31))
+        k = int(rng.integers(0, min(2**31 - 1, (2**46) // bb) + 1))
+        for aa in (k * bb - 1, k * bb, k * bb + 1, k * bb + bb - 1):
+            if 0 <= aa < 2**46 and aa // bb < 2**31:
+                a.append(aa)
+                b.append(bb)
+    # share starts and share lookups at the largest sizes the kernel accepts
+    for s in (1, 255, 256, 257, 768, 12288):
+        for n in (1, 8, 2**31 - 1, 2**31 - 12289, 123456789):
+            for w in (0, 1, s // 2, s - 1, s):
+                a.append(w * n); b.append(s)
+            for x in (0, 1, n // 2, n - 1):
+                a.append((x + 1) * s - 1); b.append(n)
+    a = np.array(a, dtype=np.int64)
+    b = np.array(b, dtype=np.int64)
+    out = np.empty(len(a), dtype=np.int32)
+    lib.pa_probe_floor_div(a.ctypes.data, b.ctypes.data, len(a), out.ctypes.data)
+    np.testing.assert_array_equal(out.astype(np.int64), a // b)
