@@ -102,3 +102,41 @@ def test_pool_tables_serving_steps(io, kv, ps):
                              partition_size=ps)
             torch.cuda.synchronize()
             check(wl, to_f64(out), ref(wl), label=f"step {step} {io}/{kv} ps{ps}")
+
+
+@pytest.mark.parametrize("io,kv,ps", [("bf16", "bf16", 512), ("f16", "fp8_e4m3", 0)])
+def test_pool_tables_speculative_verify_steps(io, kv, ps):
+    """A verify loop on pool-built tables: each step the pool takes four
+    drafted tokens per request, pa_kv_append writes their K/V (one call per
+    token), and pa_decode_multi attends with the four new tokens causal
+    among themselves; the oracle does the same steps."""
+    T = 4
+    wl, pool = pool_workload(io, kv, ps, seed=33)
+    t = W.to_device(wl)
+    rng = np.random.default_rng(8)
+    B, Hkv = wl.spec.batch, wl.spec.num_kv_heads
+    ks = wl.k_scale if kv == "fp8_e4m3" else None
+    vs = wl.v_scale if kv == "fp8_e4m3" else None
+    print(f"case verify {io}/{kv} ps{ps}", flush=True)
+    for step in range(3):
+        for i in range(T):
+            for s in range(B):
+                pool.append_token(s, int(rng.integers(0, 32000)))
+            table, lens = pool.block_table(list(range(B)), MBS, pad=0)
+            pos = (lens - 1).astype(np.int32)
+            k_new, v_new = new_rows(rng, B, Hkv, wl.spec.head_dim, io)
+            bt = torch.from_numpy(table).cuda()
+            pkd.kv_append(storage_tensor(k_new, io).cuda(), storage_tensor(v_new, io).cuda(),
+                          torch.from_numpy(pos).cuda(), bt, t["k_cache"], t["v_cache"],
+                          k_scale=t["k_scale"], v_scale=t["v_scale"])
+            wl.k_cache, wl.v_cache = oracle.kv_append_ref(wl.k_cache, wl.v_cache, k_new, v_new,
+                                                          table, pos, io, kv, ks, vs)
+        wl.block_table, wl.context_lens = table, lens
+        q = W.multi_query(wl, T, seed=100 + step)
+        out = pkd.decode(storage_tensor(q, io).cuda(), t["k_cache"], t["v_cache"], bt,
+                         torch.from_numpy(lens).cuda(), float(wl.scale), k_scale=t["k_scale"],
+                         v_scale=t["v_scale"], partition_size=ps)
+        torch.cuda.synchronize()
+        exp = oracle.multi_query_ref(q, wl.k_cache, wl.v_cache, table, lens, wl.scale, io, kv,
+                                     ks, vs)
+        check(wl, to_f64(out), exp, label=f"verify step {step} {io}/{kv} ps{ps}")
