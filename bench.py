@@ -351,6 +351,8 @@ def bench_multi(args, torch, np, pkd, W):
 
     modes = [args.partition_size] if args.partition_size is not None else \
         [spec.partition_size, 0]
+    if args.partition_size is None and spec.num_q_heads // spec.num_kv_heads * T <= 16:
+        modes.append(pkd.SPLIT_BALANCED)   # rows of one tile: the decode kernels run the call
     if args.pmc_pass:
         calls = make_calls(modes[0])
         src = torch.ones(1 << 28, dtype=torch.int32, device=dev)      # 1 GiB

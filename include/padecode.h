@@ -157,12 +157,13 @@ pa_status pa_decode(const pa_shape* shape, const void* q, const void* k_cache,
  *   q, out      [batch][q_len][num_q_heads][head_dim] in io_dtype
  *   lse_out     float32 [batch][q_len][num_q_heads] (natural log) or NULL
  *   q_len       1 .. 16
- *   shape       as for pa_decode; partition_size 0 or a positive multiple of
- *               16 (PA_SPLIT_BALANCED is not supported here)
+ *   shape       as for pa_decode; partition_size 0, a positive multiple of
+ *               16, or PA_SPLIT_BALANCED when G * q_len <= 16
+ *               (G = num_q_heads / num_kv_heads)
  *   workspace   pa_decode_multi_workspace_bytes(shape, q_len) bytes when
- *               partition_size > 0; same counter-first contract as
- *               pa_decode, with ceil(ceil(G*q_len/16)/2) counters per
- *               (sequence, KV head), G = num_q_heads / num_kv_heads
+ *               partition_size != 0; same counter-first contract as
+ *               pa_decode, with one counter per (sequence, KV head) when
+ *               G * q_len <= 16, else ceil(ceil(G*q_len/16)/2)
  * Everything else (dtypes, scales, alignment, errors) as for pa_decode. */
 size_t pa_decode_multi_workspace_bytes(const pa_shape* shape, int32_t q_len);
 pa_status pa_decode_multi(const pa_shape* shape, int32_t q_len, const void* q,

@@ -44,6 +44,7 @@
 #include <type_traits>
 
 #include "padecode.h"
+#include "pa_internal.h"
 #include "pa_schedule.h"
 #include "pa_tiles.h"
 
@@ -71,7 +72,18 @@ struct Params {
   int32_t num_blocks;
   int32_t part_tokens;  // 0: whole sequence in one unit
   int32_t p_max;        // fixed partitions: slots per (b, g)
+  int32_t q_len;        // new tokens per sequence (1: decode)
+  int32_t gq;           // query heads per KV head (group = gq * q_len rows)
 };
+
+// Several new tokens per sequence (MQ, the multi-token call when its rows fit
+// one tile): row r of pair (b, g) is new token t = r / gq of head h = r % gq,
+// stored at [b][t][g * gq + h]; token t sees positions 0 .. L - q_len + t.
+template <bool MQ>
+__device__ __forceinline__ size_t mq_row(const Params& a, int b, int g, int r) {
+  const int t = r / a.gq, h = r - t * a.gq;
+  return ((size_t)b * a.q_len + t) * a.num_q_heads + (size_t)g * a.gq + h;
+}
 
 // ---------------------------------------------------------------------------
 // LDS for the cross-wave merge and the cross-partition merge.
@@ -98,22 +110,28 @@ struct Smem {
 // so the result does not depend on which workgroup finished last.
 // red: LDS scratch of at least kMergeScratch floats.
 constexpr int kMergeScratch = 6 * kThreads;
-template <typename IO, int D>
+// MQ: a piece may hold nothing a row can see (lse = -inf, skipped; a row
+// with nothing in any piece gets 0 and -inf) and NaN is tracked explicitly;
+// pieces are not sliced.
+template <typename IO, int D, bool MQ>
 __device__ __forceinline__ void merge_partitions(const Params& a, float* red, int b, int g, int slot0, int nparts) {
   constexpr int kQuads = D / 4;
   constexpr int kBatch = 8;
   const int tid = threadIdx.x;
   const int npair = a.group * kQuads;
-  const int S = npair >= kThreads ? 1 : kThreads / npair;
+  const int S = (MQ || npair >= kThreads) ? 1 : kThreads / npair;
   const size_t slot_floats = (size_t)a.group * D;
   for (int base = 0; base < npair * S; base += kThreads) {
     const int idx = base + tid;
     const bool active = idx < npair * S;
     const int pair = idx % npair, sl = idx / npair;
     const int h = pair / kQuads, dq = pair % kQuads;
-    const size_t row = (size_t)b * a.num_q_heads + g * a.group + h;
+    size_t row;
+    if constexpr (MQ) row = mq_row<MQ>(a, b, g, h);
+    else row = (size_t)b * a.num_q_heads + g * a.group + h;
     const float* lse = a.ws_lse + (size_t)slot0 * a.group + h;
     float mr = -INFINITY, wr = 0.f;
+    bool nan = false;
     f32x4 ar = {0.f, 0.f, 0.f, 0.f};
     // batches of kBatch * S slots, each read through a resource based at the
     // batch's first slot (offsets stay small whatever nparts is)
@@ -134,6 +152,10 @@ __device__ __forceinline__ void merge_partitions(const Params& a, float* red, in
 #pragma unroll
       for (int u = 0; u < kBatch; ++u) {
         if (active && sl + u * S < nb) {
+          if constexpr (MQ) {
+            if (lp[u] != lp[u]) nan = true;
+            if (!(lp[u] > -INFINITY)) continue;
+          }
           const float mn = fmaxf(mr, lp[u]);
           const float sa = exp2_fast(mr - mn), sb = exp2_fast(lp[u] - mn);
           ar = ar * sa + ov[u] * sb;
@@ -170,8 +192,22 @@ __device__ __forceinline__ void merge_partitions(const Params& a, float* red, in
       }
     }
     if (active && sl == 0) {
-      store_out4<IO>(a.out, row * D + 4 * dq, f32x4{ar[0] / wr, ar[1] / wr, ar[2] / wr, ar[3] / wr});
-      if (dq == 0 && a.lse_out) a.lse_out[row] = (mr + log2_fast(wr)) * kLn2;
+      if constexpr (MQ) {
+        f32x4 val = {0.f, 0.f, 0.f, 0.f};
+        float lse2 = -INFINITY;
+        if (nan) {
+          val = f32x4{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
+          lse2 = __builtin_nanf("");
+        } else if (wr > 0.f) {
+          val = f32x4{ar[0] / wr, ar[1] / wr, ar[2] / wr, ar[3] / wr};
+          lse2 = (mr + log2_fast(wr)) * kLn2;
+        }
+        store_out4<IO>(a.out, row * D + 4 * dq, val);
+        if (dq == 0 && a.lse_out) a.lse_out[row] = lse2;
+      } else {
+        store_out4<IO>(a.out, row * D + 4 * dq, f32x4{ar[0] / wr, ar[1] / wr, ar[2] / wr, ar[3] / wr});
+        if (dq == 0 && a.lse_out) a.lse_out[row] = (mr + log2_fast(wr)) * kLn2;
+      }
     }
   }
 }
@@ -192,7 +228,7 @@ struct Piece {
 // whole workgroup. resolve() returns the Piece; it is called after the loads
 // that do not depend on it are issued. Control flow is uniform across the
 // workgroup.
-template <typename IO, typename KV, int D, typename Resolve>
+template <typename IO, typename KV, int D, bool MQ, typename Resolve>
 __device__ __forceinline__ void decode_piece(const Params& a, Smem<D>& sm, const int b, const int g,
                                              const int page0, Resolve resolve) {
   using T = typename TileOf<IO, KV, D>::type;
@@ -222,8 +258,11 @@ __device__ __forceinline__ void decode_piece(const Params& a, Smem<D>& sm, const
   };
   int bt_cur = fetch_bt(0);
   typename T::Q qop;
-  T::load_q(qop, (gptr)(a.q + ((size_t)b * a.num_q_heads + hq0 + (head_ok ? rr : 0)) * D * ElemSize<IO>::v),
-            jj);
+  if constexpr (MQ)
+    T::load_q(qop, (gptr)(a.q + mq_row<MQ>(a, b, g, head_ok ? rr : 0) * D * ElemSize<IO>::v), jj);
+  else
+    T::load_q(qop, (gptr)(a.q + ((size_t)b * a.num_q_heads + hq0 + (head_ok ? rr : 0)) * D * ElemSize<IO>::v),
+              jj);
 
   const Piece pc = resolve();
   if (pc.nparts == 0) return;
@@ -232,12 +271,21 @@ __device__ __forceinline__ void decode_piece(const Params& a, Smem<D>& sm, const
   if (bad_len || L == 0) {
     // No tokens (or an out-of-contract length): zeros, resp. NaN.
     const float fill = bad_len ? __builtin_nanf("") : 0.f;
-    for (int i = tid; i < G * D; i += kThreads)
-      store_out<IO>(a.out, ((size_t)b * a.num_q_heads + hq0) * D + i, fill);
-    if (a.lse_out && tid < G)
-      a.lse_out[(size_t)b * a.num_q_heads + hq0 + tid] = bad_len ? fill : -INFINITY;
+    if constexpr (MQ) {
+      for (int i = tid; i < G * D; i += kThreads)
+        store_out<IO>(a.out, mq_row<MQ>(a, b, g, i / D) * D + i % D, fill);
+      if (a.lse_out && tid < G) a.lse_out[mq_row<MQ>(a, b, g, tid)] = bad_len ? fill : -INFINITY;
+    } else {
+      for (int i = tid; i < G * D; i += kThreads)
+        store_out<IO>(a.out, ((size_t)b * a.num_q_heads + hq0) * D + i, fill);
+      if (a.lse_out && tid < G)
+        a.lse_out[(size_t)b * a.num_q_heads + hq0 + tid] = bad_len ? fill : -INFINITY;
+    }
     return;
   }
+  // MQ: last position this lane's row may see
+  int lim = 0;
+  if constexpr (MQ) lim = L - a.q_len + (head_ok ? rr : 0) / a.gq;
 
   const int t0 = page0 * kBlock;
   const int t1 = min(pc.pg_hi * kBlock, L);
@@ -304,19 +352,30 @@ __device__ __forceinline__ void decode_piece(const Params& a, Smem<D>& sm, const
     int nvalid = kBlock;
     float sc[4];
     if constexpr (kMasked) {
-      nvalid = t1 - (t0 + (w + kWaves * i) * kBlock);
+      const int pos = t0 + (w + kWaves * i) * kBlock;
+      nvalid = t1 - pos;
+      if constexpr (MQ) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) sc[e] = (4 * jj + e < nvalid) ? s[e] * kmul : -INFINITY;
+        for (int e = 0; e < 4; ++e)
+          sc[e] = (4 * jj + e < nvalid && pos + 4 * jj + e <= lim) ? s[e] * kmul : -INFINITY;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sc[e] = (4 * jj + e < nvalid) ? s[e] * kmul : -INFINITY;
+      }
     } else {
 #pragma unroll
       for (int e = 0; e < 4; ++e) sc[e] = s[e] * kmul;
     }
     const float mx = wave_max_rows(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])));
     const float mnew = fmaxf(m, mx);
-    const float alpha = exp2_fast(m - mnew);
+    // MQ: a row that sees nothing yet keeps a zero state (exponentials
+    // against 0 instead of -inf - -inf)
+    float msafe = mnew;
+    if constexpr (MQ && kMasked) msafe = mnew == -INFINITY ? 0.f : mnew;
+    const float alpha = exp2_fast(m - msafe);
     float pr[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) pr[e] = exp2_fast(sc[e] - mnew);
+    for (int e = 0; e < 4; ++e) pr[e] = exp2_fast(sc[e] - msafe);
     const typename T::P pk = T::pack(pr);
     lsum = lsum * alpha + T::psum(pk);
     m = mnew;
@@ -400,19 +459,28 @@ __device__ __forceinline__ void decode_piece(const Params& a, Smem<D>& sm, const
     for (int ww = 0; ww < kWaves; ++ww) M = fmaxf(M, sm.m[ww][h]);
     float W = 0.f;
     f32x4 o = {0.f, 0.f, 0.f, 0.f};
+    const float Ms = (MQ && M == -INFINITY) ? 0.f : M;   // MQ: a row may see nothing here
 #pragma unroll
     for (int ww = 0; ww < kWaves; ++ww) {
-      const float e = exp2_fast(sm.m[ww][h] - M);
+      const float e = exp2_fast(sm.m[ww][h] - Ms);
       W += e * sm.l[ww][h];
       o += e * *reinterpret_cast<const f32x4*>(&sm.acc[ww][h][d]);
     }
     f32x4 val = {o[0] / W * vmul, o[1] / W * vmul, o[2] / W * vmul, o[3] / W * vmul};
     float lse2 = M + log2_fast(W);
+    if constexpr (MQ) {
+      if (!(W > 0.f)) {
+        val = f32x4{0.f, 0.f, 0.f, 0.f};
+        lse2 = -INFINITY;
+      }
+    }
     if (bad) {
       val = f32x4{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
       lse2 = __builtin_nanf("");
     }
-    const size_t row = (size_t)b * a.num_q_heads + hq0 + h;
+    size_t row;
+    if constexpr (MQ) row = mq_row<MQ>(a, b, g, h);
+    else row = (size_t)b * a.num_q_heads + hq0 + h;
     if (!split) {
       store_out4<IO>(a.out, row * D + d, val);
       if (d == 0 && a.lse_out) a.lse_out[row] = lse2 * kLn2;
@@ -436,13 +504,13 @@ __device__ __forceinline__ void decode_piece(const Params& a, Smem<D>& sm, const
   __syncthreads();
   if (!__builtin_amdgcn_readfirstlane(sm.last)) return;   // uniform: a scalar branch
   static_assert(sizeof(sm.acc) >= kMergeScratch * sizeof(float), "merge scratch");
-  merge_partitions<IO, D>(a, &sm.acc[0][0][0], b, g, pc.slot0, pc.nparts);
+  merge_partitions<IO, D, MQ>(a, &sm.acc[0][0][0], b, g, pc.slot0, pc.nparts);
   if (tid == 0) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Fixed schedule: one workgroup per (sequence b, KV head g, partition p) unit
 // (partition = the whole sequence when part_tokens == 0).
-template <typename IO, typename KV, int D>
+template <typename IO, typename KV, int D, bool MQ>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3)))
 pa_decode_kernel(const Params a) {
   __shared__ Smem<D> sm;
@@ -458,7 +526,7 @@ pa_decode_kernel(const Params a) {
   const int g = bg - b * H;
   const int PT = a.part_tokens;
   const int page0 = PT > 0 ? p * (PT / kBlock) : 0;
-  decode_piece<IO, KV, D>(a, sm, b, g, page0, [&]() {
+  decode_piece<IO, KV, D, MQ>(a, sm, b, g, page0, [&]() {
     Piece pc;
     pc.L = a.context_lens[b];
     const bool bad_len = pc.L < 0 || pc.L > a.max_blocks_per_seq * kBlock;
@@ -507,6 +575,8 @@ constexpr int kMetaValid = 31;     // tokens of the page; 0: placeholder positio
 constexpr int kMetaEnd = 32;       // last position of its piece in the quarter
 constexpr int kMetaBad = 64;       // block id outside the pool
 constexpr int kMetaHeadShift = 8;  // KV head in bits 8..23
+constexpr int kMetaNear = 128;     // MQ: one of the sequence's last two pages
+constexpr int kMetaPfeShift = 24;  // MQ: bit 24 set for the second-to-last page
 
 // Dynamic LDS of the balanced kernel, sized by group G, head_dim D, batch B.
 // Pieces of one share that go through the LDS merge, at most: the share's
@@ -607,7 +677,7 @@ __device__ __forceinline__ void qcursor_at(QCursor& c, const Params& a, const Ba
 }
 
 // One wave's quarter [y0, y1) of a share.
-template <typename IO, typename KV, int D>
+template <typename IO, typename KV, int D, bool MQ>
 __device__ __forceinline__ void decode_quarter(const Params& a, const BalSm<D>& sm, const int y0,
                                                const int y1) {
   using T = typename TileOf<IO, KV, D>::type;
@@ -639,6 +709,10 @@ __device__ __forceinline__ void decode_quarter(const Params& a, const BalSm<D>& 
       if (valid) blk = a.block_table[(size_t)bl * mbs + page];
       meta = (valid ? min(kBlock, L - page * kBlock) : 0) | (xp + 1 == min(y1, pair_end) ? kMetaEnd : 0) |
              (g << kMetaHeadShift);
+      if constexpr (MQ) {
+        const int pfe = cb - 1 - page;   // pages from the end of the sequence
+        if (valid && pfe <= 1) meta |= kMetaNear | (pfe << kMetaPfeShift);
+      }
     }
   };
   int bt_cur, meta_cur, bt_nxt = 0, meta_nxt = 0;
@@ -651,8 +725,14 @@ __device__ __forceinline__ void decode_quarter(const Params& a, const BalSm<D>& 
   bool has_nxt = cur.pair_end < y1;
   if (has_nxt) qcursor_at(nxt, a, sm, cur.pair_end, y1);
   auto q_row = [&](const QCursor& c) {
-    return (gptr)(a.q + ((size_t)c.b * a.num_q_heads + c.g * G + (head_ok ? rr : 0)) * D * ElemSize<IO>::v);
+    if constexpr (MQ) return (gptr)(a.q + mq_row<MQ>(a, c.b, c.g, head_ok ? rr : 0) * D * ElemSize<IO>::v);
+    else return (gptr)(a.q + ((size_t)c.b * a.num_q_heads + c.g * G + (head_ok ? rr : 0)) * D * ElemSize<IO>::v);
   };
+  // MQ: new token of this lane's row, and the last position it may see in the
+  // current piece's sequence
+  const int t_rr = MQ ? (head_ok ? rr : 0) / a.gq : 0;
+  int lim_cur = 0;
+  if constexpr (MQ) lim_cur = cur.L - a.q_len + t_rr;
   typename T::Q q_cur, q_nxt;
   T::load_q(q_cur, q_row(cur), jj);
   if (has_nxt) T::load_q(q_nxt, q_row(nxt), jj);
@@ -712,18 +792,27 @@ __device__ __forceinline__ void decode_quarter(const Params& a, const BalSm<D>& 
   for (int t = 0; t < D / 16; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // One page of the online softmax (as in the fixed schedule).
-  auto page_math = [&](int kslot, int vslot, int nvalid, auto masked_tag) {
+  // pos: first position of the page in its sequence (MQ, masked pages only)
+  auto page_math = [&](int kslot, int vslot, int nvalid, int pos, auto masked_tag) {
     constexpr bool kMasked = decltype(masked_tag)::value;
     const f32x4 s = T::scores(ring_k[kslot], q_cur);
     float sc[4];
+    if constexpr (MQ && kMasked) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) sc[e] = (!kMasked || 4 * jj + e < nvalid) ? s[e] * kmul_cur : -INFINITY;
+      for (int e = 0; e < 4; ++e)
+        sc[e] = (4 * jj + e < nvalid && pos + 4 * jj + e <= lim_cur) ? s[e] * kmul_cur : -INFINITY;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sc[e] = (!kMasked || 4 * jj + e < nvalid) ? s[e] * kmul_cur : -INFINITY;
+    }
     const float mx = wave_max_rows(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])));
     const float mnew = fmaxf(m, mx);
-    const float alpha = exp2_fast(m - mnew);
+    float msafe = mnew;
+    if constexpr (MQ && kMasked) msafe = mnew == -INFINITY ? 0.f : mnew;
+    const float alpha = exp2_fast(m - msafe);
     float pr[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) pr[e] = exp2_fast(sc[e] - mnew);
+    for (int e = 0; e < 4; ++e) pr[e] = exp2_fast(sc[e] - msafe);
     const typename T::P pk = T::pack(pr);
     lsum = lsum * alpha + T::psum(pk);
     m = mnew;
@@ -748,15 +837,33 @@ __device__ __forceinline__ void decode_quarter(const Params& a, const BalSm<D>& 
       const bool bad_len = cur.L < 0 || cur.L > mbs * kBlock;
       if (bad_len || cur.L == 0) {
         const float fill = bad_len ? __builtin_nanf("") : 0.f;
-        for (int i = lane; i < G * D; i += 64) store_out<IO>(a.out, row0 * D + i, fill);
-        if (a.lse_out && lane < G) a.lse_out[row0 + lane] = bad_len ? fill : -INFINITY;
+        if constexpr (MQ) {
+          for (int i = lane; i < G * D; i += 64)
+            store_out<IO>(a.out, mq_row<MQ>(a, cur.b, cur.g, i / D) * D + i % D, fill);
+          if (a.lse_out && lane < G) a.lse_out[mq_row<MQ>(a, cur.b, cur.g, lane)] = bad_len ? fill : -INFINITY;
+        } else {
+          for (int i = lane; i < G * D; i += 64) store_out<IO>(a.out, row0 * D + i, fill);
+          if (a.lse_out && lane < G) a.lse_out[row0 + lane] = bad_len ? fill : -INFINITY;
+        }
       } else if (head_ok) {
-        const float inv = bad ? __builtin_nanf("") : vmul_cur / l;
+        if constexpr (MQ) {
+          // a row that saw nothing (sequence shorter than q_len) gets 0, -inf
+          const bool none = !(l > 0.f);
+          const float inv = bad ? __builtin_nanf("") : (none ? 0.f : vmul_cur / l);
+          const size_t row = mq_row<MQ>(a, cur.b, cur.g, rr);
 #pragma unroll
-        for (int t = 0; t < D / 16; ++t)
-          store_out4<IO>(a.out, (row0 + rr) * D + 16 * t + 4 * jj, acc[t] * inv);
-        if (jj == 0 && a.lse_out)
-          a.lse_out[row0 + rr] = bad ? __builtin_nanf("") : (m + log2_fast(l)) * kLn2;
+          for (int t = 0; t < D / 16; ++t)
+            store_out4<IO>(a.out, row * D + 16 * t + 4 * jj, acc[t] * inv);
+          if (jj == 0 && a.lse_out)
+            a.lse_out[row] = bad ? __builtin_nanf("") : (none ? -INFINITY : (m + log2_fast(l)) * kLn2);
+        } else {
+          const float inv = bad ? __builtin_nanf("") : vmul_cur / l;
+#pragma unroll
+          for (int t = 0; t < D / 16; ++t)
+            store_out4<IO>(a.out, (row0 + rr) * D + 16 * t + 4 * jj, acc[t] * inv);
+          if (jj == 0 && a.lse_out)
+            a.lse_out[row0 + rr] = bad ? __builtin_nanf("") : (m + log2_fast(l)) * kLn2;
+        }
       }
     } else {
       const int slot = cur.pair_first <= y0 ? 0 : 1;
@@ -781,6 +888,7 @@ __device__ __forceinline__ void decode_quarter(const Params& a, const BalSm<D>& 
       q_cur = q_nxt;
       kmul_cur = kmul_nxt;
       vmul_cur = vmul_nxt;
+      if constexpr (MQ) lim_cur = cur.L - a.q_len + t_rr;
       has_nxt = cur.pair_end < y1;
       if (has_nxt) {
         qcursor_at(nxt, a, sm, cur.pair_end, y1);
@@ -798,10 +906,17 @@ __device__ __forceinline__ void decode_quarter(const Params& a, const BalSm<D>& 
     const int nvalid = mk & kMetaValid;
     if (nvalid != 0) {
       if (mk & kMetaBad) bad = true;
-      if (nvalid == kBlock)
-        page_math(kslot, vslot, nvalid, std::integral_constant<bool, false>{});
+      bool masked = nvalid != kBlock;
+      int pos = 0;
+      if constexpr (MQ) {
+        // the last two pages of a sequence can hold positions a row may not see
+        masked = masked || (mk & kMetaNear) != 0;
+        pos = (line_pages(cur.L, mbs) - 1 - ((mk >> kMetaPfeShift) & 1)) * kBlock;
+      }
+      if (!masked)
+        page_math(kslot, vslot, nvalid, pos, std::integral_constant<bool, false>{});
       else
-        page_math(kslot, vslot, nvalid, std::integral_constant<bool, true>{});
+        page_math(kslot, vslot, nvalid, pos, std::integral_constant<bool, true>{});
     }
     if (mk & kMetaEnd) flush();
   };
@@ -853,7 +968,7 @@ __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(
 // (pair (b, g) starting at line position pair_first) and write the output
 // (nparts == 1) or the piece's partial result (slot slot0 + k). yq(ww): the
 // quarter starts.
-template <typename IO, typename KV, int D, typename YQ>
+template <typename IO, typename KV, int D, bool MQ, typename YQ>
 __device__ __forceinline__ void combine_slots(const Params& a, const BalSm<D>& sm, int b, int g, int pair_first,
                               int wa, int wb, int k, int nparts, int slot0, YQ yq) {
   const int tid = threadIdx.x;
@@ -890,21 +1005,30 @@ __device__ __forceinline__ void combine_slots(const Params& a, const BalSm<D>& s
       if (on[ww]) M = fmaxf(M, mv[ww]);
     float W = 0.f;
     f32x4 o = {0.f, 0.f, 0.f, 0.f};
+    const float Ms = (MQ && M == -INFINITY) ? 0.f : M;   // MQ: a row may see nothing here
 #pragma unroll
     for (int ww = 0; ww < kWaves; ++ww) {
       if (on[ww]) {
-        const float e = exp2_fast(mv[ww] - M);
+        const float e = exp2_fast(mv[ww] - Ms);
         W += e * lv[ww];
         o += e * av[ww];
       }
     }
     f32x4 val = {o[0] / W * vmul, o[1] / W * vmul, o[2] / W * vmul, o[3] / W * vmul};
     float lse2 = M + log2_fast(W);
+    if constexpr (MQ) {
+      if (!(W > 0.f)) {
+        val = f32x4{0.f, 0.f, 0.f, 0.f};
+        lse2 = -INFINITY;
+      }
+    }
     if (bad) {
       val = f32x4{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
       lse2 = __builtin_nanf("");
     }
-    const size_t row = (size_t)b * a.num_q_heads + hq0 + h;
+    size_t row;
+    if constexpr (MQ) row = mq_row<MQ>(a, b, g, h);
+    else row = (size_t)b * a.num_q_heads + hq0 + h;
     if (!split) {
       store_out4<IO>(a.out, row * D + d, val);
       if (d == 0 && a.lse_out) a.lse_out[row] = lse2 * kLn2;
@@ -915,7 +1039,7 @@ __device__ __forceinline__ void combine_slots(const Params& a, const BalSm<D>& s
   }
 }
 
-template <typename IO, typename KV, int D>
+template <typename IO, typename KV, int D, bool MQ>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 pa_decode_balanced_kernel(const Params a) {
   const int tid = threadIdx.x;
@@ -971,7 +1095,7 @@ pa_decode_balanced_kernel(const Params a) {
   // this wave's quarter of the share
   const int wu = __builtin_amdgcn_readfirstlane(w);
   auto yq = [&](int ww) { return x0 + share_start(ww, x1 - x0, kWaves); };
-  decode_quarter<IO, KV, D>(a, sm, yq(wu), yq(wu + 1));
+  decode_quarter<IO, KV, D, MQ>(a, sm, yq(wu), yq(wu + 1));
   __syncthreads();
 
   // Pieces of the share whose state went through LDS, in three steps:
@@ -994,7 +1118,7 @@ pa_decode_balanced_kernel(const Params a) {
         const int wa = share_of(s0 - x0, x1 - x0, kWaves);
         const int wb = share_of(lp.x_end - 1 - x0, x1 - x0, kWaves);
         if (wa == wb && pair_first >= yq(wa) && pair_end <= yq(wa + 1)) return;   // written by wave wa
-        combine_slots<IO, KV, D>(a, sm, bb, lp.g, pair_first, wa, wb, lp.k, lp.nparts, lp.slot0, yq);
+        combine_slots<IO, KV, D, MQ>(a, sm, bb, lp.g, pair_first, wa, wb, lp.k, lp.nparts, lp.slot0, yq);
         if (lp.nparts > 1) {
           if (tid == 0) {
             int* e = sm.split + 4 * nsplit;
@@ -1022,7 +1146,7 @@ pa_decode_balanced_kernel(const Params a) {
     const int g = __builtin_amdgcn_readfirstlane(sm.split[4 * i + 1]);
     const int np = __builtin_amdgcn_readfirstlane(sm.split[4 * i + 2]);
     const int slot0 = __builtin_amdgcn_readfirstlane(sm.split[4 * i + 3]);
-    merge_partitions<IO, D>(a, sm.red, bb, g, slot0, np);
+    merge_partitions<IO, D, MQ>(a, sm.red, bb, g, slot0, np);
     if (tid == 0)
       __hip_atomic_store(a.ws_cnt + (size_t)bb * H + g, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     lds_barrier();   // the merge scratch is reused by the next pair
@@ -1088,8 +1212,9 @@ static bool shape_ok(const pa_shape* s) {
   return true;
 }
 
-// shares: the balanced split's workgroup count (ignored otherwise)
-static WsLayout ws_layout(const pa_shape* s, int shares) {
+// shares: the balanced split's workgroup count (ignored otherwise); q_len:
+// new tokens per sequence (rows per pair = group * q_len)
+static WsLayout ws_layout(const pa_shape* s, int shares, int q_len) {
   WsLayout w{0, 0, 0, 0, 1};
   if (s->partition_size == 0) return w;
   size_t slots;
@@ -1101,7 +1226,7 @@ static WsLayout ws_layout(const pa_shape* s, int shares) {
     w.p_max = (int)((tokens + s->partition_size - 1) / s->partition_size);
     slots = (size_t)s->batch * s->num_kv_heads * w.p_max;
   }
-  const size_t rows = slots * (s->num_q_heads / s->num_kv_heads);
+  const size_t rows = slots * (size_t)(s->num_q_heads / s->num_kv_heads) * q_len;
   // counters first: their bytes stay where they are for every shape, so a
   // smaller call after a larger one finds them zero
   w.cnt_off = 0;
@@ -1111,47 +1236,50 @@ static WsLayout ws_layout(const pa_shape* s, int shares) {
   return w;
 }
 
-template <typename IO, typename KV, int D>
+template <typename IO, typename KV, int D, bool MQ>
 static hipError_t launch(const Params& prm, dim3 grid, bool balanced, hipStream_t stream) {
   if (balanced)
-    hipLaunchKernelGGL((pa_decode_balanced_kernel<IO, KV, D>), grid, dim3(kThreads),
+    hipLaunchKernelGGL((pa_decode_balanced_kernel<IO, KV, D, MQ>), grid, dim3(kThreads),
                        bal_layout(prm.group, D, prm.batch).total, stream, prm);
   else
-    hipLaunchKernelGGL((pa_decode_kernel<IO, KV, D>), grid, dim3(kThreads), 0, stream, prm);
+    hipLaunchKernelGGL((pa_decode_kernel<IO, KV, D, MQ>), grid, dim3(kThreads), 0, stream, prm);
   return hipGetLastError();
 }
 
-template <typename IO, typename KV>
+template <typename IO, typename KV, bool MQ>
 static hipError_t launch_d(int D, const Params& prm, dim3 grid, bool balanced, hipStream_t stream) {
-  return D == 64 ? launch<IO, KV, 64>(prm, grid, balanced, stream)
-                 : launch<IO, KV, 128>(prm, grid, balanced, stream);
+  return D == 64 ? launch<IO, KV, 64, MQ>(prm, grid, balanced, stream)
+                 : launch<IO, KV, 128, MQ>(prm, grid, balanced, stream);
 }
 
 static inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 }  // namespace pa
 
-extern "C" {
+namespace pa {
 
-size_t pa_decode_workspace_bytes(const pa_shape* shape) {
-  if (!pa::shape_ok(shape)) return 0;
+size_t decode_workspace_bytes(const pa_shape* shape, int q_len) {
+  if (!shape_ok(shape) || q_len < 1) return 0;
+  if ((long long)(shape->num_q_heads / shape->num_kv_heads) * q_len > kTileRows) return 0;
   int shares = 0;
   if (shape->partition_size == PA_SPLIT_BALANCED) {
-    shares = pa::balanced_shares();
+    shares = balanced_shares();
     if (shares < 0) return 0;
   }
-  return pa::ws_layout(shape, shares).total;
+  return ws_layout(shape, shares, q_len).total;
 }
 
-pa_status pa_decode(const pa_shape* shape, const void* q, const void* k_cache,
-                    const void* v_cache, const int32_t* block_table,
-                    const int32_t* context_lens, float scale, pa_dtype io_dtype,
-                    pa_dtype kv_dtype, const float* k_scale, const float* v_scale,
-                    void* workspace, size_t workspace_bytes, void* out, float* lse_out,
-                    void* stream) {
-  using namespace pa;
+pa_status decode_call(const pa_shape* shape, int q_len, const void* q, const void* k_cache,
+                      const void* v_cache, const int32_t* block_table,
+                      const int32_t* context_lens, float scale, pa_dtype io_dtype,
+                      pa_dtype kv_dtype, const float* k_scale, const float* v_scale,
+                      void* workspace, size_t workspace_bytes, void* out, float* lse_out,
+                      void* stream) {
   if (!shape) return PA_ERR_NULL;
-  if (!shape_ok(shape)) return PA_ERR_SHAPE;
+  if (!shape_ok(shape) || q_len < 1) return PA_ERR_SHAPE;
+  const int G = shape->num_q_heads / shape->num_kv_heads;
+  if ((long long)G * q_len > kTileRows) return PA_ERR_SHAPE;
+  if ((long long)shape->batch * q_len * shape->num_q_heads > 0x7fffffffLL) return PA_ERR_SHAPE;
   if (!q || !k_cache || !v_cache || !block_table || !context_lens || !out) return PA_ERR_NULL;
   const bool io_ok = io_dtype == PA_F32 || io_dtype == PA_F16 || io_dtype == PA_BF16;
   const bool kv_ok = kv_dtype == io_dtype || (kv_dtype == PA_FP8_E4M3 && io_dtype != PA_F32);
@@ -1168,7 +1296,7 @@ pa_status pa_decode(const pa_shape* shape, const void* q, const void* k_cache,
     shares = balanced_shares();
     if (shares < 0) return PA_ERR_HIP;
   }
-  const WsLayout wl = ws_layout(shape, shares);
+  const WsLayout wl = ws_layout(shape, shares, q_len);
   if (shape->partition_size != 0) {
     if (!workspace || workspace_bytes < wl.total) return PA_ERR_WORKSPACE;
     if ((uintptr_t)workspace & 255u) return PA_ERR_ALIGN;
@@ -1194,11 +1322,13 @@ pa_status pa_decode(const pa_shape* shape, const void* q, const void* k_cache,
   prm.batch = shape->batch;
   prm.num_q_heads = shape->num_q_heads;
   prm.num_kv_heads = shape->num_kv_heads;
-  prm.group = shape->num_q_heads / shape->num_kv_heads;
+  prm.group = G * q_len;   // rows per (sequence, KV head)
   prm.max_blocks_per_seq = shape->max_blocks_per_seq;
   prm.num_blocks = shape->num_blocks;
   prm.part_tokens = shape->partition_size;
   prm.p_max = wl.p_max;
+  prm.q_len = q_len;
+  prm.gq = G;
 
   // 1-D grid: one workgroup per unit, or one per share (see the kernels)
   const long long nbg = (long long)shape->batch * shape->num_kv_heads;
@@ -1206,15 +1336,42 @@ pa_status pa_decode(const pa_shape* shape, const void* q, const void* k_cache,
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t e;
   const int D = shape->head_dim;
-  if (io_dtype == PA_F32)
-    e = launch_d<F32, F32>(D, prm, grid, balanced, st);
-  else if (io_dtype == PA_F16)
-    e = kv_dtype == PA_FP8_E4M3 ? launch_d<F16, FP8>(D, prm, grid, balanced, st)
-                                : launch_d<F16, F16>(D, prm, grid, balanced, st);
-  else
-    e = kv_dtype == PA_FP8_E4M3 ? launch_d<BF16, FP8>(D, prm, grid, balanced, st)
-                                : launch_d<BF16, BF16>(D, prm, grid, balanced, st);
+  if (q_len == 1) {
+    if (io_dtype == PA_F32)
+      e = launch_d<F32, F32, false>(D, prm, grid, balanced, st);
+    else if (io_dtype == PA_F16)
+      e = kv_dtype == PA_FP8_E4M3 ? launch_d<F16, FP8, false>(D, prm, grid, balanced, st)
+                                  : launch_d<F16, F16, false>(D, prm, grid, balanced, st);
+    else
+      e = kv_dtype == PA_FP8_E4M3 ? launch_d<BF16, FP8, false>(D, prm, grid, balanced, st)
+                                  : launch_d<BF16, BF16, false>(D, prm, grid, balanced, st);
+  } else {
+    if (io_dtype == PA_F32)
+      e = launch_d<F32, F32, true>(D, prm, grid, balanced, st);
+    else if (io_dtype == PA_F16)
+      e = kv_dtype == PA_FP8_E4M3 ? launch_d<F16, FP8, true>(D, prm, grid, balanced, st)
+                                  : launch_d<F16, F16, true>(D, prm, grid, balanced, st);
+    else
+      e = kv_dtype == PA_FP8_E4M3 ? launch_d<BF16, FP8, true>(D, prm, grid, balanced, st)
+                                  : launch_d<BF16, BF16, true>(D, prm, grid, balanced, st);
+  }
   return e == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+}  // namespace pa
+
+extern "C" {
+
+size_t pa_decode_workspace_bytes(const pa_shape* shape) { return pa::decode_workspace_bytes(shape, 1); }
+
+pa_status pa_decode(const pa_shape* shape, const void* q, const void* k_cache,
+                    const void* v_cache, const int32_t* block_table,
+                    const int32_t* context_lens, float scale, pa_dtype io_dtype,
+                    pa_dtype kv_dtype, const float* k_scale, const float* v_scale,
+                    void* workspace, size_t workspace_bytes, void* out, float* lse_out,
+                    void* stream) {
+  return pa::decode_call(shape, 1, q, k_cache, v_cache, block_table, context_lens, scale, io_dtype,
+                         kv_dtype, k_scale, v_scale, workspace, workspace_bytes, out, lse_out, stream);
 }
 
 pa_status pa_workspace_reset(void* workspace, size_t workspace_bytes, void* stream) {

@@ -7,6 +7,10 @@
 // step). The new tokens' K and V are already in the cache, so a sequence's
 // length L counts them; new token t (0 .. T-1) sees positions 0 .. L-T+t.
 //
+// When a pair's rows fit one matrix-core tile (G * T <= 16) the call runs on
+// the decode kernels (fixed partitions or the balanced split), which take the
+// same row mapping and causal masks; this kernel serves wider row sets.
+//
 // Same building blocks and cache layouts as single-token decode. A workgroup
 // of four waves owns one (sequence b, KV head g, partition p, row chunk c)
 // unit. The query rows of a (b, g) pair are its G*T (new token, head) pairs,
@@ -37,6 +41,7 @@
 #include <type_traits>
 
 #include "padecode.h"
+#include "pa_internal.h"
 #include "pa_tiles.h"
 
 namespace pa_mq {
@@ -469,9 +474,8 @@ static bool plan(const pa_shape* s, int q_len, Plan* out) {
 
 template <typename IO, typename KV, int D>
 static hipError_t launch_nt(int nt, const Params& prm, dim3 grid, hipStream_t st) {
-  if (nt == 1)   // one tile: one chunk
-    hipLaunchKernelGGL((pa_multi_kernel<IO, KV, D, 1, false>), grid, dim3(kThreads), 0, st, prm);
-  else if (prm.chunks <= 2)
+  (void)nt;   // always 2: rows that fit one tile run on the decode kernels
+  if (prm.chunks <= 2)
     hipLaunchKernelGGL((pa_multi_kernel<IO, KV, D, 2, false>), grid, dim3(kThreads), 0, st, prm);
   else
     hipLaunchKernelGGL((pa_multi_kernel<IO, KV, D, 2, true>), grid, dim3(kThreads), 0, st, prm);
@@ -490,6 +494,9 @@ static inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; 
 extern "C" {
 
 size_t pa_decode_multi_workspace_bytes(const pa_shape* shape, int32_t q_len) {
+  if (shape && shape->num_kv_heads > 0 && q_len >= 1 && q_len <= pa_mq::kMaxQLen &&
+      (long long)(shape->num_q_heads / shape->num_kv_heads) * q_len <= pa::kTileRows)
+    return pa::decode_workspace_bytes(shape, q_len);
   pa_mq::Plan p;
   if (!pa_mq::plan(shape, q_len, &p)) return 0;
   return p.total;
@@ -503,6 +510,11 @@ pa_status pa_decode_multi(const pa_shape* shape, int32_t q_len, const void* q, c
                           void* stream) {
   using namespace pa_mq;
   if (!shape) return PA_ERR_NULL;
+  if (shape->num_kv_heads > 0 && q_len >= 1 && q_len <= kMaxQLen &&
+      (long long)(shape->num_q_heads / shape->num_kv_heads) * q_len <= pa::kTileRows)
+    return pa::decode_call(shape, q_len, q, k_cache, v_cache, block_table, context_lens, scale,
+                           io_dtype, kv_dtype, k_scale, v_scale, workspace, workspace_bytes, out,
+                           lse_out, stream);
   Plan pl;
   if (!plan(shape, q_len, &pl)) return PA_ERR_SHAPE;
   if (!q || !k_cache || !v_cache || !block_table || !context_lens || !out) return PA_ERR_NULL;

@@ -190,7 +190,7 @@ def test_multi_token_call_rejects_bad_arguments_before_any_launch():
         assert call_multi(shape(), **{kw: None}) == 1, kw
     for T in (0, 17, -1):
         assert call_multi(shape(), q_len=T) == 2
-    assert call_multi(shape(partition_size=-1)) == 2             # no balanced split here
+    assert call_multi(shape(partition_size=-1), q_len=5) == 2    # 20 rows: no balanced split
     assert call_multi(shape(partition_size=24)) == 2
     assert call_multi(shape(num_q_heads=40, num_kv_heads=2)) == 2
     assert call_multi(shape(), io=0, kv=3, ks=FAKE, vs=FAKE) == 3
@@ -228,3 +228,22 @@ def test_multi_token_workspace_size_arithmetic():
     # one new token: the same rows as decode, one counter per (sequence, KV head)
     s = shape(partition_size=512)
     assert ws(1, partition_size=512) == lib.pa_decode_workspace_bytes(ctypes.byref(s))
+
+
+def test_multi_token_rows_of_one_tile_take_the_decode_kernels():
+    # G * q_len <= 16: the decode kernels' workspace layout (one counter per
+    # (sequence, KV head)) and the balanced split are available
+    lib = _lib.load_library()
+    s = shape(partition_size=512)                 # G = 4
+    rows4 = lib.pa_decode_multi_workspace_bytes(ctypes.byref(s), 4)
+    up = lambda x: (x + 255) // 256 * 256
+    b, hkv, p, d, rows = 2, 2, 32, 128, 16        # 32 blocks of 16 tokens / 512 = 1 partition
+    p = (32 * 16 + 511) // 512
+    assert rows4 == up(b * hkv * 4) + up(b * hkv * p * rows * d * 4) + up(b * hkv * p * rows * 4)
+    if torch_gpu_count() == 0:                    # stops at the device query, nothing launched
+        assert call_multi(shape(partition_size=-1), q_len=4) == 6
+
+
+def torch_gpu_count():
+    import torch
+    return torch.cuda.device_count()

@@ -219,3 +219,54 @@ def test_largest_batch_and_rows_sampled():
     out = to_f64(run_multi(wl, q))
     seqs = sorted(set([0, 1, 777, 2047] + [int(b) for b in np.nonzero(wl.context_lens < 16)[0][:8]]))
     check(wl, out, ref_multi(wl, q, seqs=seqs), seqs=seqs, label="large")
+
+
+@pytest.mark.parametrize("io,kv", DTYPES)
+@pytest.mark.parametrize("hq,hkv,T", [(8, 2, 4), (8, 4, 8), (28, 4, 2), (16, 1, 1), (8, 8, 16)])
+def test_balanced_split_when_rows_fit_one_tile(io, kv, hq, hkv, T):
+    # G * T <= 16: the decode kernels run the call; the balanced split cuts
+    # the pairs' pages into equal shares, including the pages that hold
+    # the new tokens (causal masks) and sequences shorter than T
+    spec = spec_of(f"mq_bal_{io}_{kv}_{hq}_{hkv}_{T}", io, kv, 128, [1, 3, 17, 100, 700, 2047],
+                   hq=hq, hkv=hkv, ps=-1, seed=T + hq)
+    print(f"case {spec.name}", flush=True)
+    wl = W.make_workload(spec)
+    q = W.multi_query(wl, T)
+    out, lse = run_multi(wl, q, lse=True)
+    exp, rlse = ref_multi(wl, q, lse=True)
+    check(wl, to_f64(out), exp, label=spec.name)
+    l = lse.cpu().numpy().astype(np.float64)
+    assert np.array_equal(np.isneginf(l), np.isneginf(rlse))
+    fin = np.isfinite(rlse)
+    assert np.abs(l[fin] - rlse[fin]).max() <= 2e-3
+
+
+@pytest.mark.parametrize("ps", [-1, 0, 512])
+def test_tile_rows_long_context_shape_sampled(ps):
+    # the long-context workload (Llama-3-8B shape, G = 4) with four new
+    # tokens: 16 rows, the decode kernels in all three split modes
+    spec = W.SPECS[5]
+    wl = W.make_workload(spec)
+    q = W.multi_query(wl, 4)
+    print(f"case full {spec.name} T=4 ps{ps}", flush=True)
+    out = to_f64(run_multi(wl, q, ps=ps))
+    assert np.isfinite(out).all()
+    seqs = [0, 3, 7]
+    check(wl, out, ref_multi(wl, q, seqs=seqs), seqs=seqs, label=f"long-T4-ps{ps}")
+
+
+def test_tile_rows_split_modes_agree_and_t1_is_decode_in_every_mode():
+    spec = spec_of("mq_modes", "f16", "f16", 128, [5, 600, 1500, 33], ps=512, seed=13)
+    wl = W.make_workload(spec)
+    t = to_device(wl)
+    q = W.multi_query(wl, 4)
+    outs = [to_f64(run_multi(wl, q, t=t, ps=ps)) for ps in (0, 512, -1)]
+    assert np.abs(outs[0] - outs[1]).max() <= 2e-3 and np.abs(outs[0] - outs[2]).max() <= 2e-3
+    q1 = W.multi_query(wl, 1)
+    for ps in (0, 512, -1):
+        got = run_multi(wl, q1, t=t, ps=ps)
+        dec = pkd.decode(storage_tensor(np.ascontiguousarray(q1[:, 0]), "f16").cuda(),
+                         t["k_cache"], t["v_cache"], t["block_table"], t["context_lens"],
+                         float(wl.scale), partition_size=ps)
+        torch.cuda.synchronize()
+        assert torch.equal(got[:, 0].cpu().view(torch.int16), dec.cpu().view(torch.int16)), ps
