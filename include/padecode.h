@@ -115,12 +115,18 @@ typedef struct {
  * log-sum-exps of every (sequence, query head, partition) -- for the balanced
  * split, of (shares + batch * num_kv_heads) pieces per query head of a group,
  * where shares depends on the current device's compute units -- plus one
- * counter per (sequence, KV head). The counters come first: the workspace's
- * first 4 * batch * num_kv_heads bytes, rounded up to 256; every completed
- * call leaves them zero, and the rest is scratch. So a workspace needs
- * pa_workspace_reset (a zero fill on a stream) before its first use, and again
- * before a call whose batch * num_kv_heads is larger than that of any earlier
- * call since the last reset (its counters would cover old scratch bytes).
+ * counter per (sequence, KV head).
+ * With fixed partitions and P = ceil(16 * max_blocks_per_seq / partition_size)
+ * > 16, a sequence's partitions are merged in two levels: groups of F
+ * consecutive partitions first (F the smallest integer >= 16 with F * F >= P),
+ * then the groups. That adds ceil(P / F) group pieces per (sequence, query
+ * head) and ceil(P / F) counters per (sequence, KV head).
+ * The counters come first: the workspace's first 4 * batch * num_kv_heads *
+ * (1 + groups) bytes, rounded up to 256; every completed call leaves them
+ * zero, and the rest is scratch. So a workspace needs pa_workspace_reset (a
+ * zero fill on a stream) before its first use, and again before a call whose
+ * counter bytes exceed those of every earlier call since the last reset (its
+ * counters would cover old scratch bytes).
  * Returns 0 for a NULL or invalid shape. */
 size_t pa_decode_workspace_bytes(const pa_shape* shape);
 
@@ -161,9 +167,11 @@ pa_status pa_decode(const pa_shape* shape, const void* q, const void* k_cache,
  *               16, or PA_SPLIT_BALANCED when G * q_len <= 16
  *               (G = num_q_heads / num_kv_heads)
  *   workspace   pa_decode_multi_workspace_bytes(shape, q_len) bytes when
- *               partition_size != 0; same counter-first contract as
- *               pa_decode, with one counter per (sequence, KV head) when
- *               G * q_len <= 16, else ceil(ceil(G*q_len/16)/2)
+ *               partition_size != 0; same counter-first contract and
+ *               two-level merge as pa_decode, with one counter per
+ *               (sequence, KV head) and merge level-1 group when
+ *               G * q_len <= 16, else ceil(ceil(G*q_len/16)/2) (one per
+ *               chunk of 32 rows)
  * Everything else (dtypes, scales, alignment, errors) as for pa_decode. */
 size_t pa_decode_multi_workspace_bytes(const pa_shape* shape, int32_t q_len);
 pa_status pa_decode_multi(const pa_shape* shape, int32_t q_len, const void* q,

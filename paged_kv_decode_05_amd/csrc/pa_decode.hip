@@ -62,7 +62,8 @@ struct Params {
   float* lse_out;
   float* ws_o;       // [slot][G][D]   partial outputs, normalised
   float* ws_lse;     // [slot][G]      base 2, in units of the scaled scores
-  uint32_t* ws_cnt;  // [B][Hkv]       pieces of (b, g) finished so far
+  uint32_t* ws_cnt;  // [B][Hkv] pieces (or first-level groups) of (b, g) finished so
+                     // far, then [B][Hkv][g_max] partitions of each group finished
   float scale;
   int32_t batch;
   int32_t num_q_heads;
@@ -72,6 +73,10 @@ struct Params {
   int32_t num_blocks;
   int32_t part_tokens;  // 0: whole sequence in one unit
   int32_t p_max;        // fixed partitions: slots per (b, g)
+  int32_t fan;          // fixed partitions: partitions per first-level merge group
+                        // (0: a single merge level)
+  int32_t g_max;        // first-level groups per (b, g); their slots follow the
+                        // B * Hkv * p_max partition slots
   int32_t q_len;        // new tokens per sequence (1: decode)
   int32_t gq;           // query heads per KV head (group = gq * q_len rows)
 };
@@ -102,8 +107,10 @@ struct Smem {
 };
 
 // Merge the nparts pieces of (b, g) stored in workspace slots slot0 ...
-// slot0 + nparts - 1 (partitions, or shares of the balanced split) and write
-// the final output of its query heads. Threads take (head, 4-float quad)
+// slot0 + nparts - 1 (partitions, first-level groups of partitions, or shares
+// of the balanced split) and write the final output of its query heads, or,
+// when dst >= 0, the merged piece (normalised output and base-2 log-sum-exp,
+// like any other piece) to workspace slot dst. Threads take (head, 4-float quad)
 // pairs; when the group leaves threads over, S slices split the pieces (slice
 // s takes p = s, s + S, ...). Every thread issues the loads of 8 partitions before
 // folding them with a running max, and slices are combined in order 0, 1, ...,
@@ -114,7 +121,8 @@ constexpr int kMergeScratch = 6 * kThreads;
 // with nothing in any piece gets 0 and -inf) and NaN is tracked explicitly;
 // pieces are not sliced.
 template <typename IO, int D, bool MQ>
-__device__ __forceinline__ void merge_partitions(const Params& a, float* red, int b, int g, int slot0, int nparts) {
+__device__ __forceinline__ void merge_partitions(const Params& a, float* red, int b, int g, size_t slot0, int nparts,
+                                                 long long dst = -1) {
   constexpr int kQuads = D / 4;
   constexpr int kBatch = 8;
   const int tid = threadIdx.x;
@@ -129,7 +137,7 @@ __device__ __forceinline__ void merge_partitions(const Params& a, float* red, in
     size_t row;
     if constexpr (MQ) row = mq_row<MQ>(a, b, g, h);
     else row = (size_t)b * a.num_q_heads + g * a.group + h;
-    const float* lse = a.ws_lse + (size_t)slot0 * a.group + h;
+    const float* lse = a.ws_lse + slot0 * a.group + h;
     float mr = -INFINITY, wr = 0.f;
     bool nan = false;
     f32x4 ar = {0.f, 0.f, 0.f, 0.f};
@@ -137,7 +145,7 @@ __device__ __forceinline__ void merge_partitions(const Params& a, float* red, in
     // batch's first slot (offsets stay small whatever nparts is)
     for (int p0 = 0; p0 < nparts; p0 += kBatch * S) {
       const int nb = min(kBatch * S, nparts - p0);
-      const brsrc r = buffer_rsrc(a.ws_o + ((size_t)slot0 + p0) * slot_floats,
+      const brsrc r = buffer_rsrc(a.ws_o + (slot0 + p0) * slot_floats,
                                   (uint32_t)(nb * slot_floats * sizeof(float)));
       float lp[kBatch];
       f32x4 ov[kBatch];
@@ -192,21 +200,25 @@ __device__ __forceinline__ void merge_partitions(const Params& a, float* red, in
       }
     }
     if (active && sl == 0) {
+      // base-2 log-sum-exp of the merged piece; a NaN piece makes ar, wr NaN
+      f32x4 val = {ar[0] / wr, ar[1] / wr, ar[2] / wr, ar[3] / wr};
+      float lse2 = mr + log2_fast(wr);
       if constexpr (MQ) {
-        f32x4 val = {0.f, 0.f, 0.f, 0.f};
-        float lse2 = -INFINITY;
         if (nan) {
           val = f32x4{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
           lse2 = __builtin_nanf("");
-        } else if (wr > 0.f) {
-          val = f32x4{ar[0] / wr, ar[1] / wr, ar[2] / wr, ar[3] / wr};
-          lse2 = (mr + log2_fast(wr)) * kLn2;
+        } else if (!(wr > 0.f)) {
+          val = f32x4{0.f, 0.f, 0.f, 0.f};
+          lse2 = -INFINITY;
         }
+      }
+      if (dst < 0) {
         store_out4<IO>(a.out, row * D + 4 * dq, val);
-        if (dq == 0 && a.lse_out) a.lse_out[row] = lse2;
+        if (dq == 0 && a.lse_out) a.lse_out[row] = lse2 * kLn2;
       } else {
-        store_out4<IO>(a.out, row * D + 4 * dq, f32x4{ar[0] / wr, ar[1] / wr, ar[2] / wr, ar[3] / wr});
-        if (dq == 0 && a.lse_out) a.lse_out[row] = (mr + log2_fast(wr)) * kLn2;
+        const brsrc wd = buffer_rsrc(a.ws_o + (size_t)dst * slot_floats, (uint32_t)(slot_floats * sizeof(float)));
+        st_agent4(wd, (uint32_t)((h * D + 4 * dq) * sizeof(float)), val);
+        if (dq == 0) st_agent(a.ws_lse + (size_t)dst * a.group + h, lse2);
       }
     }
   }
@@ -492,20 +504,28 @@ __device__ __forceinline__ void decode_piece(const Params& a, Smem<D>& sm, const
   if (!split) return;
 
   // ---- split-K: the last partition of (b, g) to finish merges ------------
-  // Every wave waits until its agent-coherent stores have completed before the
-  // barrier, so the counter increment is ordered after all of them.
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  uint32_t* cnt = a.ws_cnt + (size_t)b * a.num_kv_heads + g;
-  if (tid == 0) {
-    const uint32_t done = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    sm.last = done == (uint32_t)(pc.nparts - 1);
-  }
-  __syncthreads();
-  if (!__builtin_amdgcn_readfirstlane(sm.last)) return;   // uniform: a scalar branch
+  // With more than a.fan partitions (fixed partitions only) the merge has two
+  // levels: the last finisher of each group of a.fan consecutive partitions
+  // merges the group into a group slot, and the last group merges the group
+  // slots. A single workgroup reading hundreds of partials would be held to
+  // one CU's read rate.
   static_assert(sizeof(sm.acc) >= kMergeScratch * sizeof(float), "merge scratch");
-  merge_partitions<IO, D, MQ>(a, &sm.acc[0][0][0], b, g, pc.slot0, pc.nparts);
-  if (tid == 0) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  float* red = &sm.acc[0][0][0];
+  const size_t nbg = (size_t)a.batch * a.num_kv_heads;
+  const size_t bg = (size_t)b * a.num_kv_heads + g;
+  size_t first = pc.slot0;
+  int np = pc.nparts;
+  if (a.fan > 0 && pc.nparts > a.fan) {
+    const int grp = pc.k / a.fan;
+    const int gfirst = grp * a.fan;
+    const int gn = min(a.fan, pc.nparts - gfirst);
+    first = nbg * a.p_max + bg * a.g_max;   // the group slots of (b, g)
+    if (!last_to_finish(a.ws_cnt + nbg + bg * a.g_max + grp, gn, &sm.last)) return;
+    merge_partitions<IO, D, MQ>(a, red, b, g, (size_t)pc.slot0 + gfirst, gn, (long long)(first + grp));
+    np = (pc.nparts + a.fan - 1) / a.fan;
+  }
+  if (!last_to_finish(a.ws_cnt + bg, np, &sm.last)) return;
+  merge_partitions<IO, D, MQ>(a, red, b, g, first, np);
 }
 
 // Fixed schedule: one workgroup per (sequence b, KV head g, partition p) unit
@@ -1166,8 +1186,9 @@ __global__ void fill_zero_kernel(uint8_t* p, size_t n) {
 // ---------------------------------------------------------------------------
 struct WsLayout {
   size_t o_off, lse_off, cnt_off, total;
-  int p_max;
+  int p_max, fan, g_max;
 };
+
 
 static inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
@@ -1205,32 +1226,39 @@ static bool shape_ok(const pa_shape* s) {
     return line + 4096LL * 3 < 0x7fffffffLL;   // + shares (4096 CUs at most, 3 per CU)
   }
   if (s->partition_size < 0 || s->partition_size % kBlock != 0) return false;
-  // work units B * Hkv * partitions must fit a 1-D grid
+  // work units B * Hkv * partitions, and the partition and group slots, must
+  // fit a 1-D grid and int32 slot numbers
   const long long parts =
       s->partition_size ? ((long long)s->max_blocks_per_seq * kBlock + s->partition_size - 1) / s->partition_size : 1;
-  if ((long long)s->batch * s->num_kv_heads * parts > 0x7fffffffLL) return false;
+  const int fan = merge_fan(parts);
+  const long long groups = fan ? (parts + fan - 1) / fan : 0;
+  if ((long long)s->batch * s->num_kv_heads * (parts + groups) > 0x7fffffffLL) return false;
   return true;
 }
 
 // shares: the balanced split's workgroup count (ignored otherwise); q_len:
 // new tokens per sequence (rows per pair = group * q_len)
 static WsLayout ws_layout(const pa_shape* s, int shares, int q_len) {
-  WsLayout w{0, 0, 0, 0, 1};
+  WsLayout w{0, 0, 0, 0, 1, 0, 0};
   if (s->partition_size == 0) return w;
+  const size_t nbg = (size_t)s->batch * s->num_kv_heads;
   size_t slots;
   if (s->partition_size == PA_SPLIT_BALANCED) {
     w.p_max = 0;
-    slots = (size_t)shares + (size_t)s->batch * s->num_kv_heads;
+    slots = (size_t)shares + nbg;
   } else {
     const long long tokens = (long long)s->max_blocks_per_seq * kBlock;
     w.p_max = (int)((tokens + s->partition_size - 1) / s->partition_size);
-    slots = (size_t)s->batch * s->num_kv_heads * w.p_max;
+    w.fan = merge_fan(w.p_max);
+    w.g_max = w.fan ? (w.p_max + w.fan - 1) / w.fan : 0;
+    slots = nbg * (w.p_max + w.g_max);   // partition slots, then group slots
   }
   const size_t rows = slots * (size_t)(s->num_q_heads / s->num_kv_heads) * q_len;
-  // counters first: their bytes stay where they are for every shape, so a
-  // smaller call after a larger one finds them zero
+  // counters first (one per (b, g), then g_max per (b, g)): every completed
+  // call leaves them zero, so a later call whose counters fit in the same
+  // bytes finds them zero
   w.cnt_off = 0;
-  w.o_off = align_up((size_t)s->batch * s->num_kv_heads * sizeof(uint32_t), 256);
+  w.o_off = align_up(nbg * (1 + (size_t)w.g_max) * sizeof(uint32_t), 256);
   w.lse_off = w.o_off + align_up(rows * s->head_dim * sizeof(float), 256);
   w.total = w.lse_off + align_up(rows * sizeof(float), 256);
   return w;
@@ -1327,6 +1355,8 @@ pa_status decode_call(const pa_shape* shape, int q_len, const void* q, const voi
   prm.num_blocks = shape->num_blocks;
   prm.part_tokens = shape->partition_size;
   prm.p_max = wl.p_max;
+  prm.fan = wl.fan;
+  prm.g_max = wl.g_max;
   prm.q_len = q_len;
   prm.gq = G;
 

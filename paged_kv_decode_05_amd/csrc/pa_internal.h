@@ -4,11 +4,25 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <cmath>
+
 #include "padecode.h"
 
 namespace pa {
 
 constexpr int kTileRows = 16;   // query rows one matrix-core tile holds
+
+// Fixed partitions: up to kMergeFan partitions of a sequence are merged in
+// one level; beyond that, groups of fan partitions first, fan being the
+// smallest value >= kMergeFan with fan * fan >= p_max, so that neither level
+// merges more than fan pieces. Returns 0 for one level.
+constexpr int kMergeFan = 16;
+inline int merge_fan(long long p_max) {
+  if (p_max <= kMergeFan) return 0;
+  long long f = (long long)std::sqrt((double)p_max);
+  while (f * f < p_max) ++f;
+  return (int)(f < kMergeFan ? kMergeFan : f);
+}
 
 // The decode kernels for q_len new tokens per sequence whose
 // (new token, query head) rows fit one tile: group * q_len <= kTileRows.

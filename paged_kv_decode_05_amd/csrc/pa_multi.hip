@@ -61,7 +61,7 @@ struct Params {
   float* lse_out;            // [B][T][Hq] or null
   float* ws_o;               // [slot][R][D]  partial outputs, normalised
   float* ws_lse;             // [slot][R]     base 2, in units of the scaled scores
-  uint32_t* ws_cnt;          // [B][Hkv][chunks]
+  uint32_t* ws_cnt;          // [B][Hkv][chunks], then [B][Hkv][g_max][chunks] (first-level groups)
   float scale;
   int32_t batch;
   int32_t num_q_heads;
@@ -74,7 +74,76 @@ struct Params {
   int32_t num_blocks;
   int32_t part_tokens;
   int32_t p_max;
+  int32_t fan;               // partitions per first-level merge group (0: one level)
+  int32_t g_max;             // first-level groups per (b, g); their slots follow the
+                             // B * Hkv * p_max partition slots
 };
+
+// Merge the n pieces of rows row0 .. row0 + rows_c - 1 of (b, g) stored in
+// workspace slots slot0 .. slot0 + n - 1 (partitions, or first-level groups
+// of partitions) in slot order, and write the final output of those rows
+// (dst < 0) or the merged piece to workspace slot dst. Every thread issues
+// the loads of kBatch pieces before folding them with a running max. A piece
+// a row sees nothing of (lse = -inf) adds nothing; a row that sees nothing in
+// any piece gets out = 0 and lse = -inf; NaN in any piece gives NaN.
+template <typename IO, int D>
+__device__ __forceinline__ void merge_rows(const Params& a, int b, int g, int row0, int rows_c,
+                                           size_t slot0, int n, long long dst) {
+  constexpr int kBatch = 8;
+  const int R = a.rows, G = a.group;
+  for (int i = threadIdx.x; i < rows_c * (D / 4); i += kThreads) {
+    const int r2 = i / (D / 4), d = 4 * (i - r2 * (D / 4));
+    const int rho = row0 + r2;
+    float mr = -INFINITY, wr = 0.f;
+    f32x4 ar = {0.f, 0.f, 0.f, 0.f};
+    bool nan = false;
+    for (int q0 = 0; q0 < n; q0 += kBatch) {
+      const int nb = min(kBatch, n - q0);
+      const brsrc r = buffer_rsrc(a.ws_o + (slot0 + q0) * R * D, (uint32_t)(nb * R * D * sizeof(float)));
+      float lp[kBatch];
+      f32x4 ov[kBatch];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        if (u < nb) {
+          lp[u] = ld_agent(a.ws_lse + (slot0 + q0 + u) * R + rho);
+          ov[u] = ld_agent4(r, (uint32_t)((((size_t)u * R + rho) * D + d) * sizeof(float)));
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        if (u < nb) {
+          if (lp[u] != lp[u]) nan = true;
+          if (lp[u] > -INFINITY) {
+            const float mn = fmaxf(mr, lp[u]);
+            const float sa = exp2_fast(mr - mn), sb = exp2_fast(lp[u] - mn);
+            ar = ar * sa + ov[u] * sb;
+            wr = wr * sa + sb;
+            mr = mn;
+          }
+        }
+      }
+    }
+    f32x4 val = {0.f, 0.f, 0.f, 0.f};
+    float lse2 = -INFINITY;   // base 2
+    if (nan) {
+      val = f32x4{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
+      lse2 = __builtin_nanf("");
+    } else if (wr > 0.f) {
+      val = f32x4{ar[0] / wr, ar[1] / wr, ar[2] / wr, ar[3] / wr};
+      lse2 = mr + log2_fast(wr);
+    }
+    if (dst < 0) {
+      const int t = rho / G, h = rho - t * G;
+      const size_t orow = ((size_t)b * a.q_len + t) * a.num_q_heads + (size_t)g * G + h;
+      store_out4<IO>(a.out, orow * D + d, val);
+      if (d == 0 && a.lse_out) a.lse_out[orow] = lse2 * kLn2;
+    } else {
+      const brsrc wd = buffer_rsrc(a.ws_o + (size_t)dst * R * D, (uint32_t)(R * D * sizeof(float)));
+      st_agent4(wd, (uint32_t)(((size_t)rho * D + d) * sizeof(float)), val);
+      if (d == 0) st_agent(a.ws_lse + (size_t)dst * R + rho, lse2);
+    }
+  }
+}
 
 template <typename QC, int NT, int KQ, int D>
 struct MqSmem {
@@ -368,71 +437,31 @@ pa_multi_kernel(const Params a) {
   if (!split) return;
 
   // ---- split-K: the last partition of (b, g, c) to finish merges ----------
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  uint32_t* cnt = a.ws_cnt + (size_t)bg * a.chunks + c;
-  if (tid == 0) {
-    const uint32_t done = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    sm.last = done == (uint32_t)(nparts - 1);
+  // With more than a.fan partitions the merge has two levels, as for decode:
+  // the last finisher of each group of a.fan partitions merges the group's
+  // rows of this chunk into a group slot, the last group merges the groups.
+  size_t first = (size_t)bg * a.p_max;
+  int np = nparts;
+  if (a.fan > 0 && nparts > a.fan) {
+    const int grp = p / a.fan;
+    const int gfirst = grp * a.fan;
+    const int gn = min(a.fan, nparts - gfirst);
+    const size_t gbase = (size_t)nbg * a.p_max + (size_t)bg * a.g_max;   // group slots of (b, g)
+    if (!last_to_finish(a.ws_cnt + ((size_t)nbg + (size_t)bg * a.g_max + grp) * a.chunks + c, gn, &sm.last))
+      return;
+    merge_rows<IO, D>(a, b, g, row0, rows_c, first + gfirst, gn, (long long)(gbase + grp));
+    first = gbase;
+    np = (nparts + a.fan - 1) / a.fan;
   }
-  __syncthreads();
-  if (!__builtin_amdgcn_readfirstlane(sm.last)) return;
-  constexpr int kBatch = 8;
-  const size_t slot0 = (size_t)bg * a.p_max;
-  for (int i = tid; i < rows_c * (D / 4); i += kThreads) {
-    const int r2 = i / (D / 4), d = 4 * (i - r2 * (D / 4));
-    const int rho = row0 + r2;
-    float mr = -INFINITY, wr = 0.f;
-    f32x4 ar = {0.f, 0.f, 0.f, 0.f};
-    bool nan = false;
-    for (int q0 = 0; q0 < nparts; q0 += kBatch) {
-      const int nb = min(kBatch, nparts - q0);
-      const brsrc r = buffer_rsrc(a.ws_o + (slot0 + q0) * R * D, (uint32_t)(nb * R * D * sizeof(float)));
-      float lp[kBatch];
-      f32x4 ov[kBatch];
-#pragma unroll
-      for (int u = 0; u < kBatch; ++u) {
-        if (u < nb) {
-          lp[u] = ld_agent(a.ws_lse + (slot0 + q0 + u) * R + rho);
-          ov[u] = ld_agent4(r, (uint32_t)((((size_t)u * R + rho) * D + d) * sizeof(float)));
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < kBatch; ++u) {
-        if (u < nb) {
-          if (lp[u] != lp[u]) nan = true;
-          if (lp[u] > -INFINITY) {   // a partition this row sees nothing of adds nothing
-            const float mn = fmaxf(mr, lp[u]);
-            const float sa = exp2_fast(mr - mn), sb = exp2_fast(lp[u] - mn);
-            ar = ar * sa + ov[u] * sb;
-            wr = wr * sa + sb;
-            mr = mn;
-          }
-        }
-      }
-    }
-    f32x4 val = {0.f, 0.f, 0.f, 0.f};
-    float lse = -INFINITY;
-    if (nan) {
-      val = f32x4{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
-      lse = __builtin_nanf("");
-    } else if (wr > 0.f) {
-      val = f32x4{ar[0] / wr, ar[1] / wr, ar[2] / wr, ar[3] / wr};
-      lse = (mr + log2_fast(wr)) * kLn2;
-    }
-    const int t = rho / G, h = rho - t * G;
-    const size_t orow = ((size_t)b * TQ + t) * a.num_q_heads + (size_t)g * G + h;
-    store_out4<IO>(a.out, orow * D + d, val);
-    if (d == 0 && a.lse_out) a.lse_out[orow] = lse;
-  }
-  if (tid == 0) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (!last_to_finish(a.ws_cnt + (size_t)bg * a.chunks + c, np, &sm.last)) return;
+  merge_rows<IO, D>(a, b, g, row0, rows_c, first, np, -1);
 }
 
 // ---------------------------------------------------------------------------
 // Host side.
 // ---------------------------------------------------------------------------
 struct Plan {
-  int rows, tiles, chunks, nt, p_max;
+  int rows, tiles, chunks, nt, p_max, fan, g_max;
   size_t cnt_off, o_off, lse_off, total;
 };
 
@@ -455,16 +484,22 @@ static bool plan(const pa_shape* s, int q_len, Plan* out) {
   Plan p;
   p.rows = G * q_len;
   p.tiles = (p.rows + 15) / 16;
-  p.nt = p.tiles == 1 ? 1 : 2;
+  p.nt = 2;
   p.chunks = (p.tiles + p.nt - 1) / p.nt;
   const long long tokens = (long long)s->max_blocks_per_seq * kBlock;
   p.p_max = s->partition_size ? (int)((tokens + s->partition_size - 1) / s->partition_size) : 1;
   const long long units = (long long)s->batch * s->num_kv_heads * p.chunks * p.p_max;
   if (units > 0x7fffffffLL) return false;
+  p.fan = s->partition_size ? merge_fan(p.p_max) : 0;
+  p.g_max = p.fan ? (p.p_max + p.fan - 1) / p.fan : 0;
+  if ((long long)s->batch * s->num_kv_heads * (p.p_max + p.g_max) > 0x7fffffffLL) return false;
   p.cnt_off = p.o_off = p.lse_off = p.total = 0;
   if (s->partition_size) {
-    const size_t slots = (size_t)s->batch * s->num_kv_heads * p.p_max;
-    p.o_off = align_up((size_t)s->batch * s->num_kv_heads * p.chunks * sizeof(uint32_t), 256);
+    // counters first: [B][Hkv][chunks], then [B][Hkv][g_max][chunks]; slots:
+    // partitions, then first-level groups
+    const size_t nbg = (size_t)s->batch * s->num_kv_heads;
+    const size_t slots = nbg * (p.p_max + p.g_max);
+    p.o_off = align_up(nbg * (1 + (size_t)p.g_max) * p.chunks * sizeof(uint32_t), 256);
     p.lse_off = p.o_off + align_up(slots * p.rows * s->head_dim * sizeof(float), 256);
     p.total = p.lse_off + align_up(slots * p.rows * sizeof(float), 256);
   }
@@ -559,6 +594,8 @@ pa_status pa_decode_multi(const pa_shape* shape, int32_t q_len, const void* q, c
   prm.max_blocks_per_seq = shape->max_blocks_per_seq;
   prm.num_blocks = shape->num_blocks;
   prm.part_tokens = shape->partition_size;
+  prm.fan = pl.fan;
+  prm.g_max = pl.g_max;
   prm.p_max = pl.p_max;
 
   const long long units = (long long)shape->batch * shape->num_kv_heads * pl.chunks * pl.p_max;

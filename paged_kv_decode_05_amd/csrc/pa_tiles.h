@@ -113,6 +113,22 @@ __device__ __forceinline__ void st_agent4(brsrc r, uint32_t off, f32x4 v) {
   __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, 0, kCpolSc1);
 }
 
+// Split-K hand-off: every wave waits until its agent-coherent stores have
+// completed, then one thread counts this piece on *cnt; true (uniformly) for
+// the workgroup that brings the count to n, which then owns the merge and
+// resets the counter for the next call.
+__device__ __forceinline__ bool last_to_finish(uint32_t* cnt, int n, int* flag) {
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t done = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *flag = done == (uint32_t)(n - 1);
+    if (*flag) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __syncthreads();
+  return __builtin_amdgcn_readfirstlane(*flag) != 0;
+}
+
 // ---------------------------------------------------------------------------
 // Matrix-core operand types.
 //

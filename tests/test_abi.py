@@ -109,6 +109,19 @@ def test_workspace_size_arithmetic():
     # partitions round up: MBS*16 = 512 tokens / 48 -> 11
     expect = up(2 * 8 * 11 * 128 * 4) + up(2 * 8 * 11 * 4) + up(2 * 2 * 4)
     assert ws(partition_size=48) == expect
+    # more than 16 partitions per sequence: a second merge level. 32
+    # partitions of 16 tokens -> groups of F = 16, 2 group pieces per
+    # (sequence, query head) after the partition pieces, 2 more counters per
+    # (sequence, KV head)
+    rows = 2 * 2 * (32 + 2) * 4
+    assert ws(partition_size=16) == up(2 * 2 * 3 * 4) + up(rows * 128 * 4) + up(rows * 4)
+    # 16 partitions: one level
+    rows = 2 * 2 * 16 * 4
+    assert ws(partition_size=32) == up(2 * 2 * 4) + up(rows * 128 * 4) + up(rows * 4)
+    # 8192 partitions: F = 91 (90 * 90 < 8192 <= 91 * 91), 91 groups
+    rows = 1 * 1 * (8192 + 91) * 8
+    assert ws(batch=1, num_q_heads=8, num_kv_heads=1, max_blocks_per_seq=8192,
+              partition_size=16) == up(1 * 1 * 92 * 4) + up(rows * 128 * 4) + up(rows * 4)
     assert lib.pa_decode_workspace_bytes(None) == 0
     assert ws(head_dim=100) == 0
 
@@ -221,8 +234,10 @@ def test_multi_token_workspace_size_arithmetic():
     expect = up(b * hkv * chunks * 4) + up(b * hkv * p * rows * d * 4) + up(b * hkv * p * rows * 4)
     assert ws(8, batch=b, num_q_heads=28, num_kv_heads=hkv, max_blocks_per_seq=256,
               partition_size=512) == expect
-    # G=16, T=16: 256 rows, 8 chunks; one partition of 16 tokens per block
-    expect = up(2 * 1 * 8 * 4) + up(2 * 1 * 32 * 256 * 64 * 4) + up(2 * 1 * 32 * 256 * 4)
+    # G=16, T=16: 256 rows, 8 chunks; one partition of 16 tokens per block:
+    # 32 partitions, so two merge levels with groups of 16 (2 group slots
+    # after the 32 partition slots, 2 more counters per chunk)
+    expect = up(2 * 1 * 3 * 8 * 4) + up(2 * 1 * 34 * 256 * 64 * 4) + up(2 * 1 * 34 * 256 * 4)
     assert ws(16, batch=2, num_q_heads=16, num_kv_heads=1, head_dim=64,
               partition_size=16) == expect
     # one new token: the same rows as decode, one counter per (sequence, KV head)

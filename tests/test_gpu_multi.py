@@ -96,6 +96,28 @@ def test_partitions_some_rows_cannot_see(ps):
     assert np.abs(lse.cpu().numpy()[fin] - rlse[fin]).max() <= 2e-3
 
 
+@pytest.mark.parametrize("T", [2, 4, 8])
+def test_two_level_merge(T):
+    # 16-token partitions, up to 66 per sequence: groups of 16 partitions
+    # merge first, then the groups. G = 4: T = 2 and 4 run on the decode
+    # kernels, T = 8 (32 rows) on the multi-token kernel. At 1025 and 257
+    # tokens the last group is one partition holding only the last position,
+    # which no new token but the last may see; at 7 tokens the first new
+    # tokens see nothing at all.
+    spec = spec_of(f"mq_tree_T{T}", "bf16", "bf16", 128, [1025, 1056, 272, 257, 7], ps=16,
+                   seed=20 + T)
+    print(f"case {spec.name}", flush=True)
+    wl = W.make_workload(spec)
+    q = W.multi_query(wl, T)
+    out, lse = run_multi(wl, q, lse=True)
+    exp, rlse = ref_multi(wl, q, lse=True)
+    check(wl, to_f64(out), exp, label=spec.name)
+    l = lse.cpu().numpy().astype(np.float64)
+    assert np.array_equal(np.isneginf(l), np.isneginf(rlse))
+    fin = np.isfinite(rlse)
+    assert np.abs(l[fin] - rlse[fin]).max() <= 2e-3
+
+
 def test_one_new_token_equals_decode():
     spec = spec_of("mq_t1", "f16", "f16", 128, [1, 40, 513, 2000], ps=512, seed=4)
     wl = W.make_workload(spec)

@@ -120,6 +120,37 @@ def test_partition_sizes(ps):
     check(wl, to_f64(run(wl, partition_size=ps)), ref(wl), label=f"ps{ps}")
 
 
+@pytest.mark.parametrize("io,kv", [("f32", "f32"), ("f16", "f16"), ("bf16", "bf16"),
+                                   ("f16", "fp8_e4m3")])
+def test_two_level_merge(io, kv):
+    """More than 16 partitions per sequence: groups of F partitions merge
+    first, then the groups (140 partitions of 16 tokens at most here, so
+    F = 16 and up to 9 groups). The lengths give eight full groups and a
+    partial one (2240 tokens), a group of a single partition (257: 17
+    partitions), exactly one level (256: 16 partitions), four groups (1000)
+    and a short sequence."""
+    spec = W.Spec(f"tree_{io}_{kv}", 5, 8, 2, 128, io, kv, ("fixed", [2240, 257, 256, 1000, 33]),
+                  140, ("ratio", 1.2), 16, 0, 41)
+    print(f"case {spec.name}", flush=True)
+    wl = W.make_workload(spec)
+    t = to_device(wl)
+    out, lse = run(wl, t, lse=True)
+    exp_out, exp_lse = ref(wl, lse=True)
+    got = to_f64(out)
+    check(wl, got, exp_out, label=spec.name)
+    lerr = np.abs(lse.cpu().double().numpy() - exp_lse).max()
+    print(f"  lse max-abs {lerr:.3e}", flush=True)
+    assert lerr <= 5e-3
+    # a second call on the same workspace finds the counters of both levels zero
+    ws = torch.zeros(pkd.workspace_bytes(t["q"], t["k_cache"], t["block_table"], 16),
+                     dtype=torch.uint8, device="cuda")
+    a = to_f64(run(wl, t, partition_size=16, workspace=ws))
+    b = to_f64(run(wl, t, partition_size=16, workspace=ws))
+    assert np.array_equal(a, b) and np.array_equal(a, got)
+    counters = ws[: 4 * 5 * 2 * (1 + 9)].view(torch.int32)
+    assert int(counters.abs().sum()) == 0
+
+
 # ------------------------------------------------------ full-size workloads
 
 
