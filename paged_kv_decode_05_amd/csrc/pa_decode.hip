@@ -106,122 +106,179 @@ struct Smem {
   int b0, pre0;       // balanced split: sequence holding the share's start
 };
 
-// Merge the nparts pieces of (b, g) stored in workspace slots slot0 ...
-// slot0 + nparts - 1 (partitions, first-level groups of partitions, or shares
-// of the balanced split) and write the final output of its query heads, or,
-// when dst >= 0, the merged piece (normalised output and base-2 log-sum-exp,
-// like any other piece) to workspace slot dst. Threads take (head, 4-float quad)
-// pairs; when the group leaves threads over, S slices split the pieces (slice
-// s takes p = s, s + S, ...). Every thread issues the loads of 8 partitions before
-// folding them with a running max, and slices are combined in order 0, 1, ...,
-// so the result does not depend on which workgroup finished last.
-// red: LDS scratch of at least kMergeScratch floats.
-constexpr int kMergeScratch = 6 * kThreads;
-// MQ: a piece may hold nothing a row can see (lse = -inf, skipped; a row
-// with nothing in any piece gets 0 and -inf) and NaN is tracked explicitly;
-// pieces are not sliced.
-template <typename IO, int D, bool MQ>
-__device__ __forceinline__ void merge_partitions(const Params& a, float* red, int b, int g, size_t slot0, int nparts,
-                                                 long long dst = -1) {
+// One merge: the np pieces of pair (b, g) held in workspace slots slot0 ..
+// slot0 + np - 1 (partitions, first-level groups of partitions, or pieces of
+// the balanced split), folded into the final output of the pair's query rows
+// (dst < 0) or into one piece (normalised output and base-2 log-sum-exp,
+// like any other piece) in workspace slot dst.
+struct MergeJob {
+  int b, g, np;
+  size_t slot0;
+  long long dst;
+};
+
+constexpr int kMergeBatch = 8;                 // piece loads in flight per item
+constexpr int kMergeScratch = 12 * kThreads;   // floats: slice results of 2 * kThreads items
+
+// Run m merges (job j = jobs(j), all with a.group rows per pair). Threads take
+// (job, slice, row, 4-float quad) items two at a time and issue the loads of
+// up to kMergeBatch pieces of both before folding either, so two jobs, or the
+// two halves of a job with more items than threads, cost one memory round
+// trip rather than two. A job's items fill whole waves (its item count
+// rounded up to 64), so the job, and with it the base of the buffer resource
+// its loads use, is uniform across a wave. When a job has more pieces than
+// one batch and threads are left over, S slices split its pieces (slice s
+// takes pieces s, s + S, ...) and are combined in order 0, 1, ... through
+// LDS; within a slice pieces are folded in slot order, so the result does not
+// depend on which workgroup merges. A piece a row sees nothing of (lse =
+// -inf) adds nothing, a row with nothing in any piece gets out = 0 and lse =
+// -inf, and a NaN piece makes the row NaN. red: LDS scratch of kMergeScratch
+// floats. Control flow is uniform across the workgroup.
+template <typename IO, int D, typename Jobs>
+__device__ __forceinline__ void merge_jobs(const Params& a, float* red, int m, int np_max, Jobs jobs) {
   constexpr int kQuads = D / 4;
-  constexpr int kBatch = 8;
   const int tid = threadIdx.x;
   const int npair = a.group * kQuads;
-  const int S = (MQ || npair >= kThreads) ? 1 : kThreads / npair;
+  const int npad = (npair + 63) & ~63;
+  int S = 1;
+  while (S < 8 && S * kMergeBatch < np_max && m * 2 * S * npad <= 2 * kThreads) S *= 2;
+  const int per_job = S * npad;
+  const int total = m * per_job;
   const size_t slot_floats = (size_t)a.group * D;
-  for (int base = 0; base < npair * S; base += kThreads) {
-    const int idx = base + tid;
-    const bool active = idx < npair * S;
-    const int pair = idx % npair, sl = idx / npair;
-    const int h = pair / kQuads, dq = pair % kQuads;
-    size_t row;
-    if constexpr (MQ) row = mq_row<MQ>(a, b, g, h);
-    else row = (size_t)b * a.num_q_heads + g * a.group + h;
-    const float* lse = a.ws_lse + slot0 * a.group + h;
-    float mr = -INFINITY, wr = 0.f;
-    bool nan = false;
-    f32x4 ar = {0.f, 0.f, 0.f, 0.f};
-    // batches of kBatch * S slots, each read through a resource based at the
-    // batch's first slot (offsets stay small whatever nparts is)
-    for (int p0 = 0; p0 < nparts; p0 += kBatch * S) {
-      const int nb = min(kBatch * S, nparts - p0);
-      const brsrc r = buffer_rsrc(a.ws_o + (slot0 + p0) * slot_floats,
-                                  (uint32_t)(nb * slot_floats * sizeof(float)));
-      float lp[kBatch];
-      f32x4 ov[kBatch];
+  for (int base = 0; base < total; base += 2 * kThreads) {
+    MergeJob J[2];
+    int sl[2], h[2], dq[2], cnt[2];
+    bool on[2], nan[2];
+    float mr[2], wr[2];
+    f32x4 ar[2];
 #pragma unroll
-      for (int u = 0; u < kBatch; ++u) {
-        const int q = sl + u * S;   // slot within the batch
-        if (active && q < nb) {
-          lp[u] = ld_agent(lse + (size_t)(p0 + q) * a.group);
-          ov[u] = ld_agent4(r, (uint32_t)((q * slot_floats + h * D + 4 * dq) * sizeof(float)));
+    for (int u = 0; u < 2; ++u) {
+      const int idx = base + u * kThreads + tid;
+      // uniform across the wave: per_job and npad are multiples of 64
+      const int j = __builtin_amdgcn_readfirstlane(idx / per_job);
+      const int rem = idx - j * per_job;
+      sl[u] = __builtin_amdgcn_readfirstlane(rem / npad);
+      const int pair = rem - sl[u] * npad;
+      on[u] = j < m && pair < npair;
+      J[u] = jobs(j < m ? j : m - 1);
+      cnt[u] = j < m && J[u].np > sl[u] ? (J[u].np - sl[u] + S - 1) / S : 0;   // pieces of the slice
+      h[u] = pair / kQuads;
+      dq[u] = pair - h[u] * kQuads;
+      nan[u] = false;
+      mr[u] = -INFINITY;
+      wr[u] = 0.f;
+      ar[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    const int nmax = max(cnt[0], cnt[1]);
+    for (int i0 = 0; i0 < nmax; i0 += kMergeBatch) {
+      float lp[2][kMergeBatch];
+      f32x4 ov[2][kMergeBatch];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        if (i0 < cnt[u]) {   // uniform
+          const int nb = min(kMergeBatch, cnt[u] - i0);
+          const size_t s0 = J[u].slot0 + sl[u] + (size_t)S * i0;   // first slot of the batch
+          const uint32_t nslots = (uint32_t)((nb - 1) * S + 1);
+          const brsrc ro = buffer_rsrc(a.ws_o + s0 * slot_floats, (uint32_t)(nslots * slot_floats * sizeof(float)));
+          const brsrc rl = buffer_rsrc(a.ws_lse + s0 * a.group, (uint32_t)(nslots * a.group * sizeof(float)));
+          const uint32_t vo = (uint32_t)((h[u] * D + 4 * dq[u]) * sizeof(float));
+          const uint32_t vl = (uint32_t)(h[u] * sizeof(float));
+#pragma unroll
+          for (int q = 0; q < kMergeBatch; ++q) {
+            if (on[u] && q < nb) {
+              lp[u][q] = ld_agent1(rl, vl, (uint32_t)(q * S * a.group * sizeof(float)));
+              ov[u][q] = ld_agent4(ro, vo, (uint32_t)(q * S * slot_floats * sizeof(float)));
+            }
+          }
         }
       }
 #pragma unroll
-      for (int u = 0; u < kBatch; ++u) {
-        if (active && sl + u * S < nb) {
-          if constexpr (MQ) {
-            if (lp[u] != lp[u]) nan = true;
-            if (!(lp[u] > -INFINITY)) continue;
+      for (int u = 0; u < 2; ++u) {
+#pragma unroll
+        for (int q = 0; q < kMergeBatch; ++q) {
+          if (on[u] && i0 + q < cnt[u]) {
+            const float l = lp[u][q];
+            if (l != l) {
+              nan[u] = true;
+            } else if (l > -INFINITY) {
+              const float mn = fmaxf(mr[u], l);
+              const float sa = exp2_fast(mr[u] - mn), sb = exp2_fast(l - mn);
+              ar[u] = ar[u] * sa + ov[u][q] * sb;
+              wr[u] = wr[u] * sa + sb;
+              mr[u] = mn;
+            }
           }
-          const float mn = fmaxf(mr, lp[u]);
-          const float sa = exp2_fast(mr - mn), sb = exp2_fast(lp[u] - mn);
-          ar = ar * sa + ov[u] * sb;
-          wr = wr * sa + sb;
-          mr = mn;
         }
       }
     }
     if (S > 1) {
-      // npair * S <= kThreads: one pass, every thread is here.
-      // red: [S][npair] quads, then m, then w
-      float* redm = red + 4 * npair * S;
-      float* redw = redm + npair * S;
-      if (active) {
-        *reinterpret_cast<f32x4*>(&red[4 * idx]) = ar;
-        redm[idx] = mr;
-        redw[idx] = wr;
+      // one round (total <= 2 * kThreads): slice results through LDS, then
+      // the slice-0 items combine the slices in order. red: [2 * kThreads]
+      // float4s, then m, then w (NaN for a slice that met a NaN piece).
+      float* redm = red + 8 * kThreads;
+      float* redw = redm + 2 * kThreads;
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int idx = u * kThreads + tid;
+        if (on[u]) {
+          *reinterpret_cast<f32x4*>(&red[4 * idx]) = ar[u];
+          redm[idx] = mr[u];
+          redw[idx] = nan[u] ? __builtin_nanf("") : wr[u];
+        }
       }
       __syncthreads();
-      if (active && sl == 0) {
-        float M = -INFINITY;
-        for (int s2 = 0; s2 < S; ++s2) M = fmaxf(M, redm[s2 * npair + pair]);
-        float W = 0.f;
-        f32x4 A = {0.f, 0.f, 0.f, 0.f};
-        for (int s2 = 0; s2 < S; ++s2) {
-          const int j = s2 * npair + pair;
-          const float e = exp2_fast(redm[j] - M);
-          W += e * redw[j];
-          A += e * *reinterpret_cast<const f32x4*>(&red[4 * j]);
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int idx = u * kThreads + tid;
+        if (on[u] && sl[u] == 0) {
+          float M = -INFINITY;
+          for (int s2 = 0; s2 < S; ++s2) M = fmaxf(M, redm[idx + s2 * npad]);
+          const float Ms = M == -INFINITY ? 0.f : M;
+          float W = 0.f;
+          f32x4 A = {0.f, 0.f, 0.f, 0.f};
+          for (int s2 = 0; s2 < S; ++s2) {
+            const int k = idx + s2 * npad;
+            const float e = exp2_fast(redm[k] - Ms);
+            W += e * redw[k];
+            A += e * *reinterpret_cast<const f32x4*>(&red[4 * k]);
+          }
+          mr[u] = M;
+          wr[u] = W;
+          ar[u] = A;
+          nan[u] = W != W;
         }
-        mr = M;
-        wr = W;
-        ar = A;
       }
     }
-    if (active && sl == 0) {
-      // base-2 log-sum-exp of the merged piece; a NaN piece makes ar, wr NaN
-      f32x4 val = {ar[0] / wr, ar[1] / wr, ar[2] / wr, ar[3] / wr};
-      float lse2 = mr + log2_fast(wr);
-      if constexpr (MQ) {
-        if (nan) {
-          val = f32x4{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
-          lse2 = __builtin_nanf("");
-        } else if (!(wr > 0.f)) {
-          val = f32x4{0.f, 0.f, 0.f, 0.f};
-          lse2 = -INFINITY;
-        }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      if (!on[u] || sl[u] != 0) continue;
+      f32x4 val = {0.f, 0.f, 0.f, 0.f};
+      float lse2 = -INFINITY;   // base 2
+      if (nan[u]) {
+        val = f32x4{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
+        lse2 = __builtin_nanf("");
+      } else if (wr[u] > 0.f) {
+        val = ar[u] * __builtin_amdgcn_rcpf(wr[u]);
+        lse2 = mr[u] + log2_fast(wr[u]);
       }
-      if (dst < 0) {
-        store_out4<IO>(a.out, row * D + 4 * dq, val);
-        if (dq == 0 && a.lse_out) a.lse_out[row] = lse2 * kLn2;
+      if (J[u].dst < 0) {
+        const size_t row = mq_row<true>(a, J[u].b, J[u].g, h[u]);
+        store_out4<IO>(a.out, row * D + 4 * dq[u], val);
+        if (dq[u] == 0 && a.lse_out) a.lse_out[row] = lse2 * kLn2;
       } else {
-        const brsrc wd = buffer_rsrc(a.ws_o + (size_t)dst * slot_floats, (uint32_t)(slot_floats * sizeof(float)));
-        st_agent4(wd, (uint32_t)((h * D + 4 * dq) * sizeof(float)), val);
-        if (dq == 0) st_agent(a.ws_lse + (size_t)dst * a.group + h, lse2);
+        const size_t dst = (size_t)J[u].dst;
+        const brsrc wd = buffer_rsrc(a.ws_o + dst * slot_floats, (uint32_t)(slot_floats * sizeof(float)));
+        st_agent4(wd, (uint32_t)((h[u] * D + 4 * dq[u]) * sizeof(float)), val);
+        if (dq[u] == 0) st_agent(a.ws_lse + dst * a.group + h[u], lse2);
       }
     }
   }
+}
+
+// The single merge of one pair.
+template <typename IO, int D>
+__device__ __forceinline__ void merge_one(const Params& a, float* red, const MergeJob& job) {
+  merge_jobs<IO, D>(a, red, 1, job.np, [&](int) { return job; });
 }
 
 // ---------------------------------------------------------------------------
@@ -478,7 +535,7 @@ __device__ __forceinline__ void decode_piece(const Params& a, Smem<D>& sm, const
       W += e * sm.l[ww][h];
       o += e * *reinterpret_cast<const f32x4*>(&sm.acc[ww][h][d]);
     }
-    f32x4 val = {o[0] / W * vmul, o[1] / W * vmul, o[2] / W * vmul, o[3] / W * vmul};
+    f32x4 val = o * (__builtin_amdgcn_rcpf(W) * vmul);
     float lse2 = M + log2_fast(W);
     if constexpr (MQ) {
       if (!(W > 0.f)) {
@@ -521,11 +578,11 @@ __device__ __forceinline__ void decode_piece(const Params& a, Smem<D>& sm, const
     const int gn = min(a.fan, pc.nparts - gfirst);
     first = nbg * a.p_max + bg * a.g_max;   // the group slots of (b, g)
     if (!last_to_finish(a.ws_cnt + nbg + bg * a.g_max + grp, gn, &sm.last)) return;
-    merge_partitions<IO, D, MQ>(a, red, b, g, (size_t)pc.slot0 + gfirst, gn, (long long)(first + grp));
+    merge_one<IO, D>(a, red, MergeJob{b, g, gn, (size_t)pc.slot0 + gfirst, (long long)(first + grp)});
     np = (pc.nparts + a.fan - 1) / a.fan;
   }
   if (!last_to_finish(a.ws_cnt + bg, np, &sm.last)) return;
-  merge_partitions<IO, D, MQ>(a, red, b, g, first, np);
+  merge_one<IO, D>(a, red, MergeJob{b, g, np, first, -1});
 }
 
 // Fixed schedule: one workgroup per (sequence b, KV head g, partition p) unit
@@ -599,14 +656,21 @@ constexpr int kMetaNear = 128;     // MQ: one of the sequence's last two pages
 constexpr int kMetaPfeShift = 24;  // MQ: bit 24 set for the second-to-last page
 
 // Dynamic LDS of the balanced kernel, sized by group G, head_dim D, batch B.
-// Pieces of one share that go through the LDS merge, at most: the share's
-// first and last piece and one piece across each of the three quarter
-// boundaries.
-constexpr int kMaxSplit = 8;
+// Each wave has two slots for pieces that go through the LDS merge: slot 0
+// for the piece its quarter starts with (the pair began at or before the
+// quarter), slot 1 for the piece it ends with (the pair goes on past it).
 
 struct BalLayout {
-  uint32_t acc, m, l, bad, red, len, pre, misc, split, total;   // byte offsets
+  uint32_t acc, m, l, bad, pm, red, len, pre, misc, split, total;   // byte offsets
 };
+// Per (wave, slot), recorded when the wave flushes the piece it holds: the
+// pair's sequence and KV head, its end line position, the output multiplier
+// (v_scale, as float bits), its pieces over the shares (count, this share's
+// index among them, workspace slot of the first) and flags (in use; the slot
+// leads the piece, i.e. no earlier wave of the share holds the pair).
+constexpr int kPmB = 0, kPmG = 1, kPmEnd = 2, kPmVmul = 3, kPmParts = 4, kPmK = 5, kPmSlot0 = 6, kPmFlags = 7;
+constexpr int kPieceMeta = 8;
+constexpr int kPmUsed = 1, kPmLead = 2;
 __host__ __device__ inline uint32_t lds_align(uint32_t x) { return (x + 15u) & ~15u; }
 __host__ __device__ inline BalLayout bal_layout(int G, int D, int B) {
   BalLayout o;
@@ -615,11 +679,12 @@ __host__ __device__ inline BalLayout bal_layout(int G, int D, int B) {
   o.m = p;    p = lds_align(p + 4u * kWaves * 2 * G);             // [kWaves][2][G]
   o.l = p;    p = lds_align(p + 4u * kWaves * 2 * G);
   o.bad = p;  p = lds_align(p + 4u * kWaves * 2);                 // [kWaves][2]
+  o.pm = p;   p = lds_align(p + 4u * kWaves * 2 * kPieceMeta);    // [kWaves][2][kPieceMeta]
   o.red = p;  p = lds_align(p + 4u * kMergeScratch);
   o.len = p;  p = lds_align(p + 4u * B);                          // [B]
   o.pre = p;  p = lds_align(p + 4u * (B + 1));                    // [B + 1]
   o.misc = p; p = lds_align(p + 4u * kWaves);                     // wsum[kWaves]
-  o.split = p; p = lds_align(p + 4u * 5 * kMaxSplit);             // split pieces, their flags
+  o.split = p; p = lds_align(p + 4u * 2 * kWaves);               // per candidate slot: "last" flag
   o.total = p;
   return o;
 }
@@ -632,11 +697,12 @@ struct BalSm {
   float* m;
   float* l;
   int* bad;
+  int* pm;
   float* red;
   int* len;
   int* pre;
   int* misc;
-  int* split;   // [kMaxSplit][4] (b, g, nparts, slot0), then [kMaxSplit] "last" flags
+  int* split;   // [2 * kWaves]: the workgroup completed the candidate slot's pair
   int G;
   __device__ BalSm(int G_, int B) : G(G_) {
     const BalLayout o = bal_layout(G_, D, B);
@@ -644,6 +710,7 @@ struct BalSm {
     m = reinterpret_cast<float*>(bal_lds + o.m);
     l = reinterpret_cast<float*>(bal_lds + o.l);
     bad = reinterpret_cast<int*>(bal_lds + o.bad);
+    pm = reinterpret_cast<int*>(bal_lds + o.pm);
     red = reinterpret_cast<float*>(bal_lds + o.red);
     len = reinterpret_cast<int*>(bal_lds + o.len);
     pre = reinterpret_cast<int*>(bal_lds + o.pre);
@@ -696,10 +763,15 @@ __device__ __forceinline__ void qcursor_at(QCursor& c, const Params& a, const Ba
   c.pg_hi = c.pg_lo + (min(y1, c.pair_end) - x);
 }
 
-// One wave's quarter [y0, y1) of a share.
+// The share a workgroup works on: index wg of s shares over n line positions.
+struct ShareOf {
+  int wg, n, s;
+};
+
+// One wave's quarter [y0, y1) of share sh.
 template <typename IO, typename KV, int D, bool MQ>
-__device__ __forceinline__ void decode_quarter(const Params& a, const BalSm<D>& sm, const int y0,
-                                               const int y1) {
+__device__ __forceinline__ void decode_quarter(const Params& a, const BalSm<D>& sm, const ShareOf& sh,
+                                               const int y0, const int y1) {
   using T = typename TileOf<IO, KV, D>::type;
   constexpr bool kFp8 = std::is_same<KV, FP8>::value;
   constexpr size_t kPageBytes = (size_t)kBlock * D * ElemSize<KV>::v;
@@ -887,6 +959,19 @@ __device__ __forceinline__ void decode_quarter(const Params& a, const BalSm<D>& 
       }
     } else {
       const int slot = cur.pair_first <= y0 ? 0 : 1;
+      const int s_first = share_of(cur.pair_first, sh.n, sh.s);
+      const int s_last = share_of(cur.pair_end - 1, sh.n, sh.s);
+      if (lane == 0) {
+        int* e = sm.pm + (w * 2 + slot) * kPieceMeta;
+        e[kPmB] = cur.b;
+        e[kPmG] = cur.g;
+        e[kPmEnd] = cur.pair_end;
+        e[kPmVmul] = __builtin_bit_cast(int, vmul_cur);
+        e[kPmParts] = s_last - s_first + 1;
+        e[kPmK] = sh.wg - s_first;
+        e[kPmSlot0] = s_first + cur.b * H + cur.g;
+        e[kPmFlags] = kPmUsed | (slot == 1 || w == 0 || cur.pair_first == y0 ? kPmLead : 0);
+      }
       if (head_ok) {
         float* row = sm.acc_row(w, slot, rr);
 #pragma unroll
@@ -984,77 +1069,112 @@ __device__ __forceinline__ void decode_quarter(const Params& a, const BalSm<D>& 
 // for as well).
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-// Combine the LDS slots of waves wa .. wb that hold one piece of the share
-// (pair (b, g) starting at line position pair_first) and write the output
-// (nparts == 1) or the piece's partial result (slot slot0 + k). yq(ww): the
-// quarter starts.
-template <typename IO, typename KV, int D, bool MQ, typename YQ>
-__device__ __forceinline__ void combine_slots(const Params& a, const BalSm<D>& sm, int b, int g, int pair_first,
-                              int wa, int wb, int k, int nparts, int slot0, YQ yq) {
+// Combine, for the np pieces of the share that lead in LDS (candidate slots
+// c = 2 * wave + slot in the bit mask lead, in line order), the slots of the
+// waves holding each: slot c & 1 of wave wa = c >> 1, then slot 0 of every
+// later wave of the share the pair reaches (yqv: the quarter starts). Write
+// the output of a pair whose pieces are all in this share, else the piece's
+// partial result to its workspace slot. Threads take (piece, row, 4-float
+// quad) items two at a time, a piece's items filling whole waves so that the
+// piece is uniform across a wave; the LDS reads of both items are issued
+// before any arithmetic.
+template <typename IO, typename KV, int D, bool MQ>
+__device__ __forceinline__ void combine_pieces(const Params& a, const BalSm<D>& sm, uint32_t lead, int np,
+                                               const int* yqv) {
+  constexpr int kQuads = D / 4;
   const int tid = threadIdx.x;
   const int G = a.group;
-  const int hq0 = g * G;
-  // per wave: does it hold the piece, and in which slot
-  bool on[kWaves];
-  int sl[kWaves];
-  int bad = 0;
+  const int npair = G * kQuads;
+  const int npad = (npair + 63) & ~63;
+  const int total = np * npad;
+  for (int base = 0; base < total; base += 2 * kThreads) {
+    // every LDS read of both items first (one wave per SIMD: nothing else
+    // hides their latency), then the arithmetic
+    bool on[2];
+    int c[2], h[2], d[2], bd[2][kWaves];
+    u32x4 me[2][2];
+    float mv[2][kWaves], lv[2][kWaves];
+    f32x4 av[2][kWaves];
 #pragma unroll
-  for (int ww = 0; ww < kWaves; ++ww) {
-    on[ww] = ww >= wa && ww <= wb;
-    sl[ww] = on[ww] && pair_first > yq(ww) ? 1 : 0;
-    if (on[ww]) bad |= sm.bad[ww * 2 + sl[ww]];
-  }
-  float vmul = 1.0f;
-  if constexpr (std::is_same<KV, FP8>::value) vmul = a.v_scale[g];
-  const bool split = nparts > 1;
-  const size_t slot = (size_t)slot0 + k;
-  const brsrc wr_slot = buffer_rsrc(a.ws_o + slot * G * D, (uint32_t)(G * D * sizeof(float)));
-  for (int i = tid; i < G * (D / 4); i += kThreads) {   // (head, 4-float quad)
-    const int h = i / (D / 4), d = 4 * (i - h * (D / 4));
-    float mv[kWaves], lv[kWaves];
-    f32x4 av[kWaves];
+    for (int u = 0; u < 2; ++u) {
+      const int idx = base + u * kThreads + tid;
+      const int j = __builtin_amdgcn_readfirstlane(idx / npad);   // uniform: npad % 64 == 0
+      const int pair = idx - j * npad;
+      on[u] = j < np && pair < npair;
+      // the j-th set bit of lead (the last one for items past the pieces)
+      uint32_t mk = lead;
+      for (int i = 0; i < j && i < np - 1; ++i) mk &= mk - 1;
+      c[u] = __builtin_ctz(mk);
+      h[u] = on[u] ? pair / kQuads : 0;
+      d[u] = 4 * (pair - (pair / kQuads) * kQuads);
+      const u32x4* e = reinterpret_cast<const u32x4*>(sm.pm + c[u] * kPieceMeta);
+      me[u][0] = e[0];
+      me[u][1] = e[1];
 #pragma unroll
-    for (int ww = 0; ww < kWaves; ++ww) {   // all reads first, then the arithmetic
-      mv[ww] = sm.m[sm.mi(ww, sl[ww], h)];
-      lv[ww] = sm.l[sm.mi(ww, sl[ww], h)];
-      av[ww] = *reinterpret_cast<const f32x4*>(sm.acc_row(ww, sl[ww], h) + d);
-    }
-    float M = -INFINITY;
-#pragma unroll
-    for (int ww = 0; ww < kWaves; ++ww)
-      if (on[ww]) M = fmaxf(M, mv[ww]);
-    float W = 0.f;
-    f32x4 o = {0.f, 0.f, 0.f, 0.f};
-    const float Ms = (MQ && M == -INFINITY) ? 0.f : M;   // MQ: a row may see nothing here
-#pragma unroll
-    for (int ww = 0; ww < kWaves; ++ww) {
-      if (on[ww]) {
-        const float e = exp2_fast(mv[ww] - Ms);
-        W += e * lv[ww];
-        o += e * av[ww];
+      for (int ww = 0; ww < kWaves; ++ww) {
+        const int sl = ww == (c[u] >> 1) ? (c[u] & 1) : 0;
+        bd[u][ww] = sm.bad[ww * 2 + sl];
+        mv[u][ww] = sm.m[sm.mi(ww, sl, h[u])];
+        lv[u][ww] = sm.l[sm.mi(ww, sl, h[u])];
+        av[u][ww] = *reinterpret_cast<const f32x4*>(sm.acc_row(ww, sl, h[u]) + d[u]);
       }
     }
-    f32x4 val = {o[0] / W * vmul, o[1] / W * vmul, o[2] / W * vmul, o[3] / W * vmul};
-    float lse2 = M + log2_fast(W);
-    if constexpr (MQ) {
-      if (!(W > 0.f)) {
-        val = f32x4{0.f, 0.f, 0.f, 0.f};
-        lse2 = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      if (!on[u]) continue;
+      const int wa = c[u] >> 1;
+      const int b = __builtin_amdgcn_readfirstlane((int)me[u][0][kPmB]);
+      const int g = __builtin_amdgcn_readfirstlane((int)me[u][0][kPmG]);
+      const int pend = __builtin_amdgcn_readfirstlane((int)me[u][0][kPmEnd]);
+      const float vmul = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane((int)me[u][0][kPmVmul]));
+      const int nparts = __builtin_amdgcn_readfirstlane((int)me[u][1][kPmParts - 4]);
+      bool hold[kWaves];
+      int bad = 0;
+      float M = -INFINITY;
+#pragma unroll
+      for (int ww = 0; ww < kWaves; ++ww) {
+        hold[ww] = ww == wa || (ww > wa && pend > yqv[ww]);
+        if (hold[ww]) {
+          bad |= bd[u][ww];
+          M = fmaxf(M, mv[u][ww]);
+        }
       }
-    }
-    if (bad) {
-      val = f32x4{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
-      lse2 = __builtin_nanf("");
-    }
-    size_t row;
-    if constexpr (MQ) row = mq_row<MQ>(a, b, g, h);
-    else row = (size_t)b * a.num_q_heads + hq0 + h;
-    if (!split) {
-      store_out4<IO>(a.out, row * D + d, val);
-      if (d == 0 && a.lse_out) a.lse_out[row] = lse2 * kLn2;
-    } else {
-      st_agent4(wr_slot, (uint32_t)((h * D + d) * sizeof(float)), val);
-      if (d == 0) st_agent(a.ws_lse + slot * G + h, lse2);
+      float W = 0.f;
+      f32x4 o = {0.f, 0.f, 0.f, 0.f};
+      const float Ms = (MQ && M == -INFINITY) ? 0.f : M;   // MQ: a row may see nothing here
+#pragma unroll
+      for (int ww = 0; ww < kWaves; ++ww) {
+        if (hold[ww]) {
+          const float ex = exp2_fast(mv[u][ww] - Ms);
+          W += ex * lv[u][ww];
+          o += ex * av[u][ww];
+        }
+      }
+      f32x4 val = o * (__builtin_amdgcn_rcpf(W) * vmul);
+      float lse2 = M + log2_fast(W);
+      if constexpr (MQ) {
+        if (!(W > 0.f)) {
+          val = f32x4{0.f, 0.f, 0.f, 0.f};
+          lse2 = -INFINITY;
+        }
+      }
+      if (bad) {
+        val = f32x4{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
+        lse2 = __builtin_nanf("");
+      }
+      if (nparts == 1) {
+        size_t row;
+        if constexpr (MQ) row = mq_row<MQ>(a, b, g, h[u]);
+        else row = (size_t)b * a.num_q_heads + g * G + h[u];
+        store_out4<IO>(a.out, row * D + d[u], val);
+        if (d[u] == 0 && a.lse_out) a.lse_out[row] = lse2 * kLn2;
+      } else {
+        const size_t slot = (size_t)__builtin_amdgcn_readfirstlane((int)me[u][1][kPmSlot0 - 4]) +
+                            __builtin_amdgcn_readfirstlane((int)me[u][1][kPmK - 4]);
+        const brsrc wr_slot = buffer_rsrc(a.ws_o + slot * G * D, (uint32_t)(G * D * sizeof(float)));
+        st_agent4(wr_slot, (uint32_t)((h[u] * D + d[u]) * sizeof(float)), val);
+        if (d[u] == 0) st_agent(a.ws_lse + slot * G + h[u], lse2);
+      }
     }
   }
 }
@@ -1067,6 +1187,11 @@ pa_decode_balanced_kernel(const Params a) {
   const int w = tid >> 6;
   const int B = a.batch, H = a.num_kv_heads, mbs = a.max_blocks_per_seq;
   const BalSm<D> sm(a.group, B);
+  // this wave's piece slots start unused (their use is recorded when flushed)
+  if (lane == 0) {
+    sm.pm[(w * 2) * kPieceMeta + kPmFlags] = 0;
+    sm.pm[(w * 2 + 1) * kPieceMeta + kPmFlags] = 0;
+  }
 
   // lengths of this thread's sequences [bbeg, bbeg + per) into LDS, and the
   // exclusive prefix sums of their line positions
@@ -1115,62 +1240,55 @@ pa_decode_balanced_kernel(const Params a) {
   // this wave's quarter of the share
   const int wu = __builtin_amdgcn_readfirstlane(w);
   auto yq = [&](int ww) { return x0 + share_start(ww, x1 - x0, kWaves); };
-  decode_quarter<IO, KV, D, MQ>(a, sm, yq(wu), yq(wu + 1));
+  decode_quarter<IO, KV, D, MQ>(a, sm, ShareOf{wg, N, S}, yq(wu), yq(wu + 1));
   __syncthreads();
 
   // Pieces of the share whose state went through LDS, in three steps:
-  // 1. combine each one's wave slots; write the output of whole pairs and the
-  //    partial result of split ones (remembered in LDS);
+  // 1. combine each one's wave slots (all pieces in one pass); write the
+  //    output of whole pairs and the partial result of split ones;
   // 2. once those stores are complete, count every split piece in on its
-  //    pair's counter (one thread per piece, all at once);
-  // 3. merge the pairs whose count this workgroup completed.
-  const int b0 = seq_of_uniform(sm.pre, B, H, x0);
-  const int pre0 = __builtin_amdgcn_readfirstlane(sm.pre[b0]);
-  int nsplit = 0;
-  walk_share(
-      wg, x0, x1, b0, pre0, B, H, N, S, mbs,
-      [&](int bb) { return __builtin_amdgcn_readfirstlane(sm.len[bb]); },
-      [&](int bb, int L, const LinePiece& lp) {
-        const int cb = line_pages(L, mbs);
-        const int s0 = lp.x_end - (lp.pg_hi - lp.pg_lo);
-        const int pair_first = s0 - lp.pg_lo;
-        const int pair_end = pair_first + cb;
-        const int wa = share_of(s0 - x0, x1 - x0, kWaves);
-        const int wb = share_of(lp.x_end - 1 - x0, x1 - x0, kWaves);
-        if (wa == wb && pair_first >= yq(wa) && pair_end <= yq(wa + 1)) return;   // written by wave wa
-        combine_slots<IO, KV, D, MQ>(a, sm, bb, lp.g, pair_first, wa, wb, lp.k, lp.nparts, lp.slot0, yq);
-        if (lp.nparts > 1) {
-          if (tid == 0) {
-            int* e = sm.split + 4 * nsplit;
-            e[0] = bb;
-            e[1] = lp.g;
-            e[2] = lp.nparts;
-            e[3] = lp.slot0;
-          }
-          ++nsplit;
-        }
-      });
-  if (nsplit == 0) return;   // uniform
+  //    pair's counter (one lane per candidate slot, all at once);
+  // 3. merge the pairs whose count this workgroup completed, all in one pass.
+  int yqv[kWaves + 1];
+#pragma unroll
+  for (int ww = 0; ww <= kWaves; ++ww) yqv[ww] = yq(ww);
+  // candidate slots c = 2 * wave + slot: lane c reads slot c's flags
+  const int cl = lane < 2 * kWaves ? lane : 0;
+  const int fl = sm.pm[cl * kPieceMeta + kPmFlags];
+  const int parts = sm.pm[cl * kPieceMeta + kPmParts];
+  const uint32_t lead = (uint32_t)__ballot(lane < 2 * kWaves && (fl & kPmLead)) & 0xffu;
+  const uint32_t split = (uint32_t)__ballot(lane < 2 * kWaves && (fl & kPmLead) && parts > 1) & 0xffu;
+  if (lead == 0) return;   // uniform
+  combine_pieces<IO, KV, D, MQ>(a, sm, lead, __builtin_popcount(lead), yqv);
+  if (split == 0) return;   // uniform
   __builtin_amdgcn_s_waitcnt(0);   // this wave's partial stores are complete
   __syncthreads();
-  if (tid < nsplit) {
-    const int* e = sm.split + 4 * tid;
-    uint32_t* cnt = a.ws_cnt + (size_t)e[0] * H + e[1];
+  if (tid < 2 * kWaves && ((split >> tid) & 1u)) {
+    const int* e = sm.pm + tid * kPieceMeta;
+    uint32_t* cnt = a.ws_cnt + (size_t)e[kPmB] * H + e[kPmG];
     const uint32_t done = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    sm.split[4 * kMaxSplit + tid] = done == (uint32_t)(e[2] - 1);
+    const bool last = done == (uint32_t)(e[kPmParts] - 1);
+    sm.split[tid] = last;
+    // this workgroup completes the pair: its counter is free for the next call
+    if (last) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   lds_barrier();
-  for (int i = 0; i < nsplit; ++i) {
-    if (!__builtin_amdgcn_readfirstlane(sm.split[4 * kMaxSplit + i])) continue;   // uniform
-    const int bb = __builtin_amdgcn_readfirstlane(sm.split[4 * i]);
-    const int g = __builtin_amdgcn_readfirstlane(sm.split[4 * i + 1]);
-    const int np = __builtin_amdgcn_readfirstlane(sm.split[4 * i + 2]);
-    const int slot0 = __builtin_amdgcn_readfirstlane(sm.split[4 * i + 3]);
-    merge_partitions<IO, D, MQ>(a, sm.red, bb, g, slot0, np);
-    if (tid == 0)
-      __hip_atomic_store(a.ws_cnt + (size_t)bb * H + g, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    lds_barrier();   // the merge scratch is reused by the next pair
-  }
+  // the pairs this workgroup completes, all merged in one pass
+  const uint32_t done = (uint32_t)__ballot(((split >> cl) & 1u) && lane < 2 * kWaves && sm.split[cl]) & 0xffu;
+  int npm = 0;
+  for (uint32_t mk = done; mk; mk &= mk - 1)
+    npm = max(npm, __builtin_amdgcn_readlane(parts, __builtin_ctz(mk)));
+  if (done == 0) return;   // uniform
+  const int m = __builtin_popcount(done);
+  merge_jobs<IO, D>(a, sm.red, m, npm, [&](int j) {
+    uint32_t mk = done;   // the j-th completed pair
+    for (int i = 0; i < j && i < m - 1; ++i) mk &= mk - 1;
+    const int* e = sm.pm + __builtin_ctz(mk) * kPieceMeta;
+    const int bb = __builtin_amdgcn_readfirstlane(e[kPmB]);
+    const int g = __builtin_amdgcn_readfirstlane(e[kPmG]);
+    return MergeJob{bb, g, __builtin_amdgcn_readfirstlane(e[kPmParts]),
+                    (size_t)__builtin_amdgcn_readfirstlane(e[kPmSlot0]), -1};
+  });
 }
 
 __global__ void fill_zero_kernel(uint8_t* p, size_t n) {

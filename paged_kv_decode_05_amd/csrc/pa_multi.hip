@@ -82,65 +82,94 @@ struct Params {
 // Merge the n pieces of rows row0 .. row0 + rows_c - 1 of (b, g) stored in
 // workspace slots slot0 .. slot0 + n - 1 (partitions, or first-level groups
 // of partitions) in slot order, and write the final output of those rows
-// (dst < 0) or the merged piece to workspace slot dst. Every thread issues
-// the loads of kBatch pieces before folding them with a running max. A piece
-// a row sees nothing of (lse = -inf) adds nothing; a row that sees nothing in
-// any piece gets out = 0 and lse = -inf; NaN in any piece gives NaN.
+// (dst < 0) or the merged piece to workspace slot dst. Threads take
+// (row, 4-float quad) items two at a time and issue the loads of kBatch
+// pieces of both before folding either (one memory round trip per batch for
+// both). A piece a row sees nothing of (lse = -inf) adds nothing; a row that
+// sees nothing in any piece gets out = 0 and lse = -inf; NaN in any piece
+// gives NaN.
 template <typename IO, int D>
 __device__ __forceinline__ void merge_rows(const Params& a, int b, int g, int row0, int rows_c,
                                            size_t slot0, int n, long long dst) {
   constexpr int kBatch = 8;
   const int R = a.rows, G = a.group;
-  for (int i = threadIdx.x; i < rows_c * (D / 4); i += kThreads) {
-    const int r2 = i / (D / 4), d = 4 * (i - r2 * (D / 4));
-    const int rho = row0 + r2;
-    float mr = -INFINITY, wr = 0.f;
-    f32x4 ar = {0.f, 0.f, 0.f, 0.f};
-    bool nan = false;
+  const int items = rows_c * (D / 4);
+  for (int base = 0; base < items; base += 2 * kThreads) {
+    int rho[2], d[2];
+    bool on[2], nan[2];
+    float mr[2], wr[2];
+    f32x4 ar[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int i = base + u * kThreads + threadIdx.x;
+      on[u] = i < items;
+      const int r2 = i / (D / 4);
+      d[u] = 4 * (i - r2 * (D / 4));
+      rho[u] = on[u] ? row0 + r2 : row0;
+      nan[u] = false;
+      mr[u] = -INFINITY;
+      wr[u] = 0.f;
+      ar[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
     for (int q0 = 0; q0 < n; q0 += kBatch) {
       const int nb = min(kBatch, n - q0);
-      const brsrc r = buffer_rsrc(a.ws_o + (slot0 + q0) * R * D, (uint32_t)(nb * R * D * sizeof(float)));
-      float lp[kBatch];
-      f32x4 ov[kBatch];
+      const brsrc ro = buffer_rsrc(a.ws_o + (slot0 + q0) * R * D, (uint32_t)(nb * R * D * sizeof(float)));
+      const brsrc rl = buffer_rsrc(a.ws_lse + (slot0 + q0) * R, (uint32_t)(nb * R * sizeof(float)));
+      float lp[2][kBatch];
+      f32x4 ov[2][kBatch];
 #pragma unroll
-      for (int u = 0; u < kBatch; ++u) {
-        if (u < nb) {
-          lp[u] = ld_agent(a.ws_lse + (slot0 + q0 + u) * R + rho);
-          ov[u] = ld_agent4(r, (uint32_t)((((size_t)u * R + rho) * D + d) * sizeof(float)));
+      for (int u = 0; u < 2; ++u) {
+        const uint32_t vo = (uint32_t)(((size_t)rho[u] * D + d[u]) * sizeof(float));
+        const uint32_t vl = (uint32_t)(rho[u] * sizeof(float));
+#pragma unroll
+        for (int q = 0; q < kBatch; ++q) {
+          if (on[u] && q < nb) {
+            lp[u][q] = ld_agent1(rl, vl, (uint32_t)(q * R * sizeof(float)));
+            ov[u][q] = ld_agent4(ro, vo, (uint32_t)((size_t)q * R * D * sizeof(float)));
+          }
         }
       }
 #pragma unroll
-      for (int u = 0; u < kBatch; ++u) {
-        if (u < nb) {
-          if (lp[u] != lp[u]) nan = true;
-          if (lp[u] > -INFINITY) {
-            const float mn = fmaxf(mr, lp[u]);
-            const float sa = exp2_fast(mr - mn), sb = exp2_fast(lp[u] - mn);
-            ar = ar * sa + ov[u] * sb;
-            wr = wr * sa + sb;
-            mr = mn;
+      for (int u = 0; u < 2; ++u) {
+#pragma unroll
+        for (int q = 0; q < kBatch; ++q) {
+          if (on[u] && q < nb) {
+            const float l = lp[u][q];
+            if (l != l) {
+              nan[u] = true;
+            } else if (l > -INFINITY) {
+              const float mn = fmaxf(mr[u], l);
+              const float sa = exp2_fast(mr[u] - mn), sb = exp2_fast(l - mn);
+              ar[u] = ar[u] * sa + ov[u][q] * sb;
+              wr[u] = wr[u] * sa + sb;
+              mr[u] = mn;
+            }
           }
         }
       }
     }
-    f32x4 val = {0.f, 0.f, 0.f, 0.f};
-    float lse2 = -INFINITY;   // base 2
-    if (nan) {
-      val = f32x4{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
-      lse2 = __builtin_nanf("");
-    } else if (wr > 0.f) {
-      val = f32x4{ar[0] / wr, ar[1] / wr, ar[2] / wr, ar[3] / wr};
-      lse2 = mr + log2_fast(wr);
-    }
-    if (dst < 0) {
-      const int t = rho / G, h = rho - t * G;
-      const size_t orow = ((size_t)b * a.q_len + t) * a.num_q_heads + (size_t)g * G + h;
-      store_out4<IO>(a.out, orow * D + d, val);
-      if (d == 0 && a.lse_out) a.lse_out[orow] = lse2 * kLn2;
-    } else {
-      const brsrc wd = buffer_rsrc(a.ws_o + (size_t)dst * R * D, (uint32_t)(R * D * sizeof(float)));
-      st_agent4(wd, (uint32_t)(((size_t)rho * D + d) * sizeof(float)), val);
-      if (d == 0) st_agent(a.ws_lse + (size_t)dst * R + rho, lse2);
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      if (!on[u]) continue;
+      f32x4 val = {0.f, 0.f, 0.f, 0.f};
+      float lse2 = -INFINITY;   // base 2
+      if (nan[u]) {
+        val = f32x4{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
+        lse2 = __builtin_nanf("");
+      } else if (wr[u] > 0.f) {
+        val = ar[u] * __builtin_amdgcn_rcpf(wr[u]);
+        lse2 = mr[u] + log2_fast(wr[u]);
+      }
+      if (dst < 0) {
+        const int t = rho[u] / G, h = rho[u] - t * G;
+        const size_t orow = ((size_t)b * a.q_len + t) * a.num_q_heads + (size_t)g * G + h;
+        store_out4<IO>(a.out, orow * D + d[u], val);
+        if (d[u] == 0 && a.lse_out) a.lse_out[orow] = lse2 * kLn2;
+      } else {
+        const brsrc wd = buffer_rsrc(a.ws_o + (size_t)dst * R * D, (uint32_t)(R * D * sizeof(float)));
+        st_agent4(wd, (uint32_t)(((size_t)rho[u] * D + d[u]) * sizeof(float)), val);
+        if (d[u] == 0) st_agent(a.ws_lse + (size_t)dst * R + rho[u], lse2);
+      }
     }
   }
 }
@@ -416,7 +445,7 @@ pa_multi_kernel(const Params a) {
       f32x4 val = {0.f, 0.f, 0.f, 0.f};
       float lse2 = -INFINITY;
       if (W > 0.f) {
-        val = f32x4{o[0] / W * vmul, o[1] / W * vmul, o[2] / W * vmul, o[3] / W * vmul};
+        val = o * (__builtin_amdgcn_rcpf(W) * vmul);
         lse2 = M + log2_fast(W);
       }
       if (bad) {

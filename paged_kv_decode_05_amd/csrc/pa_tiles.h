@@ -112,6 +112,15 @@ __device__ __forceinline__ f32x4 ld_agent4(brsrc r, uint32_t off) {
 __device__ __forceinline__ void st_agent4(brsrc r, uint32_t off, f32x4 v) {
   __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, 0, kCpolSc1);
 }
+// Loads at per-lane byte offset off plus the wave-uniform byte offset soff
+// (the instruction's scalar offset field: a batch of loads shares one
+// per-lane offset register).
+__device__ __forceinline__ f32x4 ld_agent4(brsrc r, uint32_t off, uint32_t soff) {
+  return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, soff, kCpolSc1));
+}
+__device__ __forceinline__ float ld_agent1(brsrc r, uint32_t off, uint32_t soff) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, soff, kCpolSc1));
+}
 
 // Split-K hand-off: every wave waits until its agent-coherent stores have
 // completed, then one thread counts this piece on *cnt; true (uniformly) for
