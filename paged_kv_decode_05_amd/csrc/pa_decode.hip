@@ -31,7 +31,9 @@
 // through agent-coherent stores; the last workgroup of each (b, g) to finish
 // (device-scope atomic counter) reads them back with agent-coherent loads,
 // merges all partitions of that sequence in a fixed order, writes the output
-// and resets the counter to zero.
+// and resets the counter to zero. Beyond 16 partitions per sequence the merge
+// takes two levels (groups of partitions first), so that no workgroup reads
+// hundreds of partials alone.
 //
 // fp8 (OCP E4M3) caches are widened exactly to f16/bf16 with the gfx950
 // conversion instructions; k_scale folds into the score multiplier and
@@ -1232,7 +1234,11 @@ pa_decode_balanced_kernel(const Params a) {
   const int total = __builtin_amdgcn_readfirstlane(sm.pre[B]);
   const int N = total * H;
   const int S = share_count(N, (int)gridDim.x);
-  const int wg = blockIdx.x;
+  // Consecutive workgroups go to the eight XCDs in turn; numbering the shares
+  // XCD by XCD puts neighbouring shares, which split a pair between them and
+  // hand its partial results over, on the same XCD (and the same L2).
+  const int wg = gridDim.x % 8 == 0 ? (int)((blockIdx.x % 8) * (gridDim.x / 8) + blockIdx.x / 8)
+                                    : (int)blockIdx.x;
   if (wg >= S) return;   // uniform: a short line takes fewer shares
   const int x0 = share_start(wg, N, S);
   const int x1 = share_start(wg + 1, N, S);

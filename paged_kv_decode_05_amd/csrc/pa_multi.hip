@@ -14,11 +14,11 @@
 // Same building blocks and cache layouts as single-token decode. A workgroup
 // of four waves owns one (sequence b, KV head g, partition p, row chunk c)
 // unit. The query rows of a (b, g) pair are its G*T (new token, head) pairs,
-// row = t*G + h, cut into chunks of NT matrix-core column tiles of 16 rows
-// (NT = 1 or 2; a pair has ceil(G*T/16) tiles, so ceil(tiles/2) chunks: four
-// tiles of accumulators do not fit in the registers at head_dim 128). Every
-// wave keeps NT sets of accumulators, so one K/V page loaded into registers
-// feeds all NT*16 rows, and the matrix-core work per byte grows with T. The
+// row = t*G + h, cut into chunks of NT = 2 matrix-core column tiles of 16
+// rows (a pair has ceil(G*T/16) tiles, so ceil(tiles/2) chunks: four tiles of
+// accumulators do not fit in the registers at head_dim 128). Every wave keeps
+// NT sets of accumulators, so one K/V page loaded into registers feeds all
+// NT*16 rows, and the matrix-core work per byte grows with T. The
 // chunks of one (b, g, p) are launched nbg workgroups apart, which keeps them
 // on one XCD (workgroups go to the XCDs round-robin; nbg = B * Hkv is
 // usually a multiple of 8) and close in time, so the second chunk's K/V reads
@@ -32,7 +32,8 @@
 // state (the running max stays -inf, exponentials are taken against 0).
 // Waves merge through LDS one column tile at a time; split-K partials go to
 // the workspace and the last partition of each (b, g, chunk) to finish merges
-// them, as for decode. Rows with no visible token get out = 0, lse = -inf.
+// them, as for decode (two levels beyond 16 partitions). Rows with no visible
+// token get out = 0, lse = -inf.
 
 #include <hip/hip_runtime.h>
 #include <stddef.h>
@@ -48,6 +49,7 @@ namespace pa_mq {
 using namespace pa;
 
 constexpr int kMaxQLen = 16;
+constexpr int kChunkTiles = 2;   // column tiles of 16 rows per workgroup
 
 struct Params {
   const uint8_t* q;          // [B][T][Hq][D]
@@ -490,7 +492,7 @@ pa_multi_kernel(const Params a) {
 // Host side.
 // ---------------------------------------------------------------------------
 struct Plan {
-  int rows, tiles, chunks, nt, p_max, fan, g_max;
+  int rows, tiles, chunks, p_max, fan, g_max;
   size_t cnt_off, o_off, lse_off, total;
 };
 
@@ -513,8 +515,7 @@ static bool plan(const pa_shape* s, int q_len, Plan* out) {
   Plan p;
   p.rows = G * q_len;
   p.tiles = (p.rows + 15) / 16;
-  p.nt = 2;
-  p.chunks = (p.tiles + p.nt - 1) / p.nt;
+  p.chunks = (p.tiles + kChunkTiles - 1) / kChunkTiles;
   const long long tokens = (long long)s->max_blocks_per_seq * kBlock;
   p.p_max = s->partition_size ? (int)((tokens + s->partition_size - 1) / s->partition_size) : 1;
   const long long units = (long long)s->batch * s->num_kv_heads * p.chunks * p.p_max;
@@ -536,19 +537,19 @@ static bool plan(const pa_shape* s, int q_len, Plan* out) {
   return true;
 }
 
+// Two tiles per chunk: rows that fit one tile run on the decode kernels.
 template <typename IO, typename KV, int D>
-static hipError_t launch_nt(int nt, const Params& prm, dim3 grid, hipStream_t st) {
-  (void)nt;   // always 2: rows that fit one tile run on the decode kernels
+static hipError_t launch_chunks(const Params& prm, dim3 grid, hipStream_t st) {
   if (prm.chunks <= 2)
-    hipLaunchKernelGGL((pa_multi_kernel<IO, KV, D, 2, false>), grid, dim3(kThreads), 0, st, prm);
+    hipLaunchKernelGGL((pa_multi_kernel<IO, KV, D, kChunkTiles, false>), grid, dim3(kThreads), 0, st, prm);
   else
-    hipLaunchKernelGGL((pa_multi_kernel<IO, KV, D, 2, true>), grid, dim3(kThreads), 0, st, prm);
+    hipLaunchKernelGGL((pa_multi_kernel<IO, KV, D, kChunkTiles, true>), grid, dim3(kThreads), 0, st, prm);
   return hipGetLastError();
 }
 
 template <typename IO, typename KV>
-static hipError_t launch_d(int D, int nt, const Params& prm, dim3 grid, hipStream_t st) {
-  return D == 64 ? launch_nt<IO, KV, 64>(nt, prm, grid, st) : launch_nt<IO, KV, 128>(nt, prm, grid, st);
+static hipError_t launch_d(int D, const Params& prm, dim3 grid, hipStream_t st) {
+  return D == 64 ? launch_chunks<IO, KV, 64>(prm, grid, st) : launch_chunks<IO, KV, 128>(prm, grid, st);
 }
 
 static inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
@@ -633,13 +634,13 @@ pa_status pa_decode_multi(const pa_shape* shape, int32_t q_len, const void* q, c
   const int D = shape->head_dim;
   hipError_t e;
   if (io_dtype == PA_F32)
-    e = launch_d<F32, F32>(D, pl.nt, prm, grid, st);
+    e = launch_d<F32, F32>(D, prm, grid, st);
   else if (io_dtype == PA_F16)
-    e = kv_dtype == PA_FP8_E4M3 ? launch_d<F16, FP8>(D, pl.nt, prm, grid, st)
-                                : launch_d<F16, F16>(D, pl.nt, prm, grid, st);
+    e = kv_dtype == PA_FP8_E4M3 ? launch_d<F16, FP8>(D, prm, grid, st)
+                                : launch_d<F16, F16>(D, prm, grid, st);
   else
-    e = kv_dtype == PA_FP8_E4M3 ? launch_d<BF16, FP8>(D, pl.nt, prm, grid, st)
-                                : launch_d<BF16, BF16>(D, pl.nt, prm, grid, st);
+    e = kv_dtype == PA_FP8_E4M3 ? launch_d<BF16, FP8>(D, prm, grid, st)
+                                : launch_d<BF16, BF16>(D, prm, grid, st);
   return e == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
