@@ -1234,12 +1234,10 @@ pa_decode_balanced_kernel(const Params a) {
   const int total = __builtin_amdgcn_readfirstlane(sm.pre[B]);
   const int N = total * H;
   const int S = share_count(N, (int)gridDim.x);
-  // Consecutive workgroups go to the eight XCDs in turn; numbering the shares
-  // XCD by XCD puts neighbouring shares, which split a pair between them and
-  // hand its partial results over, on the same XCD (and the same L2).
-  const int wg = gridDim.x % 8 == 0 ? (int)((blockIdx.x % 8) * (gridDim.x / 8) + blockIdx.x / 8)
-                                    : (int)blockIdx.x;
-  if (wg >= S) return;   // uniform: a short line takes fewer shares
+  // shares numbered XCD by XCD (pa_schedule.h); a workgroup left without one
+  // returns
+  const int wg = share_of_block((int)blockIdx.x, (int)gridDim.x, S);
+  if (wg >= S) return;   // uniform
   const int x0 = share_start(wg, N, S);
   const int x1 = share_start(wg + 1, N, S);
 

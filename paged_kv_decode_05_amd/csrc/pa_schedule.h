@@ -57,6 +57,19 @@ __host__ __device__ inline int share_of(int x, int n, int s) {
   return floor_div((long long)(x + 1) * s - 1, n);
 }
 
+// The share workgroup blk of a grid of `grid` takes when the line has s
+// shares, or s for a workgroup left without one. Consecutive workgroups go to
+// the eight XCDs in turn, so when grid is a multiple of 8 the shares are
+// numbered XCD by XCD, ceil(s / 8) consecutive shares per XCD: neighbouring
+// shares (which split a pair between them and hand its partial results over)
+// share an XCD and its L2, and a short line still spreads over all eight.
+__host__ __device__ inline int share_of_block(int blk, int grid, int s) {
+  if (grid % 8 != 0) return blk < s ? blk : s;
+  const int per_xcd = (s + 7) / 8;
+  const int wg = blk / 8 < per_xcd ? (blk % 8) * per_xcd + blk / 8 : s;
+  return wg < s ? wg : s;
+}
+
 struct LinePiece {
   int g;        // KV head
   int pg_lo;    // first page of the piece inside the sequence

@@ -181,3 +181,10 @@ extern "C" int pa_probe_schedule(const int* lens, int B, int H, int max_blocks, 
 extern "C" void pa_probe_floor_div(const long long* a, const long long* b, int n, int* out) {
   for (int i = 0; i < n; ++i) out[i] = pa::floor_div(a[i], b[i]);
 }
+
+// Host evaluation of the balanced split's workgroup-to-share numbering
+// (pa_schedule.h): out[blk] = share_of_block(blk, grid, s) for every
+// workgroup of the grid.
+extern "C" void pa_probe_share_of_block(int grid, int s, int* out) {
+  for (int blk = 0; blk < grid; ++blk) out[blk] = pa::share_of_block(blk, grid, s);
+}

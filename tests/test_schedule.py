@@ -144,3 +144,32 @@ def test_floor_div_is_exact_integer_division(lib):
     out = np.empty(len(a), dtype=np.int32)
     lib.pa_probe_floor_div(a.ctypes.data, b.ctypes.data, len(a), out.ctypes.data)
     np.testing.assert_array_equal(out.astype(np.int64), a // b)
+
+
+def test_shares_numbered_xcd_by_xcd(lib):
+    """Workgroup blk of the balanced kernel's grid takes share
+    share_of_block(blk, grid, S): every share exactly once, neighbouring
+    shares on the same XCD (workgroups go to the 8 XCDs in turn, so XCD =
+    blk % 8) except at the boundaries between XCDs, and a short line spread
+    over all 8 XCDs."""
+    lib.pa_probe_share_of_block.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    lib.pa_probe_share_of_block.restype = None
+    for grid in (8, 16, 248, 256, 768, 1024, 7, 255):
+        for S in sorted({1, 2, 7, 8, 9, 40, 63, 64, 65, grid // 2, grid - 1, grid} - {0}):
+            if S > grid:
+                continue
+            out = np.empty(grid, dtype=np.int32)
+            lib.pa_probe_share_of_block(grid, S, out.ctypes.data)
+            taken = out[out < S]
+            assert sorted(taken.tolist()) == list(range(S)), (grid, S)
+            assert (out <= S).all()
+            if grid % 8:
+                assert (out[:S] == np.arange(S)).all()
+                continue
+            xcd = np.empty(S, dtype=np.int64)
+            xcd[taken] = np.nonzero(out < S)[0] % 8
+            per = -(-S // 8)
+            # consecutive shares share an XCD except every per-th boundary
+            same = (xcd[1:] == xcd[:-1]).sum()
+            assert same >= S - 1 - 7, (grid, S, same)
+            assert len(set(xcd.tolist())) == min(8, -(-S // per)), (grid, S)
