@@ -142,8 +142,11 @@ __device__ __forceinline__ void merge_jobs(const Params& a, float* red, int m, i
   const int tid = threadIdx.x;
   const int npair = a.group * kQuads;
   const int npad = (npair + 63) & ~63;
-  int S = 1;
-  while (S < 8 && S * kMergeBatch < np_max && m * 2 * S * npad <= 2 * kThreads) S *= 2;
+  int S = 1, sshift = 0;
+  while (S < 8 && S * kMergeBatch < np_max && m * 2 * S * npad <= 2 * kThreads) {
+    S *= 2;
+    ++sshift;
+  }
   const int per_job = S * npad;
   const int total = m * per_job;
   const size_t slot_floats = (size_t)a.group * D;
@@ -155,15 +158,24 @@ __device__ __forceinline__ void merge_jobs(const Params& a, float* red, int m, i
     f32x4 ar[2];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      const int idx = base + u * kThreads + tid;
-      // uniform across the wave: per_job and npad are multiples of 64
-      const int j = __builtin_amdgcn_readfirstlane(idx / per_job);
-      const int rem = idx - j * per_job;
-      sl[u] = __builtin_amdgcn_readfirstlane(rem / npad);
-      const int pair = rem - sl[u] * npad;
+      // the wave's first item: per_job and npad are multiples of 64, so the
+      // job and the slice are uniform across the wave (found by counting,
+      // not dividing: at most 8 jobs and 8 slices)
+      const int wbase = __builtin_amdgcn_readfirstlane(base + u * kThreads + (tid & ~63));
+      int j = 0, rem = wbase;
+      while (j < m && rem >= per_job) {
+        ++j;
+        rem -= per_job;
+      }
+      sl[u] = 0;
+      while (rem >= npad) {
+        ++sl[u];
+        rem -= npad;
+      }
+      const int pair = rem + (tid & 63);
       on[u] = j < m && pair < npair;
       J[u] = jobs(j < m ? j : m - 1);
-      cnt[u] = j < m && J[u].np > sl[u] ? (J[u].np - sl[u] + S - 1) / S : 0;   // pieces of the slice
+      cnt[u] = j < m && J[u].np > sl[u] ? (J[u].np - sl[u] + S - 1) >> sshift : 0;   // pieces of the slice
       h[u] = pair / kQuads;
       dq[u] = pair - h[u] * kQuads;
       nan[u] = false;
@@ -704,7 +716,7 @@ struct BalSm {
   int* len;
   int* pre;
   int* misc;
-  int* split;   // [2 * kWaves]: the workgroup completed the candidate slot's pair
+  int* split;   // [0]: bit c set when the workgroup completed candidate slot c's pair
   int G;
   __device__ BalSm(int G_, int B) : G(G_) {
     const BalLayout o = bal_layout(G_, D, B);
@@ -1256,10 +1268,13 @@ pa_decode_balanced_kernel(const Params a) {
   int yqv[kWaves + 1];
 #pragma unroll
   for (int ww = 0; ww <= kWaves; ++ww) yqv[ww] = yq(ww);
-  // candidate slots c = 2 * wave + slot: lane c reads slot c's flags
+  // candidate slots c = 2 * wave + slot: lane c of every wave reads slot c's
+  // record once; later steps take its fields with readlane
   const int cl = lane < 2 * kWaves ? lane : 0;
-  const int fl = sm.pm[cl * kPieceMeta + kPmFlags];
-  const int parts = sm.pm[cl * kPieceMeta + kPmParts];
+  const int* rec = sm.pm + cl * kPieceMeta;
+  const int fl = rec[kPmFlags];
+  const int parts = rec[kPmParts];
+  const int rb = rec[kPmB], rg = rec[kPmG], rs0 = rec[kPmSlot0];
   const uint32_t lead = (uint32_t)__ballot(lane < 2 * kWaves && (fl & kPmLead)) & 0xffu;
   const uint32_t split = (uint32_t)__ballot(lane < 2 * kWaves && (fl & kPmLead) && parts > 1) & 0xffu;
   if (lead == 0) return;   // uniform
@@ -1267,31 +1282,32 @@ pa_decode_balanced_kernel(const Params a) {
   if (split == 0) return;   // uniform
   __builtin_amdgcn_s_waitcnt(0);   // this wave's partial stores are complete
   __syncthreads();
-  if (tid < 2 * kWaves && ((split >> tid) & 1u)) {
-    const int* e = sm.pm + tid * kPieceMeta;
-    uint32_t* cnt = a.ws_cnt + (size_t)e[kPmB] * H + e[kPmG];
-    const uint32_t done = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const bool last = done == (uint32_t)(e[kPmParts] - 1);
-    sm.split[tid] = last;
-    // this workgroup completes the pair: its counter is free for the next call
-    if (last) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (wu == 0) {
+    bool last = false;
+    if (lane < 2 * kWaves && ((split >> lane) & 1u)) {
+      uint32_t* cnt = a.ws_cnt + (size_t)rb * H + rg;
+      const uint32_t done = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      last = done == (uint32_t)(parts - 1);
+      // this workgroup completes the pair: its counter is free for the next call
+      if (last) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    const uint32_t dm = (uint32_t)__ballot(last) & 0xffu;
+    if (lane == 0) sm.split[0] = (int)dm;
   }
   lds_barrier();
   // the pairs this workgroup completes, all merged in one pass
-  const uint32_t done = (uint32_t)__ballot(((split >> cl) & 1u) && lane < 2 * kWaves && sm.split[cl]) & 0xffu;
+  const uint32_t done = (uint32_t)__builtin_amdgcn_readfirstlane(sm.split[0]);
+  if (done == 0) return;   // uniform
   int npm = 0;
   for (uint32_t mk = done; mk; mk &= mk - 1)
     npm = max(npm, __builtin_amdgcn_readlane(parts, __builtin_ctz(mk)));
-  if (done == 0) return;   // uniform
   const int m = __builtin_popcount(done);
   merge_jobs<IO, D>(a, sm.red, m, npm, [&](int j) {
     uint32_t mk = done;   // the j-th completed pair
     for (int i = 0; i < j && i < m - 1; ++i) mk &= mk - 1;
-    const int* e = sm.pm + __builtin_ctz(mk) * kPieceMeta;
-    const int bb = __builtin_amdgcn_readfirstlane(e[kPmB]);
-    const int g = __builtin_amdgcn_readfirstlane(e[kPmG]);
-    return MergeJob{bb, g, __builtin_amdgcn_readfirstlane(e[kPmParts]),
-                    (size_t)__builtin_amdgcn_readfirstlane(e[kPmSlot0]), -1};
+    const int c = __builtin_ctz(mk);
+    return MergeJob{__builtin_amdgcn_readlane(rb, c), __builtin_amdgcn_readlane(rg, c),
+                    __builtin_amdgcn_readlane(parts, c), (size_t)__builtin_amdgcn_readlane(rs0, c), -1};
   });
 }
 
