@@ -165,13 +165,17 @@ def prepare(q, k_cache, v_cache, block_table, context_lens, scale, *, k_scale=No
     float32 k_scale, v_scale [Hkv]); block_table int32 [B, MBS];
     context_lens int32 [B]. partition_size: 0 = one pass per sequence, a
     positive multiple of 16 = split-K partitions of that many tokens,
-    SPLIT_BALANCED = equal page shares per workgroup. `workspace` (uint8,
-    zero-filled once) is used when partition_size != 0; `workspace_bytes`
-    gives its size.
+    SPLIT_BALANCED = equal page shares per workgroup. `workspace` (uint8) is
+    used when partition_size != 0; `workspace_bytes` gives its size. It must be
+    zero-filled (reset_workspace) before first use and before a call whose
+    counters take more bytes than any earlier call's (include/padecode.h);
+    every completed call leaves the counters zero. Without a workspace a
+    zeroed one is allocated per call.
 
     q [B, T, Hq, D] selects the multi-token call (pa_decode_multi): T new
     tokens per sequence whose K/V are already in the cache, new token t seeing
     positions 0 .. L-T+t; out [B, T, Hq, D], lse_out [B, T, Hq].
+    SPLIT_BALANCED needs G * T <= 16 there (G = Hq / Hkv).
     """
     import torch
     lib = load_library()
