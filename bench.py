@@ -43,8 +43,8 @@ PEAK_GBPS = 8000.0            # MI355X HBM3E, published
 MALL_BYTES = 256 << 20        # Infinity Cache
 CSRC = os.path.join(ROOT, "paged_kv_decode_05_amd", "csrc")
 # the sources each kernel is compiled from (its file and the headers it includes)
-KERNEL_SRCS = {"decode": ("pa_decode.hip", "pa_tiles.h", "pa_schedule.h"),
-               "multi": ("pa_multi.hip", "pa_tiles.h")}
+KERNEL_SRCS = {"decode": ("pa_decode.hip", "pa_tiles.h", "pa_schedule.h", "pa_internal.h"),
+               "multi": ("pa_multi.hip", "pa_tiles.h", "pa_internal.h")}
 PROBES = os.path.join(ROOT, "tests", "probes", "libpaprobes.so")
 
 
@@ -349,8 +349,11 @@ def bench_multi(args, torch, np, pkd, W):
                             partition_size=ps, out=out, workspace=ws, stream=stream)
                 for i in range(reps)]
 
+    # the workload's own split, one pass, and longer partitions (fewer partial
+    # results to write and merge when every row costs a partial: they win for
+    # several row counts and context mixes); the caller picks partition_size
     modes = [args.partition_size] if args.partition_size is not None else \
-        [spec.partition_size, 0]
+        [spec.partition_size, 0, 1024, 2048]
     if args.partition_size is None and spec.num_q_heads // spec.num_kv_heads * T <= 16:
         modes.append(pkd.SPLIT_BALANCED)   # rows of one tile: the decode kernels run the call
     if args.pmc_pass:
