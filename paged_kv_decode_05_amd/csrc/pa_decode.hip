@@ -633,9 +633,9 @@ pa_decode_kernel(const Params a) {
 // ---------------------------------------------------------------------------
 // Balanced schedule.
 //
-// The work line (pa_schedule.h) is cut into gridDim.x equal shares, one per
-// workgroup; the grid (kWgPerCu workgroups per CU) is resident all at once,
-// so every CU gets the same number of pages. Each workgroup first loads the
+// The work line (pa_schedule.h) is cut into equal shares, one per workgroup
+// (numbered XCD by XCD); the grid (kWgPerCu workgroups per CU) is resident
+// all at once, so every CU gets the same number of pages. Each workgroup first loads the
 // context lengths into LDS with the exclusive prefix sums of their line
 // positions (a scan over the workgroup, batch <= kThreads * kScanPerThread);
 // every later lookup of "which sequence holds line position x" is a binary
@@ -651,11 +651,13 @@ pa_decode_kernel(const Params a) {
 //     state: a pair that lies whole inside the quarter gets its output
 //     written by the wave; any other piece (it continues into a neighbouring
 //     quarter or share) goes to one of the wave's two LDS slots, slot 0 for
-//     the piece that starts the quarter, slot 1 for the one that ends it.
-// After its quarter, the workgroup merges, for every piece of the share that
-// went through LDS, the slots of the waves holding it, and writes the output
-// (pair inside the share) or a partial result, handed on to the last-finisher
-// merge of the pair as in the fixed schedule.
+//     the piece that starts the quarter, slot 1 for the one that ends it,
+//     with a record of its pair, its range of shares and whether it leads.
+// After its quarter, the workgroup combines, for every leading piece of the
+// share, the slots of the waves holding it (all pieces in one pass), and
+// writes the output (pair inside the share) or a partial result, handed on to
+// the last-finisher merge of the pair as in the fixed schedule; the pairs it
+// completes are merged together in one pass.
 // ---------------------------------------------------------------------------
 constexpr int kScanPerThread = 16;
 constexpr int kBalancedMaxBatch = kThreads * kScanPerThread;
