@@ -5,6 +5,7 @@
 import os
 import subprocess
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
@@ -30,19 +31,43 @@ TARGETS = [
 ]
 
 
-def build_one(srcs, dst, verbose=False):
-    if isinstance(srcs, str):
-        srcs = [srcs]
-    tmp = dst + ".tmp"
-    cmd = [HIPCC, *COMMON, *srcs, "-o", tmp]
+OBJDIR = os.path.join(ROOT, "_build")
+
+
+def _run(cmd, what, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
     out = "\n".join(l for l in res.stdout.splitlines() if "packed-fp32-ops" not in l)
     if res.returncode != 0:
-        raise RuntimeError(f"hipcc failed for {srcs}:\n{out}")
+        raise RuntimeError(f"hipcc failed for {what}:\n{out}")
     if verbose and out.strip():
         print(out)
+
+
+def _jobs():
+    try:
+        n = int(os.environ.get("MAX_JOBS", "0"))
+    except ValueError:
+        n = 0
+    return max(1, min(n or (os.cpu_count() or 1), 16))
+
+
+def build_one(srcs, dst, verbose=False):
+    """Compile every source to an object in parallel, then link dst."""
+    if isinstance(srcs, str):
+        srcs = [srcs]
+    os.makedirs(OBJDIR, exist_ok=True)
+    stem = os.path.splitext(os.path.basename(dst))[0]
+    objs = [os.path.join(OBJDIR, f"{stem}.{os.path.basename(s)}.o") for s in srcs]
+    compile_flags = [f for f in COMMON if f != "-shared"]
+    with ThreadPoolExecutor(max_workers=_jobs()) as pool:
+        futures = [pool.submit(_run, [HIPCC, *compile_flags, "-c", s, "-o", o], s, verbose)
+                   for s, o in zip(srcs, objs)]
+        for f in futures:
+            f.result()
+    tmp = dst + ".tmp"
+    _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp], dst, verbose)
     os.replace(tmp, dst)
     return dst
 
