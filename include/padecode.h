@@ -122,11 +122,18 @@ typedef struct {
  * then the groups. That adds ceil(P / F) group pieces per (sequence, query
  * head) and ceil(P / F) counters per (sequence, KV head).
  * The counters come first: the workspace's first 4 * batch * num_kv_heads *
- * (1 + groups) bytes, rounded up to 256; every completed call leaves them
- * zero, and the rest is scratch. So a workspace needs pa_workspace_reset (a
- * zero fill on a stream) before its first use, and again before a call whose
- * counter bytes exceed those of every earlier call since the last reset (its
- * counters would cover old scratch bytes).
+ * (1 + groups) bytes, rounded up to 256; every completed call leaves its own
+ * counters zero, and the rest is scratch that a call overwrites with partial
+ * results. A call of another shape (or split mode, or q_len) lays its counters
+ * over bytes that an earlier call may have used for partial results. So a
+ * workspace needs pa_workspace_reset (a zero fill on a stream) before its
+ * first use and before every call whose counter bytes exceed the smallest
+ * counter bytes of any call since the last reset; calls of one shape and mode
+ * back to back need no reset. A counter found at or above the number of
+ * pieces it counts (a broken rule) makes the affected (sequence, KV head)
+ * rows NaN instead of a silently wrong merge, and keeps doing so until the
+ * workspace is reset; a stale counter below that number cannot be told apart
+ * from a live one.
  * Returns 0 for a NULL or invalid shape. */
 size_t pa_decode_workspace_bytes(const pa_shape* shape);
 

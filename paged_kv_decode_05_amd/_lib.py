@@ -155,6 +155,60 @@ class Prepared:
         return self.out
 
 
+def _on_device(t):
+    return t.is_cuda
+
+
+def check_buffers(q, inputs, *, out=None, lse_out=None, workspace=None, k_scale=None,
+                  v_scale=None, fp8=False, on_device=None):
+    """Reject caller-supplied buffers the kernels would misuse, before anything
+    is marshalled: every tensor on q's device and contiguous; out of q's dtype
+    and shape; lse_out float32 of q's shape without the head dimension;
+    k_scale / v_scale float32 [Hkv] (required for an fp8 cache); workspace a
+    uint8 device tensor. Raises PaError(2) for a shape, layout or device
+    mismatch and PaError(3) for a dtype mismatch. `on_device` decides what
+    counts as device memory (tests pass their own to exercise the checks
+    without a GPU)."""
+    import torch
+    dev_ok = on_device or _on_device
+    Hkv = inputs[0].shape[1]
+
+    def placed(name, t):
+        if not dev_ok(t) or t.device != q.device:
+            raise PaError(2, f"{name} must be on q's device ({q.device}), not {t.device}")
+        if not t.is_contiguous():
+            raise PaError(2, f"{name} must be contiguous")
+
+    for name, t in zip(("k_cache", "v_cache", "block_table", "context_lens"), inputs):
+        placed(name, t)
+    if out is not None:
+        placed("out", out)
+        if out.dtype != q.dtype:
+            raise PaError(3, f"out must have q's dtype {q.dtype}, not {out.dtype}")
+        if tuple(out.shape) != tuple(q.shape):
+            raise PaError(2, f"out must have q's shape {tuple(q.shape)}, not {tuple(out.shape)}")
+    if lse_out is not None:
+        placed("lse_out", lse_out)
+        if lse_out.dtype != torch.float32:
+            raise PaError(3, f"lse_out must be float32, not {lse_out.dtype}")
+        if tuple(lse_out.shape) != tuple(q.shape[:-1]):
+            raise PaError(2, "lse_out must have q's shape without the head dimension")
+    for name, t in (("k_scale", k_scale), ("v_scale", v_scale)):
+        if t is None:
+            if fp8:
+                raise PaError(1, f"{name} is required for an fp8 cache")
+            continue
+        placed(name, t)
+        if t.dtype != torch.float32:
+            raise PaError(3, f"{name} must be float32, not {t.dtype}")
+        if tuple(t.shape) != (Hkv,):
+            raise PaError(2, f"{name} must have shape [{Hkv}] (one per KV head)")
+    if workspace is not None:
+        placed("workspace", workspace)
+        if workspace.dtype != torch.uint8:
+            raise PaError(3, f"workspace must be a uint8 tensor, not {workspace.dtype}")
+
+
 def prepare(q, k_cache, v_cache, block_table, context_lens, scale, *, k_scale=None,
             v_scale=None, partition_size=0, out=None, workspace=None, lse_out=None,
             stream=None):
@@ -199,10 +253,10 @@ def prepare(q, k_cache, v_cache, block_table, context_lens, scale, *, k_scale=No
             or k_cache.shape[2] * k_cache.shape[4] != D
             or tuple(block_table.shape[:1]) != (B,) or tuple(context_lens.shape) != (B,)):
         raise PaError(2, "inconsistent tensor shapes")
+    check_buffers(q, (k_cache, v_cache, block_table, context_lens), out=out, lse_out=lse_out,
+                  workspace=workspace, k_scale=k_scale, v_scale=v_scale, fp8=kv == "fp8_e4m3")
     if out is None:
         out = torch.empty_like(q)
-    if lse_out is not None and tuple(lse_out.shape) != tuple(q.shape[:-1]):
-        raise PaError(2, "lse_out must have q's shape without the head dimension")
     shape = make_shape(q, k_cache, block_table, partition_size)
     ws_ptr, ws_bytes = None, 0
     if partition_size:
@@ -274,6 +328,20 @@ def prepare_append(k_new, v_new, positions, block_table, k_cache, v_cache, *, k_
             or tuple(positions.shape) != (B,) or block_table.dim() != 2
             or block_table.shape[0] != B):
         raise PaError(2, "inconsistent tensor shapes")
+    fp8 = kv == "fp8_e4m3"
+    for name, t in (("k_scale", k_scale), ("v_scale", v_scale)):
+        if t is None:
+            if fp8:
+                raise PaError(1, f"{name} is required for an fp8 cache")
+            continue
+        if not t.is_cuda or t.device != k_new.device or not t.is_contiguous():
+            raise PaError(2, f"{name} must be a contiguous tensor on {k_new.device}")
+        if t.dtype != torch.float32 or tuple(t.shape) != (H,):
+            raise PaError(3, f"{name} must be float32 of shape [{H}]")
+    for name, t in (("v_new", v_new), ("positions", positions), ("block_table", block_table),
+                    ("k_cache", k_cache), ("v_cache", v_cache)):
+        if t.device != k_new.device:
+            raise PaError(2, f"{name} must be on {k_new.device}, not {t.device}")
     shape = PaShape(batch=B, num_q_heads=H, num_kv_heads=H, head_dim=D,
                     block_size=k_cache.shape[3], max_blocks_per_seq=block_table.shape[1],
                     num_blocks=nb, partition_size=0)
@@ -303,8 +371,19 @@ def lse_merge(shard_out, shard_lse, *, out=None, lse_out=None, stream=None):
         raise PaError(2, "expected shard_out [S, ..., D] and shard_lse [S, ...]")
     S, D = shard_out.shape[0], shard_out.shape[-1]
     rows = shard_lse[0].numel()
+    if shard_lse.device != shard_out.device:
+        raise PaError(2, "shard_lse must be on shard_out's device")
     if out is None:
         out = torch.empty(shard_out.shape[1:], dtype=shard_out.dtype, device=shard_out.device)
+    if (not out.is_cuda or out.device != shard_out.device or not out.is_contiguous()
+            or out.dtype != shard_out.dtype or tuple(out.shape) != tuple(shard_out.shape[1:])):
+        raise PaError(2, "out must be a contiguous tensor of shard_out's dtype, device and "
+                         "shape without the shard dimension")
+    if lse_out is not None and (not lse_out.is_cuda or lse_out.device != shard_out.device
+                                or not lse_out.is_contiguous() or lse_out.dtype != torch.float32
+                                or tuple(lse_out.shape) != tuple(shard_lse.shape[1:])):
+        raise PaError(2, "lse_out must be a contiguous float32 tensor of shard_lse's shape "
+                         "without the shard dimension, on shard_out's device")
     s = stream if stream is not None else torch.cuda.current_stream()
     _check(lib.pa_lse_merge(S, rows, D, shard_out.data_ptr(), shard_lse.data_ptr(),
                             DTYPE_CODE[dt], out.data_ptr(),

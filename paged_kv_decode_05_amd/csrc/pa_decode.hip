@@ -129,24 +129,33 @@ constexpr int kMergeScratch = 12 * kThreads;   // floats: slice results of 2 * k
 // trip rather than two. A job's items fill whole waves (its item count
 // rounded up to 64), so the job, and with it the base of the buffer resource
 // its loads use, is uniform across a wave. When a job has more pieces than
-// one batch and threads are left over, S slices split its pieces (slice s
-// takes pieces s, s + S, ...) and are combined in order 0, 1, ... through
-// LDS; within a slice pieces are folded in slot order, so the result does not
-// depend on which workgroup merges. A piece a row sees nothing of (lse =
+// one batch, S slices split its pieces (slice s takes pieces s, s + S, ...)
+// and are combined in order 0, 1, ... through LDS; within a slice pieces are
+// folded in slot order. S is a function of the job's own piece count and row
+// count only (merge_jobs gives a job with more than one batch of pieces a pass
+// of its own), never of which other jobs the merging workgroup happens to
+// hold, so the rounding does not depend on which workgroup merges: the result
+// is bit-identical from run to run. A piece a row sees nothing of (lse =
 // -inf) adds nothing, a row with nothing in any piece gets out = 0 and lse =
 // -inf, and a NaN piece makes the row NaN. red: LDS scratch of kMergeScratch
 // floats. Control flow is uniform across the workgroup.
+// Slices for a job of np pieces alone in a pass (its items in one round).
+__device__ __forceinline__ int merge_slices(int np, int npad, int* shift) {
+  int S = 1, sh = 0;
+  while (S < 8 && S * kMergeBatch < np && 2 * S * npad <= 2 * kThreads) {
+    S *= 2;
+    ++sh;
+  }
+  *shift = sh;
+  return S;
+}
+
 template <typename IO, int D, typename Jobs>
-__device__ __forceinline__ void merge_jobs(const Params& a, float* red, int m, int np_max, Jobs jobs) {
+__device__ __forceinline__ void merge_pass(const Params& a, float* red, int m, int S, int sshift, Jobs jobs) {
   constexpr int kQuads = D / 4;
   const int tid = threadIdx.x;
   const int npair = a.group * kQuads;
   const int npad = (npair + 63) & ~63;
-  int S = 1, sshift = 0;
-  while (S < 8 && S * kMergeBatch < np_max && m * 2 * S * npad <= 2 * kThreads) {
-    S *= 2;
-    ++sshift;
-  }
   const int per_job = S * npad;
   const int total = m * per_job;
   const size_t slot_floats = (size_t)a.group * D;
@@ -289,10 +298,41 @@ __device__ __forceinline__ void merge_jobs(const Params& a, float* red, int m, i
   }
 }
 
+// Run m merges: jobs of at most kMergeBatch pieces all in one pass (one slice
+// each); otherwise every job in a pass of its own, with its own slice count.
+template <typename IO, int D, typename Jobs>
+__device__ __forceinline__ void merge_jobs(const Params& a, float* red, int m, int np_max, Jobs jobs) {
+  if (np_max <= kMergeBatch) {
+    merge_pass<IO, D>(a, red, m, 1, 0, jobs);
+    return;
+  }
+  const int npad = (a.group * (D / 4) + 63) & ~63;
+  for (int j = 0; j < m; ++j) {
+    const MergeJob J = jobs(j);
+    int sh;
+    const int S = merge_slices(J.np, npad, &sh);
+    if (j > 0) __syncthreads();   // the previous pass's slice results in LDS are consumed
+    merge_pass<IO, D>(a, red, 1, S, sh, [&](int) { return J; });
+  }
+}
+
 // The single merge of one pair.
 template <typename IO, int D>
 __device__ __forceinline__ void merge_one(const Params& a, float* red, const MergeJob& job) {
   merge_jobs<IO, D>(a, red, 1, job.np, [&](int) { return job; });
+}
+
+// Every output row of pair (b, g) (and its lse) set to x by the workgroup.
+template <typename IO, int D, bool MQ>
+__device__ __forceinline__ void fill_rows(const Params& a, int b, int g, float x) {
+  const int tid = threadIdx.x;
+  for (int i = tid; i < a.group * D; i += kThreads) {
+    size_t row;
+    if constexpr (MQ) row = mq_row<MQ>(a, b, g, i / D);
+    else row = (size_t)b * a.num_q_heads + (size_t)g * a.group + i / D;
+    store_out<IO>(a.out, row * D + i % D, x);
+    if (i % D == 0 && a.lse_out) a.lse_out[row] = x;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -586,17 +626,32 @@ __device__ __forceinline__ void decode_piece(const Params& a, Smem<D>& sm, const
   const size_t bg = (size_t)b * a.num_kv_heads + g;
   size_t first = pc.slot0;
   int np = pc.nparts;
+  bool reporter = pc.k == 0;   // the piece that reports a stale count of (b, g)
   if (a.fan > 0 && pc.nparts > a.fan) {
     const int grp = pc.k / a.fan;
     const int gfirst = grp * a.fan;
     const int gn = min(a.fan, pc.nparts - gfirst);
     first = nbg * a.p_max + bg * a.g_max;   // the group slots of (b, g)
-    if (!last_to_finish(a.ws_cnt + nbg + bg * a.g_max + grp, gn, &sm.last)) return;
-    merge_one<IO, D>(a, red, MergeJob{b, g, gn, (size_t)pc.slot0 + gfirst, (long long)(first + grp)});
+    const int c1 = last_to_finish(a.ws_cnt + nbg + bg * a.g_max + grp, gn, &sm.last);
+    if (c1 == kCountMore) return;
+    if (c1 == kCountStale) {
+      // one piece of the group (its first) reports it: the group slot gets a
+      // NaN log-sum-exp, so the final merge makes the rows NaN, and the group
+      // is counted at the second level like a merged one
+      if (pc.k != gfirst) return;
+      if (tid < G) st_agent(a.ws_lse + (first + grp) * G + tid, __builtin_nanf(""));
+    } else {
+      merge_one<IO, D>(a, red, MergeJob{b, g, gn, (size_t)pc.slot0 + gfirst, (long long)(first + grp)});
+    }
     np = (pc.nparts + a.fan - 1) / a.fan;
+    reporter = grp == 0;
   }
-  if (!last_to_finish(a.ws_cnt + bg, np, &sm.last)) return;
-  merge_one<IO, D>(a, red, MergeJob{b, g, np, first, -1});
+  const int c2 = last_to_finish(a.ws_cnt + bg, np, &sm.last);
+  if (c2 == kCountLast) {
+    merge_one<IO, D>(a, red, MergeJob{b, g, np, first, -1});
+  } else if (c2 == kCountStale && reporter) {
+    fill_rows<IO, D, MQ>(a, b, g, __builtin_nanf(""));
+  }
 }
 
 // Fixed schedule: one workgroup per (sequence b, KV head g, partition p) unit
@@ -700,7 +755,7 @@ __host__ __device__ inline BalLayout bal_layout(int G, int D, int B) {
   o.len = p;  p = lds_align(p + 4u * B);                          // [B]
   o.pre = p;  p = lds_align(p + 4u * (B + 1));                    // [B + 1]
   o.misc = p; p = lds_align(p + 4u * kWaves);                     // wsum[kWaves]
-  o.split = p; p = lds_align(p + 4u * 2 * kWaves);               // per candidate slot: "last" flag
+  o.split = p; p = lds_align(p + 4u * 2 * kWaves);               // [0]: completed pairs, [1]: stale ones
   o.total = p;
   return o;
 }
@@ -718,7 +773,8 @@ struct BalSm {
   int* len;
   int* pre;
   int* misc;
-  int* split;   // [0]: bit c set when the workgroup completed candidate slot c's pair
+  int* split;   // bit c set when the workgroup completed candidate slot c's pair ([0]) or
+                // found its counter stale and reports it ([1])
   int G;
   __device__ BalSm(int G_, int B) : G(G_) {
     const BalLayout o = bal_layout(G_, D, B);
@@ -1285,18 +1341,24 @@ pa_decode_balanced_kernel(const Params a) {
   __builtin_amdgcn_s_waitcnt(0);   // this wave's partial stores are complete
   __syncthreads();
   if (wu == 0) {
-    bool last = false;
-    if (lane < 2 * kWaves && ((split >> lane) & 1u)) {
-      uint32_t* cnt = a.ws_cnt + (size_t)rb * H + rg;
-      const uint32_t done = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      last = done == (uint32_t)(parts - 1);
-      // this workgroup completes the pair: its counter is free for the next call
-      if (last) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    int outcome = kCountMore;
+    if (lane < 2 * kWaves && ((split >> lane) & 1u))
+      outcome = count_piece(a.ws_cnt + (size_t)rb * H + rg, parts);
+    const uint32_t dm = (uint32_t)__ballot(outcome == kCountLast) & 0xffu;
+    // a stale counter: the pair's first piece makes its rows NaN
+    const uint32_t sm_ = (uint32_t)__ballot(outcome == kCountStale && rec[kPmK] == 0) & 0xffu;
+    if (lane == 0) {
+      sm.split[0] = (int)dm;
+      sm.split[1] = (int)sm_;
     }
-    const uint32_t dm = (uint32_t)__ballot(last) & 0xffu;
-    if (lane == 0) sm.split[0] = (int)dm;
   }
   lds_barrier();
+  const uint32_t stale = (uint32_t)__builtin_amdgcn_readfirstlane(sm.split[1]);
+  for (uint32_t mk = stale; mk; mk &= mk - 1) {
+    const int c = __builtin_ctz(mk);
+    fill_rows<IO, D, MQ>(a, __builtin_amdgcn_readlane(rb, c), __builtin_amdgcn_readlane(rg, c),
+                         __builtin_nanf(""));
+  }
   // the pairs this workgroup completes, all merged in one pass
   const uint32_t done = (uint32_t)__builtin_amdgcn_readfirstlane(sm.split[0]);
   if (done == 0) return;   // uniform
@@ -1327,6 +1389,7 @@ __global__ void fill_zero_kernel(uint8_t* p, size_t n) {
 struct WsLayout {
   size_t o_off, lse_off, cnt_off, total;
   int p_max, fan, g_max;
+  size_t cnt_bytes;   // bytes of counters the call uses (from cnt_off)
 };
 
 
@@ -1377,9 +1440,12 @@ static bool shape_ok(const pa_shape* s) {
 }
 
 // shares: the balanced split's workgroup count (ignored otherwise); q_len:
-// new tokens per sequence (rows per pair = group * q_len)
-static WsLayout ws_layout(const pa_shape* s, int shares, int q_len) {
-  WsLayout w{0, 0, 0, 0, 1, 0, 0};
+// new tokens per sequence (rows per pair = group * q_len); cnt_region: 0 to
+// pack the counters first (rounded up to 256 bytes), else the partial results
+// start at that fixed byte offset, so counters and partials of calls of any
+// shape never overlap.
+static WsLayout ws_layout(const pa_shape* s, int shares, int q_len, size_t cnt_region = 0) {
+  WsLayout w{0, 0, 0, 0, 1, 0, 0, 0};
   if (s->partition_size == 0) return w;
   const size_t nbg = (size_t)s->batch * s->num_kv_heads;
   size_t slots;
@@ -1398,7 +1464,8 @@ static WsLayout ws_layout(const pa_shape* s, int shares, int q_len) {
   // call leaves them zero, so a later call whose counters fit in the same
   // bytes finds them zero
   w.cnt_off = 0;
-  w.o_off = align_up(nbg * (1 + (size_t)w.g_max) * sizeof(uint32_t), 256);
+  w.cnt_bytes = nbg * (1 + (size_t)w.g_max) * sizeof(uint32_t);
+  w.o_off = cnt_region ? cnt_region : align_up(w.cnt_bytes, 256);
   w.lse_off = w.o_off + align_up(rows * s->head_dim * sizeof(float), 256);
   w.total = w.lse_off + align_up(rows * sizeof(float), 256);
   return w;
@@ -1437,12 +1504,14 @@ size_t decode_workspace_bytes(const pa_shape* shape, int q_len) {
   return ws_layout(shape, shares, q_len).total;
 }
 
-pa_status decode_call(const pa_shape* shape, int q_len, const void* q, const void* k_cache,
-                      const void* v_cache, const int32_t* block_table,
-                      const int32_t* context_lens, float scale, pa_dtype io_dtype,
-                      pa_dtype kv_dtype, const float* k_scale, const float* v_scale,
-                      void* workspace, size_t workspace_bytes, void* out, float* lse_out,
-                      void* stream) {
+// cnt_region: 0 for a caller's workspace (counters packed first), else a
+// fixed counter region (see ws_layout).
+static pa_status decode_launch(const pa_shape* shape, int q_len, const void* q, const void* k_cache,
+                               const void* v_cache, const int32_t* block_table,
+                               const int32_t* context_lens, float scale, pa_dtype io_dtype,
+                               pa_dtype kv_dtype, const float* k_scale, const float* v_scale,
+                               void* workspace, size_t workspace_bytes, size_t cnt_region,
+                               void* out, float* lse_out, void* stream) {
   if (!shape) return PA_ERR_NULL;
   if (!shape_ok(shape) || q_len < 1) return PA_ERR_SHAPE;
   const int G = shape->num_q_heads / shape->num_kv_heads;
@@ -1464,7 +1533,7 @@ pa_status decode_call(const pa_shape* shape, int q_len, const void* q, const voi
     shares = balanced_shares();
     if (shares < 0) return PA_ERR_HIP;
   }
-  const WsLayout wl = ws_layout(shape, shares, q_len);
+  const WsLayout wl = ws_layout(shape, shares, q_len, cnt_region);
   if (shape->partition_size != 0) {
     if (!workspace || workspace_bytes < wl.total) return PA_ERR_WORKSPACE;
     if ((uintptr_t)workspace & 255u) return PA_ERR_ALIGN;
@@ -1526,6 +1595,16 @@ pa_status decode_call(const pa_shape* shape, int q_len, const void* q, const voi
                                   : launch_d<BF16, BF16, true>(D, prm, grid, balanced, st);
   }
   return e == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+pa_status decode_call(const pa_shape* shape, int q_len, const void* q, const void* k_cache,
+                      const void* v_cache, const int32_t* block_table,
+                      const int32_t* context_lens, float scale, pa_dtype io_dtype,
+                      pa_dtype kv_dtype, const float* k_scale, const float* v_scale,
+                      void* workspace, size_t workspace_bytes, void* out, float* lse_out,
+                      void* stream) {
+  return decode_launch(shape, q_len, q, k_cache, v_cache, block_table, context_lens, scale, io_dtype,
+                       kv_dtype, k_scale, v_scale, workspace, workspace_bytes, 0, out, lse_out, stream);
 }
 
 }  // namespace pa

@@ -473,19 +473,40 @@ pa_multi_kernel(const Params a) {
   // rows of this chunk into a group slot, the last group merges the groups.
   size_t first = (size_t)bg * a.p_max;
   int np = nparts;
+  bool reporter = p == 0;   // the piece that reports a stale count of (b, g, c)
   if (a.fan > 0 && nparts > a.fan) {
     const int grp = p / a.fan;
     const int gfirst = grp * a.fan;
     const int gn = min(a.fan, nparts - gfirst);
     const size_t gbase = (size_t)nbg * a.p_max + (size_t)bg * a.g_max;   // group slots of (b, g)
-    if (!last_to_finish(a.ws_cnt + ((size_t)nbg + (size_t)bg * a.g_max + grp) * a.chunks + c, gn, &sm.last))
-      return;
-    merge_rows<IO, D>(a, b, g, row0, rows_c, first + gfirst, gn, (long long)(gbase + grp));
+    const int c1 =
+        last_to_finish(a.ws_cnt + ((size_t)nbg + (size_t)bg * a.g_max + grp) * a.chunks + c, gn, &sm.last);
+    if (c1 == kCountMore) return;
+    if (c1 == kCountStale) {
+      // the group's first partition reports it: a NaN log-sum-exp in the
+      // group slot makes the final merge's rows NaN
+      if (p != gfirst) return;
+      if ((int)threadIdx.x < rows_c)
+        st_agent(a.ws_lse + (gbase + grp) * R + row0 + threadIdx.x, __builtin_nanf(""));
+    } else {
+      merge_rows<IO, D>(a, b, g, row0, rows_c, first + gfirst, gn, (long long)(gbase + grp));
+    }
     first = gbase;
     np = (nparts + a.fan - 1) / a.fan;
+    reporter = grp == 0;
   }
-  if (!last_to_finish(a.ws_cnt + (size_t)bg * a.chunks + c, np, &sm.last)) return;
-  merge_rows<IO, D>(a, b, g, row0, rows_c, first, np, -1);
+  const int c2 = last_to_finish(a.ws_cnt + (size_t)bg * a.chunks + c, np, &sm.last);
+  if (c2 == kCountLast) {
+    merge_rows<IO, D>(a, b, g, row0, rows_c, first, np, -1);
+  } else if (c2 == kCountStale && reporter) {
+    for (int i = threadIdx.x; i < rows_c * D; i += kThreads) {
+      const int rho = row0 + i / D;
+      const int t = rho / G, h = rho - t * G;
+      const size_t orow = ((size_t)b * TQ + t) * a.num_q_heads + (size_t)g * G + h;
+      store_out<IO>(a.out, orow * D + i % D, __builtin_nanf(""));
+      if (i % D == 0 && a.lse_out) a.lse_out[orow] = __builtin_nanf("");
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------

@@ -122,20 +122,40 @@ __device__ __forceinline__ float ld_agent1(brsrc r, uint32_t off, uint32_t soff)
   return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, soff, kCpolSc1));
 }
 
+// Outcome of counting one piece of n on a workspace counter.
+constexpr int kCountMore = 0;    // other pieces are still to come
+constexpr int kCountLast = 1;    // this piece completed the count: merge, counter reset to 0
+constexpr int kCountStale = 2;   // the counter held n or more before this call
+
+// Count one piece on *cnt (one thread). A completed call leaves every counter
+// at 0, so during a call a counter runs 0 .. n-1; a value of n or more can only
+// be left over from a broken workspace-reuse rule. Such a piece takes its
+// count back (the counter keeps its stale value, so later calls see it too
+// until the workspace is reset) and reports kCountStale, and the caller makes
+// the rows NaN rather than merge partial results that were never counted.
+__device__ __forceinline__ int count_piece(uint32_t* cnt, int n) {
+  const uint32_t done = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (done == (uint32_t)(n - 1)) {
+    __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return kCountLast;
+  }
+  if (done >= (uint32_t)n) {
+    __hip_atomic_fetch_sub(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return kCountStale;
+  }
+  return kCountMore;
+}
+
 // Split-K hand-off: every wave waits until its agent-coherent stores have
-// completed, then one thread counts this piece on *cnt; true (uniformly) for
-// the workgroup that brings the count to n, which then owns the merge and
-// resets the counter for the next call.
-__device__ __forceinline__ bool last_to_finish(uint32_t* cnt, int n, int* flag) {
+// completed, then one thread counts this piece on *cnt; the outcome
+// (count_piece) is returned uniformly to the whole workgroup. kCountLast
+// makes the workgroup the owner of the merge.
+__device__ __forceinline__ int last_to_finish(uint32_t* cnt, int n, int* flag) {
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  if (threadIdx.x == 0) {
-    const uint32_t done = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    *flag = done == (uint32_t)(n - 1);
-    if (*flag) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
+  if (threadIdx.x == 0) *flag = count_piece(cnt, n);
   __syncthreads();
-  return __builtin_amdgcn_readfirstlane(*flag) != 0;
+  return __builtin_amdgcn_readfirstlane(*flag);
 }
 
 // ---------------------------------------------------------------------------

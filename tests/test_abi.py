@@ -129,7 +129,7 @@ def test_workspace_size_arithmetic():
 def test_status_strings():
     lib = _lib.load_library()
     for code in range(9):
-        assert lib.pa_status_str(code)
+        assert lib.pa_status_str(code) and lib.pa_status_str(code) != b"unknown status"
     assert lib.pa_status_str(99) == b"unknown status"
 
 
@@ -262,3 +262,76 @@ def test_multi_token_rows_of_one_tile_take_the_decode_kernels():
 def torch_gpu_count():
     import torch
     return torch.cuda.device_count()
+
+
+# ---- the binding's buffer checks, exercised on CPU tensors ------------------
+
+def _buffers(dtype="f16", fp8=False):
+    import torch
+    tq = {"f16": torch.float16, "bf16": torch.bfloat16, "f32": torch.float32}[dtype]
+    B, Hq, Hkv, D = 2, 8, 2, 128
+    q = torch.zeros(B, Hq, D, dtype=tq)
+    kd = torch.uint8 if fp8 else tq
+    x = 16 if fp8 else 8
+    k = torch.zeros(10, Hkv, D // x, 16, x, dtype=kd)
+    v = torch.zeros(10, Hkv, D, 16, dtype=kd)
+    bt = torch.zeros(B, 4, dtype=torch.int32)
+    cl = torch.zeros(B, dtype=torch.int32)
+    return q, (k, v, bt, cl)
+
+
+def _check(q, inputs, **kw):
+    return _lib.check_buffers(q, inputs, on_device=lambda t: True, **kw)
+
+
+def test_buffer_checks_accept_well_formed_buffers():
+    import torch
+    q, inp = _buffers()
+    _check(q, inp, out=torch.empty_like(q), lse_out=torch.empty(2, 8),
+           workspace=torch.empty(1024, dtype=torch.uint8))
+    q, inp = _buffers(fp8=True)
+    _check(q, inp, k_scale=torch.ones(2), v_scale=torch.ones(2), fp8=True)
+
+
+@pytest.mark.parametrize("what,status", [
+    ("out_dtype", 3), ("out_shape", 2), ("out_strided", 2), ("lse_dtype", 3), ("lse_shape", 2),
+    ("scale_dtype", 3), ("scale_shape", 2), ("scale_missing", 1), ("ws_dtype", 3),
+    ("ws_strided", 2), ("host_out", 2), ("host_ws", 2), ("host_scale", 2)])
+def test_buffer_checks_reject_misfit_buffers(what, status):
+    import torch
+    q, inp = _buffers(fp8=what.startswith("scale") or what == "host_scale")
+    fp8 = q is not None and inp[0].dtype == torch.uint8
+    kw = dict(k_scale=torch.ones(2), v_scale=torch.ones(2)) if fp8 else {}
+    on_device = lambda t: True
+    if what == "out_dtype":
+        kw["out"] = torch.empty(q.shape, dtype=torch.float32)      # twice q's element size
+    elif what == "out_shape":
+        kw["out"] = torch.empty(2, 8, 64, dtype=q.dtype)
+    elif what == "out_strided":
+        kw["out"] = torch.empty(2, 8, 256, dtype=q.dtype)[..., ::2]
+    elif what == "lse_dtype":
+        kw["lse_out"] = torch.empty(2, 8, dtype=torch.bfloat16)
+    elif what == "lse_shape":
+        kw["lse_out"] = torch.empty(2, 4)
+    elif what == "scale_dtype":
+        kw["k_scale"] = torch.ones(2, dtype=torch.float16)
+    elif what == "scale_shape":
+        kw["v_scale"] = torch.ones(4)
+    elif what == "scale_missing":
+        kw.pop("k_scale")
+    elif what == "ws_dtype":
+        kw["workspace"] = torch.empty(256, dtype=torch.int32)
+    elif what == "ws_strided":
+        kw["workspace"] = torch.empty(512, dtype=torch.uint8)[::2]
+    elif what.startswith("host_"):
+        # the tensor named is the one that is not device memory
+        target = {"host_out": "out", "host_ws": "workspace", "host_scale": "k_scale"}[what]
+        kw.setdefault("out", torch.empty_like(q))
+        kw.setdefault("workspace", torch.empty(256, dtype=torch.uint8))
+        if target == "k_scale":
+            kw["k_scale"] = torch.ones(2)
+        bad = kw[target]
+        on_device = lambda t: t is not bad
+    with pytest.raises(_lib.PaError) as e:
+        _lib.check_buffers(q, inp, on_device=on_device, fp8=fp8, **kw)
+    assert e.value.status == status, (what, str(e.value))

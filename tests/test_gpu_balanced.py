@@ -133,3 +133,73 @@ def test_workspace_serves_smaller_calls_without_reset(ps):
         for wl in (big, small, small):
             out = run(wl, partition_size=ps, workspace=ws)
             check(wl, to_f64(out), ref(wl), label=f"ws order {i} {wl.spec.batch}")
+
+
+@pytest.mark.parametrize("ps", [512, BAL])
+def test_workspace_rule_big_small_big_across_a_counter_boundary(ps):
+    # B=32 with 4 KV heads (512 counter bytes), then 2 KV heads (256 bytes),
+    # then 4 again: the small call's partial results cover the big call's
+    # counters 64..127, so the header's rule asks for a reset before the
+    # third call (its counter bytes exceed the smallest since the last reset)
+    big = W.make_workload(W.small_variant(W.SPECS[3], 32, ("uniform", 100, 1500)))
+    small = W.make_workload(W.small_variant(W.SPECS[2], 32, ("uniform", 100, 1500)), seed=77)
+    need = max(pkd.workspace_bytes(to_device(w)["q"], to_device(w)["k_cache"],
+                                   to_device(w)["block_table"], ps) for w in (big, small))
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    pkd.reset_workspace(ws)
+    for i, wl in enumerate((big, small, big)):
+        if i == 2:
+            pkd.reset_workspace(ws)
+        print(f"case workspace rule ps={ps} call {i}: Hkv {wl.spec.num_kv_heads}", flush=True)
+        out = run(wl, partition_size=ps, workspace=ws)
+        check(wl, to_f64(out), ref(wl), label=f"rule {ps} call {i}")
+
+
+def _stale_case(ps, counter_index, value, spec):
+    wl = W.make_workload(spec)
+    t = to_device(wl)
+    need = pkd.workspace_bytes(t["q"], t["k_cache"], t["block_table"], ps)
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    ws.view(torch.int32)[counter_index] = value
+    return wl, t, ws
+
+
+@pytest.mark.parametrize("ps,counter,label", [
+    (512, 0, "pair counter, one merge level"),
+    (BAL, 0, "pair counter, balanced split"),
+    (16, 2 * 2 + 0, "first merge-group counter of pair 0, two merge levels"),
+    (16, 0, "pair counter, two merge levels")])
+def test_stale_counter_gives_nan_rows_until_reset(ps, counter, label):
+    # A counter left at or above the number of pieces it counts (a broken
+    # reuse rule) makes the rows of its (sequence, KV head) NaN, every other
+    # row stays right, the state persists, and a reset restores the call.
+    spec = W.Spec("stale", 2, 8, 2, 128, "f16", "f16", ("fixed", [3000, 700]), 200,
+                  ("ratio", 1.2), ps, 0, 5)
+    print(f"case stale counter ps={ps}: {label}", flush=True)
+    wl, t, ws = _stale_case(ps, counter, 1000, spec)
+    exp = ref(wl)
+    G = spec.num_q_heads // spec.num_kv_heads
+    for rep in range(2):
+        out = to_f64(run(wl, t, partition_size=ps, workspace=ws))
+        assert np.isnan(out[0, :G]).all(), (label, rep)                # pair (0, 0)
+        assert np.isfinite(out[0, G:]).all() and np.isfinite(out[1]).all()
+        assert np.abs(out[0, G:] - exp[0, G:]).max() <= 1e-2
+        assert np.abs(out[1] - exp[1]).max() <= 1e-2
+    pkd.reset_workspace(ws)
+    out = to_f64(run(wl, t, partition_size=ps, workspace=ws))
+    check(wl, out, exp, label=f"stale {label} after reset")
+
+
+def test_bit_identical_when_merging_workgroups_hold_several_pairs():
+    # Short shares cut each pair into more than 8 pieces, and which workgroup
+    # finishes a pair last (and so merges it, maybe together with other pairs)
+    # changes from run to run; the merge's slicing depends on the pair alone,
+    # so every run gives the same bits.
+    spec = W.small_variant(W.SPECS[3], 8, ("uniform", 100, 3000))
+    wl = W.make_workload(spec, seed=40)
+    t = to_device(wl)
+    first = run(wl, t, partition_size=BAL).cpu()
+    for i in range(12):
+        again = run(wl, t, partition_size=BAL).cpu()
+        assert torch.equal(first.view(torch.int16), again.view(torch.int16)), i
+    check(wl, to_f64(first), ref(wl), label="bal determinism")
