@@ -81,7 +81,8 @@ typedef enum {
   PA_ERR_ALIGN = 5,     /* a tensor pointer is not 16-byte aligned */
   PA_ERR_HIP = 6,       /* the HIP runtime refused the launch */
   PA_ERR_CAPACITY = 7,  /* block pool: not enough free blocks (or host memory) */
-  PA_ERR_STATE = 8      /* block pool: sequence id unknown, or already present */
+  PA_ERR_STATE = 8,     /* block pool: sequence id unknown, or already present */
+  PA_ERR_SCRATCH = 9    /* pa_decode_noalloc: the call needs more scratch than it holds */
 } pa_status;
 
 typedef struct {
@@ -155,6 +156,33 @@ pa_status pa_decode(const pa_shape* shape, const void* q, const void* k_cache,
                     const float* v_scale, void* workspace,
                     size_t workspace_bytes, void* out, float* lse_out,
                     void* stream);
+
+/* pa_decode for callers that cannot allocate device memory or pass a
+ * workspace: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation. Same arguments, results and errors as pa_decode
+ * without workspace and workspace_bytes: the split modes keep their partial
+ * results and counters in a scratch array of PA_NOALLOC_SCRATCH_BYTES that
+ * the library holds on each GPU it runs on until the process ends. Its first
+ * PA_NOALLOC_COUNTER_BYTES hold the counters (4 bytes per (sequence, KV
+ * head), plus the merge-group counters of fixed partitions beyond 16 per
+ * sequence); the partial results of pa_decode_workspace_bytes's layout follow
+ * them. A call that needs more than either gets PA_ERR_SCRATCH and launches
+ * nothing (with 512-token partitions over 4096-token tables, head_dim 128 and
+ * 7 query heads per KV head, a (sequence, KV head) pair takes 8 x 7 x 129
+ * floats, so about 570 pairs fit; the balanced split needs far less). The
+ * library allocates nothing in this call;
+ * its first call on a GPU looks up that GPU's array and enqueues one zero
+ * fill of the counter region on `stream`. Every call on a GPU shares the
+ * array: calls that may overlap on one GPU (other streams, other host
+ * threads) race and must be serialised by the caller. partition_size 0 uses
+ * no scratch. */
+#define PA_NOALLOC_SCRATCH_BYTES (16u << 20)
+#define PA_NOALLOC_COUNTER_BYTES (256u << 10)
+pa_status pa_decode_noalloc(const pa_shape* shape, const void* q, const void* k_cache,
+                            const void* v_cache, const int32_t* block_table,
+                            const int32_t* context_lens, float scale, pa_dtype io_dtype,
+                            pa_dtype kv_dtype, const float* k_scale, const float* v_scale,
+                            void* out, float* lse_out, void* stream);
 
 /* Attention of q_len new tokens per sequence over the paged cache, causal
  * among the new tokens: the attention step of chunked prefill ("Litellama",

@@ -4,10 +4,10 @@ The compute path is the HIP library built from csrc/ (libpadecode.so); the
 Python side only marshals torch tensors into its C ABI. Importing this package
 does not load the library; `decode()` does, and raises if it is missing.
 """
-from ._lib import (SPLIT_BALANCED, BlockPool, PaError, Prepared, decode, kv_append,
+from ._lib import (SPLIT_BALANCED, BlockPool, PaError, Prepared, decode, decode_noalloc, kv_append,
                    library_path, load_library, lse_merge, prepare, reset_workspace,
                    workspace_bytes)
 
-__all__ = ["SPLIT_BALANCED", "BlockPool", "PaError", "Prepared", "decode",
+__all__ = ["SPLIT_BALANCED", "BlockPool", "PaError", "Prepared", "decode", "decode_noalloc",
            "kv_append", "library_path", "load_library", "lse_merge", "prepare", "reset_workspace",
            "workspace_bytes"]

@@ -14,12 +14,14 @@ PA_F32, PA_F16, PA_BF16, PA_FP8_E4M3 = 0, 1, 2, 3
 SPLIT_BALANCED = -1   # partition_size value of the balanced split (PA_SPLIT_BALANCED)
 DTYPE_CODE = {"f32": PA_F32, "f16": PA_F16, "bf16": PA_BF16, "fp8_e4m3": PA_FP8_E4M3}
 
-EXPORTED = ("pa_decode", "pa_decode_workspace_bytes", "pa_decode_multi",
+EXPORTED = ("pa_decode", "pa_decode_workspace_bytes", "pa_decode_noalloc", "pa_decode_multi",
             "pa_decode_multi_workspace_bytes", "pa_kv_append", "pa_lse_merge",
             "pa_workspace_reset", "pa_status_str", "pa_pool_create", "pa_pool_destroy",
             "pa_pool_add_sequence", "pa_pool_append_token", "pa_pool_free_sequence",
             "pa_pool_num_free", "pa_pool_block_table")
-PA_ERR_CAPACITY, PA_ERR_STATE = 7, 8
+PA_ERR_CAPACITY, PA_ERR_STATE, PA_ERR_SCRATCH = 7, 8, 9
+NOALLOC_SCRATCH_BYTES = 16 << 20    # PA_NOALLOC_SCRATCH_BYTES
+NOALLOC_COUNTER_BYTES = 256 << 10   # PA_NOALLOC_COUNTER_BYTES
 
 
 class PaError(RuntimeError):
@@ -58,6 +60,9 @@ def load_library(path=None):
                               ctypes.c_int, ctypes.c_int, vp, vp, vp, ctypes.c_size_t, vp,
                               vp, vp]
     lib.pa_decode.restype = ctypes.c_int
+    lib.pa_decode_noalloc.argtypes = [ctypes.POINTER(PaShape), vp, vp, vp, vp, vp, ctypes.c_float,
+                                      ctypes.c_int, ctypes.c_int, vp, vp, vp, vp, vp]
+    lib.pa_decode_noalloc.restype = ctypes.c_int
     lib.pa_decode_multi_workspace_bytes.argtypes = [ctypes.POINTER(PaShape), ctypes.c_int32]
     lib.pa_decode_multi_workspace_bytes.restype = ctypes.c_size_t
     lib.pa_decode_multi.argtypes = [ctypes.POINTER(PaShape), ctypes.c_int32, vp, vp, vp, vp, vp,
@@ -138,6 +143,46 @@ def decode(q, k_cache, v_cache, block_table, context_lens, scale, *, k_scale=Non
     return prepare(q, k_cache, v_cache, block_table, context_lens, scale, k_scale=k_scale,
                    v_scale=v_scale, partition_size=partition_size, out=out,
                    workspace=workspace, lse_out=lse_out, stream=stream)()
+
+
+def decode_noalloc(q, k_cache, v_cache, block_table, context_lens, scale, *, k_scale=None,
+                   v_scale=None, partition_size=0, out=None, lse_out=None, stream=None):
+    """pa_decode_noalloc: as `decode` for q [B, Hq, D], with the split modes'
+    partial results in the library's per-GPU scratch instead of a workspace
+    (the C call allocates nothing; pass `out` to keep this call allocation-free
+    on the Python side too). Calls that may overlap on one GPU race on that
+    scratch. Returns out."""
+    import torch
+    lib = load_library()
+    io = _torch_dtype_name(q)
+    kv = _torch_dtype_name(k_cache)
+    if io is None or kv is None or _torch_dtype_name(v_cache) != kv or q.dim() != 3:
+        raise PaError(3, f"unsupported dtypes or rank: q={q.dtype} [{q.dim()}-d] k={k_cache.dtype}")
+    if not q.is_cuda or not q.is_contiguous():
+        raise PaError(2, "q must be a contiguous device tensor")
+    if (k_cache.dim() != 5 or v_cache.dim() != 4 or block_table.dim() != 2
+            or block_table.dtype != torch.int32 or context_lens.dtype != torch.int32):
+        raise PaError(2, "expected k_cache [nb,Hkv,D/X,16,X], v_cache [nb,Hkv,D,16] and int32 "
+                         "block_table [B,MBS], context_lens [B]")
+    B, Hq, D = q.shape
+    nb, Hkv = k_cache.shape[0], k_cache.shape[1]
+    if (tuple(v_cache.shape) != (nb, Hkv, D, k_cache.shape[3])
+            or k_cache.shape[2] * k_cache.shape[4] != D
+            or tuple(block_table.shape[:1]) != (B,) or tuple(context_lens.shape) != (B,)):
+        raise PaError(2, "inconsistent tensor shapes")
+    check_buffers(q, (k_cache, v_cache, block_table, context_lens), out=out, lse_out=lse_out,
+                  k_scale=k_scale, v_scale=v_scale, fp8=kv == "fp8_e4m3")
+    if out is None:
+        out = torch.empty_like(q)
+    shape = make_shape(q, k_cache, block_table, partition_size)
+    s = stream if stream is not None else torch.cuda.current_stream()
+    _check(lib.pa_decode_noalloc(
+        ctypes.byref(shape), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+        block_table.data_ptr(), context_lens.data_ptr(), float(scale), DTYPE_CODE[io],
+        DTYPE_CODE[kv], k_scale.data_ptr() if k_scale is not None else None,
+        v_scale.data_ptr() if v_scale is not None else None, out.data_ptr(),
+        lse_out.data_ptr() if lse_out is not None else None, s.cuda_stream))
+    return out
 
 
 class Prepared:

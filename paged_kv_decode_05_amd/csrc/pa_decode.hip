@@ -43,6 +43,7 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <mutex>
 #include <type_traits>
 
 #include "padecode.h"
@@ -1443,7 +1444,7 @@ static bool shape_ok(const pa_shape* s) {
 // new tokens per sequence (rows per pair = group * q_len); cnt_region: 0 to
 // pack the counters first (rounded up to 256 bytes), else the partial results
 // start at that fixed byte offset, so counters and partials of calls of any
-// shape never overlap.
+// shape never overlap (the no-allocation entry point's scratch).
 static WsLayout ws_layout(const pa_shape* s, int shares, int q_len, size_t cnt_region = 0) {
   WsLayout w{0, 0, 0, 0, 1, 0, 0, 0};
   if (s->partition_size == 0) return w;
@@ -1504,8 +1505,8 @@ size_t decode_workspace_bytes(const pa_shape* shape, int q_len) {
   return ws_layout(shape, shares, q_len).total;
 }
 
-// cnt_region: 0 for a caller's workspace (counters packed first), else a
-// fixed counter region (see ws_layout).
+// cnt_region: 0 for a caller's workspace (counters packed first), else the
+// fixed counter region of the no-allocation scratch (see ws_layout).
 static pa_status decode_launch(const pa_shape* shape, int q_len, const void* q, const void* k_cache,
                                const void* v_cache, const int32_t* block_table,
                                const int32_t* context_lens, float scale, pa_dtype io_dtype,
@@ -1535,6 +1536,7 @@ static pa_status decode_launch(const pa_shape* shape, int q_len, const void* q, 
   }
   const WsLayout wl = ws_layout(shape, shares, q_len, cnt_region);
   if (shape->partition_size != 0) {
+    if (cnt_region && (wl.cnt_bytes > cnt_region || wl.total > workspace_bytes)) return PA_ERR_SCRATCH;
     if (!workspace || workspace_bytes < wl.total) return PA_ERR_WORKSPACE;
     if ((uintptr_t)workspace & 255u) return PA_ERR_ALIGN;
   }
@@ -1607,6 +1609,45 @@ pa_status decode_call(const pa_shape* shape, int q_len, const void* q, const voi
                        kv_dtype, k_scale, v_scale, workspace, workspace_bytes, 0, out, lse_out, stream);
 }
 
+// ---------------------------------------------------------------------------
+// Scratch of the no-allocation entry point: one array per GPU the library
+// runs on, held until the process ends. The first kScratchCounterBytes hold
+// the (sequence, KV head) and merge-group counters of every call; partial
+// results follow at that fixed offset, so no call's partials ever land on
+// another call's counters. The array starts zeroed (and is zero-filled once
+// more when a device first uses it); every completed call leaves the counters
+// it used at zero, so calls need no clearing in between.
+// ---------------------------------------------------------------------------
+constexpr size_t kScratchBytes = (size_t)16 << 20;
+constexpr size_t kScratchCounterBytes = (size_t)256 << 10;
+static_assert(kScratchBytes == PA_NOALLOC_SCRATCH_BYTES, "scratch size in the header");
+static_assert(kScratchCounterBytes == PA_NOALLOC_COUNTER_BYTES, "counter region in the header");
+
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[kMaxDevices];
+
+// The device address of this GPU's scratch (the array's name in host code is
+// only a handle for hipGetSymbolAddress, never an address to pass on). On the
+// first call on a device its counter region is zero-filled on `stream`.
+static pa_status scratch_of_current_device(hipStream_t stream, void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return PA_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return PA_ERR_HIP;
+    hipLaunchKernelGGL(fill_zero_kernel, dim3(64), dim3(256), 0, stream, static_cast<uint8_t*>(ptr),
+                       kScratchCounterBytes);
+    if (hipGetLastError() != hipSuccess) return PA_ERR_HIP;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return PA_OK;
+}
+
 }  // namespace pa
 
 extern "C" {
@@ -1621,6 +1662,29 @@ pa_status pa_decode(const pa_shape* shape, const void* q, const void* k_cache,
                     void* stream) {
   return pa::decode_call(shape, 1, q, k_cache, v_cache, block_table, context_lens, scale, io_dtype,
                          kv_dtype, k_scale, v_scale, workspace, workspace_bytes, out, lse_out, stream);
+}
+
+pa_status pa_decode_noalloc(const pa_shape* shape, const void* q, const void* k_cache,
+                            const void* v_cache, const int32_t* block_table,
+                            const int32_t* context_lens, float scale, pa_dtype io_dtype,
+                            pa_dtype kv_dtype, const float* k_scale, const float* v_scale,
+                            void* out, float* lse_out, void* stream) {
+  if (!shape) return PA_ERR_NULL;
+  if (shape->partition_size == 0)   // one pass: no scratch at all
+    return pa::decode_launch(shape, 1, q, k_cache, v_cache, block_table, context_lens, scale, io_dtype,
+                             kv_dtype, k_scale, v_scale, nullptr, 0, 0, out, lse_out, stream);
+  // fixed partitions: the size check needs no device, so an oversized call is
+  // refused before the scratch is looked up
+  if (shape->partition_size > 0 && pa::shape_ok(shape)) {
+    const pa::WsLayout wl = pa::ws_layout(shape, 0, 1, pa::kScratchCounterBytes);
+    if (wl.cnt_bytes > pa::kScratchCounterBytes || wl.total > pa::kScratchBytes) return PA_ERR_SCRATCH;
+  }
+  void* ws = nullptr;
+  const pa_status st = pa::scratch_of_current_device(static_cast<hipStream_t>(stream), &ws);
+  if (st != PA_OK) return st;
+  return pa::decode_launch(shape, 1, q, k_cache, v_cache, block_table, context_lens, scale, io_dtype,
+                           kv_dtype, k_scale, v_scale, ws, pa::kScratchBytes, pa::kScratchCounterBytes,
+                           out, lse_out, stream);
 }
 
 pa_status pa_workspace_reset(void* workspace, size_t workspace_bytes, void* stream) {
@@ -1648,6 +1712,7 @@ const char* pa_status_str(pa_status status) {
     case PA_ERR_HIP: return "the HIP runtime refused the launch";
     case PA_ERR_CAPACITY: return "not enough free blocks in the pool";
     case PA_ERR_STATE: return "unknown or already present sequence id";
+    case PA_ERR_SCRATCH: return "the call needs more scratch than the no-allocation entry point holds";
   }
   return "unknown status";
 }

@@ -128,7 +128,7 @@ def test_workspace_size_arithmetic():
 
 def test_status_strings():
     lib = _lib.load_library()
-    for code in range(9):
+    for code in range(10):
         assert lib.pa_status_str(code) and lib.pa_status_str(code) != b"unknown status"
     assert lib.pa_status_str(99) == b"unknown status"
 
@@ -262,6 +262,34 @@ def test_multi_token_rows_of_one_tile_take_the_decode_kernels():
 def torch_gpu_count():
     import torch
     return torch.cuda.device_count()
+
+
+def call_noalloc(s, io=1, kv=1, ks=None, vs=None, out=FAKE, q=FAKE, k=FAKE, v=FAKE, bt=FAKE,
+                 cl=FAKE, lse=None):
+    lib = _lib.load_library()
+    sp = ctypes.byref(s) if s is not None else None
+    return lib.pa_decode_noalloc(sp, q, k, v, bt, cl, 0.1, io, kv, ks, vs, out, lse, None)
+
+
+def test_noalloc_rejects_calls_beyond_its_scratch_before_any_launch():
+    assert call_noalloc(None) == 1
+    # 512-token partitions, 28/4 heads, 4096-token tables: partial results of
+    # 8 partitions x 7 rows x 129 floats per (sequence, KV head) pair; 16 MiB
+    # minus the 256 KiB counter region holds about 570 pairs, not 2400
+    big = shape(batch=600, num_q_heads=28, num_kv_heads=4, max_blocks_per_seq=256,
+                partition_size=512)
+    assert call_noalloc(big) == 9
+    # more counters than the counter region holds (16 partitions of 16
+    # tokens per sequence: one counter per pair, tiny partial results)
+    many = shape(batch=65535, num_q_heads=2, num_kv_heads=2, head_dim=64, max_blocks_per_seq=1,
+                 partition_size=16)
+    assert call_noalloc(many) == 9
+    for kw in ("q", "k", "v", "bt", "cl", "out"):       # argument checks as pa_decode
+        assert call_noalloc(shape(), **{kw: None}) == 1, kw
+    assert call_noalloc(shape(head_dim=96)) == 2
+    assert call_noalloc(shape(), io=1, kv=2) == 3
+    assert call_noalloc(shape(), q=FAKE + 8) == 5
+    assert call_noalloc(shape(batch=0)) == 0
 
 
 # ---- the binding's buffer checks, exercised on CPU tensors ------------------
