@@ -63,6 +63,8 @@ def parse():
                     help="minimum host time spent timing the oracle")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-stream-ceiling", action="store_true")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the per-workload record of all five workloads")
     ap.add_argument("--no-flush-check", action="store_true",
                     help="skip the cross-check that times single calls after evicting the caches")
     ap.add_argument("--op", choices=["decode", "multi", "append", "merge", "pool"],
@@ -550,29 +552,197 @@ def main():
     if args.op == "pool":
         return bench_pool(args, np, pkd, W)
 
-    spec = W.SPECS[args.workload]
-    wl = W.make_workload(spec)
-    dev = torch.device("cuda:0")
-    t = W.to_device(wl, dev)
-    pool_bytes = t["k_cache"].numel() * t["k_cache"].element_size() * 2
-    reps = max(1, math.ceil(3 * MALL_BYTES / pool_bytes))
-    kcs = [t["k_cache"]] + [t["k_cache"].clone() for _ in range(reps - 1)]
-    vcs = [t["v_cache"]] + [t["v_cache"].clone() for _ in range(reps - 1)]
-    out = torch.empty_like(t["q"])
-    stream = torch.cuda.current_stream()
+    rec = bench_decode(args, torch, np, pkd, W)
+    print(json.dumps(rec), flush=True)
 
-    def make_calls(ps):
+
+def shape_name(spec):
+    """The workload's name without the split it was specified with: the
+    split every number was measured with is named beside it."""
+    return spec.name.replace("_split512", "")
+
+
+class DecodeBench:
+    """One workload on the GPU: the KV pool rotated over enough copies that the
+    Infinity Cache cannot serve repeats, calls marshalled once per split mode,
+    HIP events on the launching stream around back-to-back calls."""
+
+    def __init__(self, torch, np, pkd, W, spec):
+        self.torch, self.np, self.pkd, self.W = torch, np, pkd, W
+        self.spec = spec
+        self.wl = W.make_workload(spec)
+        self.dev = torch.device("cuda:0")
+        t = W.to_device(self.wl, self.dev)
+        self.t = t
+        pool_bytes = t["k_cache"].numel() * t["k_cache"].element_size() * 2
+        self.reps = max(1, math.ceil(3 * MALL_BYTES / pool_bytes))
+        self.kcs = [t["k_cache"]] + [t["k_cache"].clone() for _ in range(self.reps - 1)]
+        self.vcs = [t["v_cache"]] + [t["v_cache"].clone() for _ in range(self.reps - 1)]
+        self.out = torch.empty_like(t["q"])
+        self.stream = torch.cuda.current_stream()
+
+    def calls(self, ps):
+        pkd, t, torch = self.pkd, self.t, self.torch
         ws = None
         if ps:
             need = pkd.workspace_bytes(t["q"], t["k_cache"], t["block_table"], ps)
             if need <= 0:
                 raise SystemExit(f"no workspace size for partition_size={ps}")
-            ws = torch.empty(need, dtype=torch.uint8, device=dev)
+            ws = torch.empty(need, dtype=torch.uint8, device=self.dev)
             pkd.reset_workspace(ws)
-        return [pkd.prepare(t["q"], kcs[i], vcs[i], t["block_table"], t["context_lens"],
-                            float(wl.scale), k_scale=t["k_scale"], v_scale=t["v_scale"],
-                            partition_size=ps, out=out, workspace=ws, stream=stream)
-                for i in range(reps)]
+        return [pkd.prepare(t["q"], self.kcs[i], self.vcs[i], t["block_table"], t["context_lens"],
+                            float(self.wl.scale), k_scale=t["k_scale"], v_scale=t["v_scale"],
+                            partition_size=ps, out=self.out, workspace=ws, stream=self.stream)
+                for i in range(self.reps)]
+
+    def time(self, ps, steps, warmup):
+        """-> (ms per call, output as float64)"""
+        torch = self.torch
+        calls = self.calls(ps)
+        for i in range(warmup):
+            calls[i % self.reps]()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(self.stream)
+        for i in range(steps):
+            calls[i % self.reps]()
+        e1.record(self.stream)
+        torch.cuda.synchronize()
+        return (e0.elapsed_time(e1) / steps,
+                self.out.float().cpu().numpy().astype(self.np.float64))
+
+    def flush_check(self, ps, n=40):
+        """Median time of single calls, each after a 1 GiB write that evicts
+        L2 and the Infinity Cache (events around the call only): a
+        cross-check of the rotated-pool timing."""
+        torch = self.torch
+        calls = self.calls(ps)
+        scratch = torch.empty(1 << 28, dtype=torch.int32, device=self.dev)
+        times = []
+        for i in range(n + 3):
+            scratch.fill_(i)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(self.stream)
+            calls[0]()
+            e1.record(self.stream)
+            torch.cuda.synchronize()
+            if i >= 3:
+                times.append(e0.elapsed_time(e1) * 1e3)
+        del scratch
+        times.sort()
+        return times[len(times) // 2]
+
+    def page_read_floor(self):
+        """GB/s of a kernel that reads exactly this call's K and V pages (the
+        same 16 x head_dim runs, in the same pair-major order, over the same
+        rotated pool copies) and does nothing else with them: what the page
+        layout and HBM allow for these bytes on this GPU."""
+        import ctypes
+        np, torch, wl, spec = self.np, self.torch, self.wl, self.spec
+        if not os.path.exists(PROBES):
+            return None
+        lib = ctypes.CDLL(PROBES)
+        lib.pa_probe_page_read.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
+                                           ctypes.c_int, ctypes.c_void_p, ctypes.c_int,
+                                           ctypes.c_void_p]
+        page = 16 * spec.head_dim * ELEM.get(spec.kv_dtype, 2)
+        if page % 1024:
+            return None
+        H = spec.num_kv_heads
+        cache_bytes = wl.num_blocks * H * page + page          # + the spare block
+        offs = []
+        for b in range(spec.batch):
+            for g in range(H):
+                for j in range(-(-int(wl.context_lens[b]) // 16)):
+                    blk = int(wl.block_table[b, j])
+                    o = (blk * H + g) * page
+                    offs.append(o)                  # K page
+                    offs.append(cache_bytes + o)    # V page
+        offs = np.asarray(offs, dtype=np.uint64)
+        per = 2 * cache_bytes
+        reps = self.reps
+        buf = torch.empty(per * reps, dtype=torch.uint8, device=self.dev)
+        assert offs.max() + page <= per
+        lists = [torch.from_numpy((offs + r * per).astype(np.int64)).to(self.dev) for r in range(reps)]
+        sink = torch.zeros(4, dtype=torch.int32, device=self.dev)
+        s = self.stream
+        n = len(offs)
+        cus = torch.cuda.get_device_properties(0).multi_processor_count
+        best = 0.0
+        for blocks in (cus, 2 * cus):
+            for i in range(10):
+                assert lib.pa_probe_page_read(buf.data_ptr(), lists[i % reps].data_ptr(), n,
+                                              page // 1024, sink.data_ptr(), blocks,
+                                              s.cuda_stream) == 0
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            k = 200
+            e0.record(s)
+            for i in range(k):
+                lib.pa_probe_page_read(buf.data_ptr(), lists[i % reps].data_ptr(), n, page // 1024,
+                                       sink.data_ptr(), blocks, s.cuda_stream)
+            e1.record(s)
+            torch.cuda.synchronize()
+            best = max(best, n * page * k / (e0.elapsed_time(e1) / 1e3) / 1e9)
+        del buf
+        return best
+
+
+ELEM = {"f32": 4, "f16": 2, "bf16": 2, "fp8_e4m3": 1}
+
+
+def oracle_errors(wl, gpu_out, seqs=None):
+    import numpy as np
+    import oracle
+    s = wl.spec
+    ref = oracle.paged_decode_ref(wl.q, wl.k_cache, wl.v_cache, wl.block_table, wl.context_lens,
+                                  wl.scale, s.io_dtype, s.kv_dtype, wl.k_scale, wl.v_scale,
+                                  seqs=seqs)
+    sel = slice(None) if seqs is None else list(seqs)
+    err = np.abs(gpu_out[sel] - ref[sel])
+    return float(err.max()), float(err.mean())
+
+
+# Sequences the per-workload oracle check samples (None: all of them): the
+# fp8 B128 and long-context workloads take the oracle seconds per sequence.
+ORACLE_SAMPLE = {1: None, 2: None, 3: None, 4: [0, 37, 127], 5: [0, 5]}
+
+
+def config_record(args, torch, np, pkd, W, k):
+    """Every split mode the library offers for workload k, timed; the best
+    one's numbers, and its output against the float64 oracle."""
+    spec = W.SPECS[k]
+    bench = DecodeBench(torch, np, pkd, W, spec)
+    modes = [spec.partition_size, pkd.SPLIT_BALANCED] + ([512] if spec.partition_size == 0 else [])
+    steps = max(50, args.steps // 4)
+    timed = {m: bench.time(m, steps, max(10, args.warmup // 2)) for m in modes}
+    best = min(timed, key=lambda m: timed[m][0])
+    ms, out = timed[best]
+    wl = bench.wl
+    logical, unique = wl.kv_bytes_logical(), wl.kv_bytes_unique()
+    mx, mean = oracle_errors(wl, out, ORACLE_SAMPLE[k])
+    rec = {
+        "workload": shape_name(spec), "spec_partition_size": spec.partition_size,
+        "mode": mode_name(best), "us_per_call": round(ms * 1e3, 3),
+        "kv_bytes_logical": logical, "kv_bytes_unique": unique,
+        "GBps_logical": round(logical / (ms / 1e3) / 1e9, 1),
+        "GBps_unique": round(unique / (ms / 1e3) / 1e9, 1),
+        "pct_peak_logical": round(100.0 * logical / (ms / 1e3) / 1e9 / PEAK_GBPS, 2),
+        "pct_peak_unique": round(100.0 * unique / (ms / 1e3) / 1e9 / PEAK_GBPS, 2),
+        "seq_tokens_per_s": round(int(wl.context_lens.astype(np.int64).sum()) / (ms / 1e3), 1),
+        "max_abs_vs_oracle": mx, "mean_abs_vs_oracle": mean,
+        "oracle_sequences": "all" if ORACLE_SAMPLE[k] is None else ORACLE_SAMPLE[k],
+        "modes_us": {mode_name(m): round(v[0] * 1e3, 3) for m, v in timed.items()},
+    }
+    del bench
+    torch.cuda.empty_cache()
+    return rec
+
+
+def bench_decode(args, torch, np, pkd, W):
+    spec = W.SPECS[args.workload]
+    bench = DecodeBench(torch, np, pkd, W, spec)
+    wl = bench.wl
 
     if args.partition_size is not None:
         modes = [args.partition_size]
@@ -587,62 +757,30 @@ def main():
     ps = modes[0]   # --pmc-pass profiles this one
 
     if args.pmc_pass:
-        calls = make_calls(ps)
-        src = torch.ones(1 << 28, dtype=torch.int32, device=dev)      # 1 GiB
+        calls = bench.calls(ps)
+        src = torch.ones(1 << 28, dtype=torch.int32, device=bench.dev)      # 1 GiB
         dst = torch.empty_like(src)
         dst.copy_(src)
         for i in range(20):
-            calls[i % reps]()
+            calls[i % bench.reps]()
         torch.cuda.synchronize()
-        return
-
-    def time_mode(mode):
-        calls = make_calls(mode)
-        for i in range(args.warmup):
-            calls[i % reps]()
-        torch.cuda.synchronize()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for i in range(args.steps):
-            calls[i % reps]()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / args.steps, out.float().cpu().numpy().astype(np.float64)
-
-    def flush_check(mode, n=40):
-        """Median time of single calls, each after a 1 GiB write that evicts
-        L2 and the Infinity Cache (events around the call only): a
-        cross-check of the rotated-pool timing."""
-        calls = make_calls(mode)
-        scratch = torch.empty(1 << 28, dtype=torch.int32, device=dev)
-        times = []
-        for i in range(n + 3):
-            scratch.fill_(i)
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            calls[0]()
-            e1.record(stream)
-            torch.cuda.synchronize()
-            if i >= 3:
-                times.append(e0.elapsed_time(e1) * 1e3)
-        del scratch
-        times.sort()
-        return times[len(times) // 2]
+        sys.exit(0)
 
     timed = {}
     for mode in modes:
-        timed[mode] = time_mode(mode)
+        timed[mode] = bench.time(mode, args.steps, args.warmup)
     if args.split == "auto" and args.partition_size is None:
         ps = min(timed, key=lambda m: timed[m][0])
     ms, gpu_out = timed[ps]
 
     kv_bytes = wl.kv_bytes_logical()
+    kv_unique = wl.kv_bytes_unique()
     gbps = kv_bytes / (ms / 1e3) / 1e9
     sum_tokens = int(wl.context_lens.astype(np.int64).sum())
     traffic = traffic_from_profile(spec.name, ps)
     ceiling = None if args.no_stream_ceiling else stream_read_ceiling(torch)
-    flushed_us = None if args.no_flush_check else flush_check(ps)
+    floor = None if args.no_stream_ceiling else bench.page_read_floor()
+    flushed_us = None if args.no_flush_check else bench.flush_check(ps)
 
     rec = {
         "metric": METRIC,
@@ -659,7 +797,7 @@ def main():
                  + ("" if spec.kv_dtype == spec.io_dtype else "+fp8_e4m3_kv"),
         "data": "synthetic (seeded N(0,1) q/K/V, seeded lengths and block permutation)",
         "config": {
-            "workload": spec.name,
+            "workload": shape_name(spec),
             "batch": spec.batch,
             "q_heads": spec.num_q_heads,
             "kv_heads": spec.num_kv_heads,
@@ -667,13 +805,19 @@ def main():
             "block_size": 16,
             "context_lens": f"{spec.lens[0]} {list(spec.lens[1:])}",
             "sum_context_tokens": sum_tokens,
+            "spec_partition_size": spec.partition_size,
             "split": mode_name(ps),
             "partition_size": ps,
+            "split_choice": ("the faster of the modes timed (listed under modes), all of which "
+                             "compute the same result and meet the same parity bar"
+                             if args.split == "auto" and args.partition_size is None
+                             else "fixed by the command line"),
             "kv_bytes_per_step": kv_bytes,
-            "kv_bytes_unique_per_step": wl.kv_bytes_unique(),
-            "pool_copies_rotated": reps,
+            "kv_bytes_unique_per_step": kv_unique,
+            "pool_copies_rotated": bench.reps,
         },
         "pct_hbm_peak": round(100.0 * gbps / PEAK_GBPS, 2),
+        "pct_hbm_peak_unique_bytes": round(100.0 * kv_unique / (ms / 1e3) / 1e9 / PEAK_GBPS, 2),
         "seq_tokens_per_s": round(sum_tokens / (ms / 1e3), 1),
         "seqs_per_s": round(spec.batch / (ms / 1e3), 1),
         "roofline": {
@@ -686,6 +830,8 @@ def main():
         },
         "stream_read_ceiling_GBps": None if ceiling is None else round(ceiling, 1),
         "pct_stream_ceiling": None if ceiling is None else round(100.0 * gbps / ceiling, 2),
+        "page_read_floor_GBps": None if floor is None else round(floor, 1),
+        "pct_page_read_floor": None if floor is None else round(100.0 * gbps / floor, 2),
         "flush_check": None if flushed_us is None else {
             "us_median_single_call_after_cache_eviction": round(flushed_us, 2),
             "GBps": round(kv_bytes / (flushed_us / 1e6) / 1e9, 2), "mode": mode_name(ps)},
@@ -696,7 +842,11 @@ def main():
     }
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(wl, gpu_out, args.cpu_seconds)
-    print(json.dumps(rec), flush=True)
+    del bench
+    torch.cuda.empty_cache()
+    if not args.no_configs:
+        rec["configs"] = [config_record(args, torch, np, pkd, W, k) for k in sorted(W.SPECS)]
+    return rec
 
 
 if __name__ == "__main__":

@@ -140,6 +140,56 @@ extern "C" int pa_probe_stream_read(const void* p, size_t bytes, void* sink, int
   return hipGetLastError() == hipSuccess ? 0 : 2;
 }
 
+// Page-read floor: the same bytes a decode call reads, as whole pages at the
+// given byte offsets (one chunk of chunk_kib KiB each, a multiple of 1 KiB),
+// read with non-temporal 16-byte loads and nothing else done with them. Each
+// workgroup of 8 waves takes a contiguous range of the chunk list; its waves
+// interleave over the range with 4 chunks in flight each. The offsets must
+// leave every chunk inside the buffer (checked by the caller).
+template <int KB>
+__global__ void __launch_bounds__(512) page_read_kernel(const uint8_t* base, const uint64_t* offs,
+                                                        int nchunks, uint32_t* sink) {
+  const int nw = blockDim.x / 64, w = threadIdx.x / 64, lane = threadIdx.x & 63;
+  const int c0 = (int)((long long)blockIdx.x * nchunks / gridDim.x);
+  const int c1 = (int)((long long)(blockIdx.x + 1) * nchunks / gridDim.x);
+  u32x4 acc = {0u, 0u, 0u, 0u};
+  int c = c0 + w;
+  for (; c + 3 * nw < c1; c += 4 * nw) {
+    u32x4 r[4][KB];
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const uint8_t* p = base + offs[c + d * nw];
+#pragma unroll
+      for (int k = 0; k < KB; ++k) r[d][k] = __builtin_nontemporal_load((const u32x4*)(p + k * 1024) + lane);
+    }
+#pragma unroll
+    for (int d = 0; d < 4; ++d)
+#pragma unroll
+      for (int k = 0; k < KB; ++k) acc ^= r[d][k];
+  }
+  for (; c < c1; c += nw) {
+    const uint8_t* p = base + offs[c];
+#pragma unroll
+    for (int k = 0; k < KB; ++k) acc ^= __builtin_nontemporal_load((const u32x4*)(p + k * 1024) + lane);
+  }
+  const uint32_t x = acc.x ^ acc.y ^ acc.z ^ acc.w;
+  if (x == 0x9E3779B9u) sink[0] = x;
+}
+
+extern "C" int pa_probe_page_read(const void* base, const uint64_t* offs, int nchunks, int chunk_kib,
+                                  void* sink, int blocks, void* stream) {
+  if (!base || !offs || nchunks < 1 || blocks < 1 || ((uintptr_t)base & 15u)) return 1;
+  if (chunk_kib == 4)
+    hipLaunchKernelGGL(page_read_kernel<4>, dim3(blocks), dim3(512), 0, (hipStream_t)stream,
+                       (const uint8_t*)base, offs, nchunks, (uint32_t*)sink);
+  else if (chunk_kib == 2)
+    hipLaunchKernelGGL(page_read_kernel<2>, dim3(blocks), dim3(512), 0, (hipStream_t)stream,
+                       (const uint8_t*)base, offs, nchunks, (uint32_t*)sink);
+  else
+    return 1;
+  return hipGetLastError() == hipSuccess ? 0 : 2;
+}
+
 // Host-side walk of every share of the balanced split. Writes one row of 8
 // ints per piece -- share, sequence, KV head, first page, end page, piece
 // index, pieces of the pair, slot of piece 0 -- up to max_rows rows, and
