@@ -1142,82 +1142,79 @@ __device__ __forceinline__ void decode_quarter(const Params& a, const BalSm<D>& 
 // for as well).
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-// Combine, for the np pieces of the share that lead in LDS (candidate slots
-// c = 2 * wave + slot in the bit mask lead, in line order), the slots of the
-// waves holding each: slot c & 1 of wave wa = c >> 1, then slot 0 of every
-// later wave of the share the pair reaches (yqv: the quarter starts). Write
-// the output of a pair whose pieces are all in this share, else the piece's
-// partial result to its workspace slot. Threads take (piece, row, 4-float
-// quad) items two at a time, a piece's items filling whole waves so that the
-// piece is uniform across a wave; the LDS reads of both items are issued
-// before any arithmetic.
+// Per candidate slot c = 2 * wave + slot, what the combine needs of the piece
+// it leads, one value per lane c < 2 * kWaves (taken with readlane).
+struct SlotFacts {
+  int b, g;     // the pair
+  int vmul;     // output multiplier (v_scale), float bits
+  int parts;    // pieces of the pair over the shares (1: the pair is whole here)
+  int slot;     // workspace slot of this piece
+  int hold;     // waves holding the piece: bit wave c >> 1, and bit w of every
+                // later wave whose quarter the pair reaches (its slot 0)
+};
+
+// Combine, for every piece of the share that leads in LDS (candidate slots c
+// in the bit mask lead), the slots of the waves holding it, and write the
+// pair's output (a pair whose pieces are all in this share) or the piece's
+// partial result to its workspace slot. One piece at a time, uniform across
+// the workgroup; its G x D/4 (row, 4-float quad) items at most two per
+// thread (G <= 16), every LDS read of both issued before any arithmetic, so a
+// piece costs one LDS round trip.
 template <typename IO, typename KV, int D, bool MQ>
-__device__ __forceinline__ void combine_pieces(const Params& a, const BalSm<D>& sm, uint32_t lead, int np,
-                                               const int* yqv) {
+__device__ __forceinline__ void combine_pieces(const Params& a, const BalSm<D>& sm, uint32_t lead,
+                                               const SlotFacts& f) {
   constexpr int kQuads = D / 4;
+  static_assert(kMaxGroup * kQuads <= 2 * kThreads, "two items per thread cover a piece");
   const int tid = threadIdx.x;
   const int G = a.group;
-  const int npair = G * kQuads;
-  const int npad = (npair + 63) & ~63;
-  const int total = np * npad;
-  for (int base = 0; base < total; base += 2 * kThreads) {
-    // every LDS read of both items first (one wave per SIMD: nothing else
-    // hides their latency), then the arithmetic
+  const int items = G * kQuads;
+  for (uint32_t mk = lead; mk; mk &= mk - 1) {
+    const int c = __builtin_ctz(mk);   // uniform
+    const int wa = c >> 1, sa = c & 1;
+    const int b = __builtin_amdgcn_readlane(f.b, c);
+    const int g = __builtin_amdgcn_readlane(f.g, c);
+    const float vmul = __builtin_bit_cast(float, __builtin_amdgcn_readlane(f.vmul, c));
+    const int nparts = __builtin_amdgcn_readlane(f.parts, c);
+    const int wslot = __builtin_amdgcn_readlane(f.slot, c);
+    const int hold = __builtin_amdgcn_readlane(f.hold, c);
     bool on[2];
-    int c[2], h[2], d[2], bd[2][kWaves];
-    u32x4 me[2][2];
+    int h[2], d[2], bd[kWaves];
     float mv[2][kWaves], lv[2][kWaves];
     f32x4 av[2][kWaves];
 #pragma unroll
+    for (int ww = 0; ww < kWaves; ++ww) bd[ww] = sm.bad[ww * 2 + (ww == wa ? sa : 0)];
+#pragma unroll
     for (int u = 0; u < 2; ++u) {
-      const int idx = base + u * kThreads + tid;
-      const int j = __builtin_amdgcn_readfirstlane(idx / npad);   // uniform: npad % 64 == 0
-      const int pair = idx - j * npad;
-      on[u] = j < np && pair < npair;
-      // the j-th set bit of lead (the last one for items past the pieces)
-      uint32_t mk = lead;
-      for (int i = 0; i < j && i < np - 1; ++i) mk &= mk - 1;
-      c[u] = __builtin_ctz(mk);
-      h[u] = on[u] ? pair / kQuads : 0;
-      d[u] = 4 * (pair - (pair / kQuads) * kQuads);
-      const u32x4* e = reinterpret_cast<const u32x4*>(sm.pm + c[u] * kPieceMeta);
-      me[u][0] = e[0];
-      me[u][1] = e[1];
+      const int i = tid + u * kThreads;
+      on[u] = i < items;
+      h[u] = on[u] ? i / kQuads : 0;
+      d[u] = on[u] ? 4 * (i - h[u] * kQuads) : 0;
 #pragma unroll
       for (int ww = 0; ww < kWaves; ++ww) {
-        const int sl = ww == (c[u] >> 1) ? (c[u] & 1) : 0;
-        bd[u][ww] = sm.bad[ww * 2 + sl];
+        const int sl = ww == wa ? sa : 0;
         mv[u][ww] = sm.m[sm.mi(ww, sl, h[u])];
         lv[u][ww] = sm.l[sm.mi(ww, sl, h[u])];
         av[u][ww] = *reinterpret_cast<const f32x4*>(sm.acc_row(ww, sl, h[u]) + d[u]);
       }
     }
+    int bad = 0;
+#pragma unroll
+    for (int ww = 0; ww < kWaves; ++ww)
+      if ((hold >> ww) & 1) bad |= bd[ww];
+    const brsrc wr_slot = buffer_rsrc(a.ws_o + (size_t)wslot * G * D, (uint32_t)(G * D * sizeof(float)));
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       if (!on[u]) continue;
-      const int wa = c[u] >> 1;
-      const int b = __builtin_amdgcn_readfirstlane((int)me[u][0][kPmB]);
-      const int g = __builtin_amdgcn_readfirstlane((int)me[u][0][kPmG]);
-      const int pend = __builtin_amdgcn_readfirstlane((int)me[u][0][kPmEnd]);
-      const float vmul = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane((int)me[u][0][kPmVmul]));
-      const int nparts = __builtin_amdgcn_readfirstlane((int)me[u][1][kPmParts - 4]);
-      bool hold[kWaves];
-      int bad = 0;
       float M = -INFINITY;
 #pragma unroll
-      for (int ww = 0; ww < kWaves; ++ww) {
-        hold[ww] = ww == wa || (ww > wa && pend > yqv[ww]);
-        if (hold[ww]) {
-          bad |= bd[u][ww];
-          M = fmaxf(M, mv[u][ww]);
-        }
-      }
+      for (int ww = 0; ww < kWaves; ++ww)
+        if ((hold >> ww) & 1) M = fmaxf(M, mv[u][ww]);
       float W = 0.f;
       f32x4 o = {0.f, 0.f, 0.f, 0.f};
       const float Ms = (MQ && M == -INFINITY) ? 0.f : M;   // MQ: a row may see nothing here
 #pragma unroll
       for (int ww = 0; ww < kWaves; ++ww) {
-        if (hold[ww]) {
+        if ((hold >> ww) & 1) {
           const float ex = exp2_fast(mv[u][ww] - Ms);
           W += ex * lv[u][ww];
           o += ex * av[u][ww];
@@ -1242,11 +1239,8 @@ __device__ __forceinline__ void combine_pieces(const Params& a, const BalSm<D>& 
         store_out4<IO>(a.out, row * D + d[u], val);
         if (d[u] == 0 && a.lse_out) a.lse_out[row] = lse2 * kLn2;
       } else {
-        const size_t slot = (size_t)__builtin_amdgcn_readfirstlane((int)me[u][1][kPmSlot0 - 4]) +
-                            __builtin_amdgcn_readfirstlane((int)me[u][1][kPmK - 4]);
-        const brsrc wr_slot = buffer_rsrc(a.ws_o + slot * G * D, (uint32_t)(G * D * sizeof(float)));
         st_agent4(wr_slot, (uint32_t)((h[u] * D + d[u]) * sizeof(float)), val);
-        if (d[u] == 0) st_agent(a.ws_lse + slot * G + h[u], lse2);
+        if (d[u] == 0) st_agent(a.ws_lse + (size_t)wslot * G + h[u], lse2);
       }
     }
   }
@@ -1337,7 +1331,24 @@ pa_decode_balanced_kernel(const Params a) {
   const uint32_t lead = (uint32_t)__ballot(lane < 2 * kWaves && (fl & kPmLead)) & 0xffu;
   const uint32_t split = (uint32_t)__ballot(lane < 2 * kWaves && (fl & kPmLead) && parts > 1) & 0xffu;
   if (lead == 0) return;   // uniform
-  combine_pieces<IO, KV, D, MQ>(a, sm, lead, __builtin_popcount(lead), yqv);
+  SlotFacts facts;
+  facts.b = rb;
+  facts.g = rg;
+  facts.vmul = rec[kPmVmul];
+  facts.parts = parts;
+  facts.slot = rs0 + rec[kPmK];
+  {
+    // the waves holding the piece slot cl leads: its own, and every later
+    // one whose quarter starts before the pair's end (it holds the pair in
+    // its slot 0)
+    const int wa = cl >> 1, pend = rec[kPmEnd];
+    int hold = 1 << wa;
+#pragma unroll
+    for (int ww = 1; ww < kWaves; ++ww)
+      if (ww > wa && pend > yqv[ww]) hold |= 1 << ww;
+    facts.hold = hold;
+  }
+  combine_pieces<IO, KV, D, MQ>(a, sm, lead, facts);
   if (split == 0) return;   // uniform
   __builtin_amdgcn_s_waitcnt(0);   // this wave's partial stores are complete
   __syncthreads();
