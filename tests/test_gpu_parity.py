@@ -1,9 +1,18 @@
 """Parity of the HIP path (through the C ABI) with the float64 oracle, plus the
 invariants and edge cases of the method, on an MI355X.
 
-Bar: q/out in f32, f16 or bf16: max-abs <= 1e-2 and mean-abs <= 1e-3 against
-the oracle; fp8-e4m3 cache: max-abs <= 3e-2 against the oracle on the same
-dequantized values (mean-abs reported, and held to 3e-3).
+Bar, against the oracle on the same stored (and, for fp8, dequantized) values:
+every case meets the stated contract -- q/out in f32, f16 or bf16: max-abs <=
+1e-2 and mean-abs <= 1e-3; fp8-e4m3 cache: max-abs <= 3e-2 -- and the tighter
+of that and a bar set by the arithmetic of the io type. P is rounded to the io
+type for the PV product (the running sum adds the same rounded values) and the
+output once more at the end, so with unit roundoff u and |v| <= about 4.5 for
+N(0,1) data the error is at most about u * (4.5 + 1): f32 (nothing rounded but
+fp32 sums) max-abs 1e-5, mean 1e-6; f16 (u = 2^-11, 2.7e-3) 4e-3, 3e-4; bf16
+(u = 2^-8, 2.1e-2) 2.5e-2, 1.5e-3. An fp8 cache widens exactly, so it takes
+its io type's bar. The largest errors seen on MI355X are 6.7e-7 (f32), 1.0e-3
+(f16), 9.4e-3 (bf16, contexts of a few tokens) and 1.4e-2 (bf16 q, fp8 cache,
+two new tokens per sequence).
 """
 import numpy as np
 import pytest
@@ -16,12 +25,18 @@ from tests.gpu_util import errors, to_device, to_f64
 
 pytestmark = pytest.mark.gpu
 
-TOL = {"max": 1e-2, "mean": 1e-3}
-TOL_FP8 = {"max": 3e-2, "mean": 3e-3}
+TOL = {"max": 1e-2, "mean": 1e-3}          # the contract for f32/f16/bf16 caches
+TOL_FP8 = {"max": 3e-2, "mean": 3e-3}      # the contract for an fp8 cache (mean reported)
+# the io type's arithmetic (module docstring); each is within the contract
+TIGHT = {"f32": {"max": 1e-5, "mean": 1e-6}, "f16": {"max": 4e-3, "mean": 3e-4},
+         "bf16": {"max": 2.5e-2, "mean": 1.5e-3}}
 
 
 def tol(spec):
-    return TOL_FP8 if spec.kv_dtype == "fp8_e4m3" else TOL
+    """The tighter of the contract and the io type's bar."""
+    c = TOL_FP8 if spec.kv_dtype == "fp8_e4m3" else TOL
+    t = TIGHT[spec.io_dtype]
+    return {"max": min(c["max"], t["max"]), "mean": min(c["mean"], t["mean"])}
 
 
 def run(wl, t=None, partition_size=None, lse=False, workspace=None, stream=None):
@@ -152,6 +167,17 @@ def test_two_level_merge(io, kv):
 
 
 # ------------------------------------------------------ full-size workloads
+
+@pytest.mark.parametrize("ps", [512, pkd.SPLIT_BALANCED])
+def test_full_size_qwen2_5_1_5b_shape_in_the_split_modes_bench_times(ps):
+    # The Qwen2.5-1.5B-shaped workload is specified as one pass, but bench.py
+    # also times (and may report) 512-token partitions and the balanced split.
+    spec = W.SPECS[2]
+    print(f"case full workload 2 with partition_size {ps}", flush=True)
+    wl = W.make_workload(spec)
+    out = to_f64(run(wl, partition_size=ps))
+    check(wl, out, ref(wl), label=f"full2 ps={ps}")
+
 
 
 

@@ -15,7 +15,7 @@ import oracle
 import paged_kv_decode_05_amd as pkd
 from paged_kv_decode_05_amd import workloads as W
 from tests.gpu_util import errors, to_device, to_f64
-from tests.test_gpu_parity import TOL, TOL_FP8
+from tests.test_gpu_parity import tol as parity_tol
 
 pytestmark = pytest.mark.gpu
 
@@ -72,7 +72,7 @@ def test_random_configuration(seed):
     got = to_f64(out)
     assert np.isfinite(got).all(), spec.name
     mx, mean = errors(got, exp)
-    tol = TOL_FP8 if spec.kv_dtype == "fp8_e4m3" else TOL
+    tol = parity_tol(spec)
     print(f"  max-abs {mx:.3e} mean-abs {mean:.3e}", flush=True)
     assert mx <= tol["max"] and mean <= tol["mean"], (spec.name, mx, mean)
     l = lse.cpu().numpy().astype(np.float64)
