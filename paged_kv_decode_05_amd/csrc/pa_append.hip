@@ -20,10 +20,11 @@
 #include <type_traits>
 
 #include "padecode.h"
+#include "pa_host.h"
 
 namespace pa_append {
 
-constexpr int kBlock = 16;
+constexpr int kBlock = pa_host::kPageTokens;
 
 struct F32 {};
 struct F16 {};
@@ -127,23 +128,11 @@ extern "C" pa_status pa_kv_append(const pa_shape* s, const void* k_new, const vo
                                   const float* v_scale, void* k_cache, void* v_cache,
                                   void* stream) {
   using namespace pa_append;
-  if (!s) return PA_ERR_NULL;
-  if (s->batch < 0 || s->num_kv_heads < 1 || s->num_kv_heads > 65535) return PA_ERR_SHAPE;
-  if (s->head_dim != 64 && s->head_dim != 128) return PA_ERR_SHAPE;
-  if (s->block_size != kBlock || s->max_blocks_per_seq < 1 || s->max_blocks_per_seq > (1 << 26) ||
-      s->num_blocks < 1)
-    return PA_ERR_SHAPE;
-  if ((long long)s->batch * s->num_kv_heads > 0x7fffffffLL) return PA_ERR_SHAPE;
-  if (!k_new || !v_new || !positions || !block_table || !k_cache || !v_cache) return PA_ERR_NULL;
-  const bool src_ok = src_dtype == PA_F32 || src_dtype == PA_F16 || src_dtype == PA_BF16;
-  if (!src_ok || (kv_dtype != src_dtype && kv_dtype != PA_FP8_E4M3)) return PA_ERR_DTYPE;
-  if (kv_dtype == PA_FP8_E4M3 && (!k_scale || !v_scale)) return PA_ERR_NULL;
-  const uintptr_t es = src_dtype == PA_F32 ? 4 : 2;
-  if (((uintptr_t)k_new | (uintptr_t)v_new) % es) return PA_ERR_ALIGN;
-  if (((uintptr_t)k_cache | (uintptr_t)v_cache) & 15u) return PA_ERR_ALIGN;
-  if (((uintptr_t)positions | (uintptr_t)block_table) & 3u) return PA_ERR_ALIGN;
-  if (kv_dtype == PA_FP8_E4M3 && (((uintptr_t)k_scale | (uintptr_t)v_scale) & 3u)) return PA_ERR_ALIGN;
-  if (s->batch == 0) return PA_OK;
+  unsigned grid = 0;
+  const pa_status status = pa_host::append_status(s, k_new, v_new, positions, block_table, src_dtype,
+                                                  kv_dtype, k_scale, v_scale, k_cache, v_cache, &grid);
+  if (status != PA_OK) return status;
+  if (grid == 0) return PA_OK;
 
   Params p;
   p.k_new = static_cast<const uint8_t*>(k_new);
@@ -157,7 +146,6 @@ extern "C" pa_status pa_kv_append(const pa_shape* s, const void* k_new, const vo
   p.num_kv_heads = s->num_kv_heads;
   p.max_blocks_per_seq = s->max_blocks_per_seq;
   p.num_blocks = s->num_blocks;
-  const unsigned grid = (unsigned)((long long)s->batch * s->num_kv_heads);
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int D = s->head_dim;
   hipError_t e;

@@ -47,6 +47,7 @@
 #include <type_traits>
 
 #include "padecode.h"
+#include "pa_host.h"
 #include "pa_internal.h"
 #include "pa_schedule.h"
 #include "pa_tiles.h"
@@ -716,7 +717,10 @@ pa_decode_kernel(const Params a) {
 // completes are merged together in one pass.
 // ---------------------------------------------------------------------------
 constexpr int kScanPerThread = 16;
-constexpr int kBalancedMaxBatch = kThreads * kScanPerThread;
+constexpr int kBalancedMaxBatch = pa_host::kBalancedMaxBatch;
+static_assert(kBlock == pa_host::kPageTokens && kLineBlock == pa_host::kPageTokens, "page size");
+static_assert(kMaxGroup == pa_host::kMaxGroup, "group limit");
+static_assert(kBalancedMaxBatch <= kThreads * kScanPerThread, "the scan covers the batch");
 static_assert(kMinSharePages >= kWaves, "a share gives every wave a page");
 
 // Per-position facts in a lane's meta word.
@@ -1398,15 +1402,6 @@ __global__ void fill_zero_kernel(uint8_t* p, size_t n) {
 // ---------------------------------------------------------------------------
 // Host side.
 // ---------------------------------------------------------------------------
-struct WsLayout {
-  size_t o_off, lse_off, cnt_off, total;
-  int p_max, fan, g_max;
-  size_t cnt_bytes;   // bytes of counters the call uses (from cnt_off)
-};
-
-
-static inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
-
 // Shares of the balanced split per CU. One share (one workgroup of four
 // waves with deep register rings) per CU measured as fast as two or three on
 // MI355X at streaming and faster overall: every share pays a fixed cost at
@@ -1422,65 +1417,6 @@ static int balanced_shares() {
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return -1;
   if (cus <= 0 || cus > 4096) return -1;
   return cus * kWgPerCu;
-}
-
-static bool shape_ok(const pa_shape* s) {
-  if (!s) return false;
-  if (s->batch < 0 || s->batch > 65535) return false;
-  if (s->num_kv_heads < 1 || s->num_kv_heads > 65535) return false;
-  if (s->num_q_heads < 1 || s->num_q_heads % s->num_kv_heads != 0) return false;
-  if (s->num_q_heads / s->num_kv_heads > kMaxGroup) return false;
-  if (s->head_dim != 64 && s->head_dim != 128) return false;
-  if (s->block_size != kBlock) return false;
-  if (s->max_blocks_per_seq < 1 || s->max_blocks_per_seq > (1 << 26)) return false;
-  if (s->num_blocks < 1) return false;
-  if (s->partition_size == PA_SPLIT_BALANCED) {
-    // the workgroup-wide scan covers the batch, and line positions fit int32
-    if (s->batch > kBalancedMaxBatch) return false;
-    const long long line = (long long)s->batch * s->num_kv_heads * s->max_blocks_per_seq;
-    return line + 4096LL * 3 < 0x7fffffffLL;   // + shares (4096 CUs at most, 3 per CU)
-  }
-  if (s->partition_size < 0 || s->partition_size % kBlock != 0) return false;
-  // work units B * Hkv * partitions, and the partition and group slots, must
-  // fit a 1-D grid and int32 slot numbers
-  const long long parts =
-      s->partition_size ? ((long long)s->max_blocks_per_seq * kBlock + s->partition_size - 1) / s->partition_size : 1;
-  const int fan = merge_fan(parts);
-  const long long groups = fan ? (parts + fan - 1) / fan : 0;
-  if ((long long)s->batch * s->num_kv_heads * (parts + groups) > 0x7fffffffLL) return false;
-  return true;
-}
-
-// shares: the balanced split's workgroup count (ignored otherwise); q_len:
-// new tokens per sequence (rows per pair = group * q_len); cnt_region: 0 to
-// pack the counters first (rounded up to 256 bytes), else the partial results
-// start at that fixed byte offset, so counters and partials of calls of any
-// shape never overlap (the no-allocation entry point's scratch).
-static WsLayout ws_layout(const pa_shape* s, int shares, int q_len, size_t cnt_region = 0) {
-  WsLayout w{0, 0, 0, 0, 1, 0, 0, 0};
-  if (s->partition_size == 0) return w;
-  const size_t nbg = (size_t)s->batch * s->num_kv_heads;
-  size_t slots;
-  if (s->partition_size == PA_SPLIT_BALANCED) {
-    w.p_max = 0;
-    slots = (size_t)shares + nbg;
-  } else {
-    const long long tokens = (long long)s->max_blocks_per_seq * kBlock;
-    w.p_max = (int)((tokens + s->partition_size - 1) / s->partition_size);
-    w.fan = merge_fan(w.p_max);
-    w.g_max = w.fan ? (w.p_max + w.fan - 1) / w.fan : 0;
-    slots = nbg * (w.p_max + w.g_max);   // partition slots, then group slots
-  }
-  const size_t rows = slots * (size_t)(s->num_q_heads / s->num_kv_heads) * q_len;
-  // counters first (one per (b, g), then g_max per (b, g)): every completed
-  // call leaves them zero, so a later call whose counters fit in the same
-  // bytes finds them zero
-  w.cnt_off = 0;
-  w.cnt_bytes = nbg * (1 + (size_t)w.g_max) * sizeof(uint32_t);
-  w.o_off = cnt_region ? cnt_region : align_up(w.cnt_bytes, 256);
-  w.lse_off = w.o_off + align_up(rows * s->head_dim * sizeof(float), 256);
-  w.total = w.lse_off + align_up(rows * sizeof(float), 256);
-  return w;
 }
 
 template <typename IO, typename KV, int D, bool MQ>
@@ -1499,58 +1435,45 @@ static hipError_t launch_d(int D, const Params& prm, dim3 grid, bool balanced, h
                  : launch<IO, KV, 128, MQ>(prm, grid, balanced, stream);
 }
 
-static inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
-
 }  // namespace pa
 
 namespace pa {
 
 size_t decode_workspace_bytes(const pa_shape* shape, int q_len) {
-  if (!shape_ok(shape) || q_len < 1) return 0;
+  if (!pa_host::decode_shape_ok(shape) || q_len < 1) return 0;
   if ((long long)(shape->num_q_heads / shape->num_kv_heads) * q_len > kTileRows) return 0;
   int shares = 0;
   if (shape->partition_size == PA_SPLIT_BALANCED) {
     shares = balanced_shares();
     if (shares < 0) return 0;
   }
-  return ws_layout(shape, shares, q_len).total;
+  return pa_host::decode_layout(shape, shares, q_len).total;
 }
 
 // cnt_region: 0 for a caller's workspace (counters packed first), else the
-// fixed counter region of the no-allocation scratch (see ws_layout).
+// fixed counter region of the no-allocation scratch (see decode_layout).
 static pa_status decode_launch(const pa_shape* shape, int q_len, const void* q, const void* k_cache,
                                const void* v_cache, const int32_t* block_table,
                                const int32_t* context_lens, float scale, pa_dtype io_dtype,
                                pa_dtype kv_dtype, const float* k_scale, const float* v_scale,
                                void* workspace, size_t workspace_bytes, size_t cnt_region,
                                void* out, float* lse_out, void* stream) {
-  if (!shape) return PA_ERR_NULL;
-  if (!shape_ok(shape) || q_len < 1) return PA_ERR_SHAPE;
+  pa_status st = pa_host::decode_shape_status(shape, q_len);
+  if (st != PA_OK) return st;
+  st = pa_host::io_args_status(q, k_cache, v_cache, block_table, context_lens, io_dtype, kv_dtype,
+                               k_scale, v_scale, out, lse_out);
+  if (st != PA_OK) return st;
   const int G = shape->num_q_heads / shape->num_kv_heads;
-  if ((long long)G * q_len > kTileRows) return PA_ERR_SHAPE;
-  if ((long long)shape->batch * q_len * shape->num_q_heads > 0x7fffffffLL) return PA_ERR_SHAPE;
-  if (!q || !k_cache || !v_cache || !block_table || !context_lens || !out) return PA_ERR_NULL;
-  const bool io_ok = io_dtype == PA_F32 || io_dtype == PA_F16 || io_dtype == PA_BF16;
-  const bool kv_ok = kv_dtype == io_dtype || (kv_dtype == PA_FP8_E4M3 && io_dtype != PA_F32);
-  if (!io_ok || !kv_ok) return PA_ERR_DTYPE;
-  if (kv_dtype == PA_FP8_E4M3 && (!k_scale || !v_scale)) return PA_ERR_NULL;
-  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out))
-    return PA_ERR_ALIGN;
-  if (((uintptr_t)block_table & 3u) || ((uintptr_t)context_lens & 3u) ||
-      ((uintptr_t)lse_out & 3u))
-    return PA_ERR_ALIGN;
   const bool balanced = shape->partition_size == PA_SPLIT_BALANCED;
   int shares = 0;
   if (balanced) {
     shares = balanced_shares();
     if (shares < 0) return PA_ERR_HIP;
   }
-  const WsLayout wl = ws_layout(shape, shares, q_len, cnt_region);
-  if (shape->partition_size != 0) {
-    if (cnt_region && (wl.cnt_bytes > cnt_region || wl.total > workspace_bytes)) return PA_ERR_SCRATCH;
-    if (!workspace || workspace_bytes < wl.total) return PA_ERR_WORKSPACE;
-    if ((uintptr_t)workspace & 255u) return PA_ERR_ALIGN;
-  }
+  const pa_host::DecodeLayout wl = pa_host::decode_layout(shape, shares, q_len, cnt_region);
+  st = pa_host::workspace_status(shape->partition_size, wl.total, wl.cnt_bytes, cnt_region, workspace,
+                                 workspace_bytes);
+  if (st != PA_OK) return st;
   if (shape->batch == 0) return PA_OK;
 
   Params prm;
@@ -1583,29 +1506,28 @@ static pa_status decode_launch(const pa_shape* shape, int q_len, const void* q, 
   prm.gq = G;
 
   // 1-D grid: one workgroup per unit, or one per share (see the kernels)
-  const long long nbg = (long long)shape->batch * shape->num_kv_heads;
-  const dim3 grid(balanced ? (unsigned)shares : (unsigned)(nbg * wl.p_max), 1, 1);
-  hipStream_t st = static_cast<hipStream_t>(stream);
+  const dim3 grid(pa_host::decode_grid(shape, wl, shares), 1, 1);
+  hipStream_t hs = static_cast<hipStream_t>(stream);
   hipError_t e;
   const int D = shape->head_dim;
   if (q_len == 1) {
     if (io_dtype == PA_F32)
-      e = launch_d<F32, F32, false>(D, prm, grid, balanced, st);
+      e = launch_d<F32, F32, false>(D, prm, grid, balanced, hs);
     else if (io_dtype == PA_F16)
-      e = kv_dtype == PA_FP8_E4M3 ? launch_d<F16, FP8, false>(D, prm, grid, balanced, st)
-                                  : launch_d<F16, F16, false>(D, prm, grid, balanced, st);
+      e = kv_dtype == PA_FP8_E4M3 ? launch_d<F16, FP8, false>(D, prm, grid, balanced, hs)
+                                  : launch_d<F16, F16, false>(D, prm, grid, balanced, hs);
     else
-      e = kv_dtype == PA_FP8_E4M3 ? launch_d<BF16, FP8, false>(D, prm, grid, balanced, st)
-                                  : launch_d<BF16, BF16, false>(D, prm, grid, balanced, st);
+      e = kv_dtype == PA_FP8_E4M3 ? launch_d<BF16, FP8, false>(D, prm, grid, balanced, hs)
+                                  : launch_d<BF16, BF16, false>(D, prm, grid, balanced, hs);
   } else {
     if (io_dtype == PA_F32)
-      e = launch_d<F32, F32, true>(D, prm, grid, balanced, st);
+      e = launch_d<F32, F32, true>(D, prm, grid, balanced, hs);
     else if (io_dtype == PA_F16)
-      e = kv_dtype == PA_FP8_E4M3 ? launch_d<F16, FP8, true>(D, prm, grid, balanced, st)
-                                  : launch_d<F16, F16, true>(D, prm, grid, balanced, st);
+      e = kv_dtype == PA_FP8_E4M3 ? launch_d<F16, FP8, true>(D, prm, grid, balanced, hs)
+                                  : launch_d<F16, F16, true>(D, prm, grid, balanced, hs);
     else
-      e = kv_dtype == PA_FP8_E4M3 ? launch_d<BF16, FP8, true>(D, prm, grid, balanced, st)
-                                  : launch_d<BF16, BF16, true>(D, prm, grid, balanced, st);
+      e = kv_dtype == PA_FP8_E4M3 ? launch_d<BF16, FP8, true>(D, prm, grid, balanced, hs)
+                                  : launch_d<BF16, BF16, true>(D, prm, grid, balanced, hs);
   }
   return e == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
@@ -1686,8 +1608,8 @@ pa_status pa_decode_noalloc(const pa_shape* shape, const void* q, const void* k_
                              kv_dtype, k_scale, v_scale, nullptr, 0, 0, out, lse_out, stream);
   // fixed partitions: the size check needs no device, so an oversized call is
   // refused before the scratch is looked up
-  if (shape->partition_size > 0 && pa::shape_ok(shape)) {
-    const pa::WsLayout wl = pa::ws_layout(shape, 0, 1, pa::kScratchCounterBytes);
+  if (shape->partition_size > 0 && pa_host::decode_shape_ok(shape)) {
+    const pa_host::DecodeLayout wl = pa_host::decode_layout(shape, 0, 1, pa::kScratchCounterBytes);
     if (wl.cnt_bytes > pa::kScratchCounterBytes || wl.total > pa::kScratchBytes) return PA_ERR_SCRATCH;
   }
   void* ws = nullptr;

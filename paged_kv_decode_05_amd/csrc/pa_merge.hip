@@ -18,12 +18,13 @@
 #include <stdint.h>
 
 #include "padecode.h"
+#include "pa_host.h"
 
 namespace pa_merge {
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-constexpr int kThreads = 256;
+constexpr int kThreads = pa_host::kMergeThreads;
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
@@ -134,18 +135,13 @@ extern "C" pa_status pa_lse_merge(int32_t num_shards, int32_t rows, int32_t head
                                   const void* shard_out, const float* shard_lse,
                                   pa_dtype dtype, void* out, float* lse_out, void* stream) {
   using namespace pa_merge;
-  if (num_shards < 1 || num_shards > 65535 || rows < 0) return PA_ERR_SHAPE;
-  if (head_dim < 4 || head_dim > 1024 || head_dim % 4) return PA_ERR_SHAPE;
-  if (!shard_out || !shard_lse || !out) return PA_ERR_NULL;
-  if (dtype != PA_F32 && dtype != PA_F16 && dtype != PA_BF16) return PA_ERR_DTYPE;
-  if ((((uintptr_t)shard_out | (uintptr_t)out) & 15u) ||
-      (((uintptr_t)shard_lse | (uintptr_t)lse_out) & 3u))
-    return PA_ERR_ALIGN;
-  const long long threads = (long long)rows * (head_dim / 4);
-  if (threads == 0) return PA_OK;
-  if ((threads + kThreads - 1) / kThreads > 0x7fffffffLL) return PA_ERR_SHAPE;
+  unsigned blocks = 0;
+  const pa_status status = pa_host::merge_status(num_shards, rows, head_dim, shard_out, shard_lse, dtype,
+                                                 out, lse_out, &blocks);
+  if (status != PA_OK) return status;
+  if (blocks == 0) return PA_OK;
   Params p{shard_out, shard_lse, out, lse_out, num_shards, rows, head_dim};
-  const dim3 grid((unsigned)((threads + kThreads - 1) / kThreads));
+  const dim3 grid(blocks);
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (dtype == PA_F32)
     hipLaunchKernelGGL(lse_merge_kernel<F32>, grid, dim3(kThreads), 0, st, p);

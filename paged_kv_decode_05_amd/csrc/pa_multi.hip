@@ -42,14 +42,15 @@
 #include <type_traits>
 
 #include "padecode.h"
+#include "pa_host.h"
 #include "pa_internal.h"
 #include "pa_tiles.h"
 
 namespace pa_mq {
 using namespace pa;
 
-constexpr int kMaxQLen = 16;
-constexpr int kChunkTiles = 2;   // column tiles of 16 rows per workgroup
+constexpr int kMaxQLen = pa_host::kMaxQLen;
+constexpr int kChunkTiles = pa_host::kChunkTiles;   // column tiles of 16 rows per workgroup
 
 struct Params {
   const uint8_t* q;          // [B][T][Hq][D]
@@ -512,52 +513,6 @@ pa_multi_kernel(const Params a) {
 // ---------------------------------------------------------------------------
 // Host side.
 // ---------------------------------------------------------------------------
-struct Plan {
-  int rows, tiles, chunks, p_max, fan, g_max;
-  size_t cnt_off, o_off, lse_off, total;
-};
-
-static inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
-
-static bool plan(const pa_shape* s, int q_len, Plan* out) {
-  if (!s) return false;
-  if (q_len < 1 || q_len > kMaxQLen) return false;
-  if (s->batch < 0 || s->batch > 65535) return false;
-  if (s->num_kv_heads < 1 || s->num_kv_heads > 65535) return false;
-  if (s->num_q_heads < 1 || s->num_q_heads % s->num_kv_heads != 0) return false;
-  const int G = s->num_q_heads / s->num_kv_heads;
-  if (G > kMaxGroup) return false;
-  if ((long long)s->batch * q_len * s->num_q_heads > 0x7fffffffLL) return false;
-  if (s->head_dim != 64 && s->head_dim != 128) return false;
-  if (s->block_size != kBlock) return false;
-  if (s->max_blocks_per_seq < 1 || s->max_blocks_per_seq > (1 << 26)) return false;
-  if (s->num_blocks < 1) return false;
-  if (s->partition_size < 0 || s->partition_size % kBlock != 0) return false;
-  Plan p;
-  p.rows = G * q_len;
-  p.tiles = (p.rows + 15) / 16;
-  p.chunks = (p.tiles + kChunkTiles - 1) / kChunkTiles;
-  const long long tokens = (long long)s->max_blocks_per_seq * kBlock;
-  p.p_max = s->partition_size ? (int)((tokens + s->partition_size - 1) / s->partition_size) : 1;
-  const long long units = (long long)s->batch * s->num_kv_heads * p.chunks * p.p_max;
-  if (units > 0x7fffffffLL) return false;
-  p.fan = s->partition_size ? merge_fan(p.p_max) : 0;
-  p.g_max = p.fan ? (p.p_max + p.fan - 1) / p.fan : 0;
-  if ((long long)s->batch * s->num_kv_heads * (p.p_max + p.g_max) > 0x7fffffffLL) return false;
-  p.cnt_off = p.o_off = p.lse_off = p.total = 0;
-  if (s->partition_size) {
-    // counters first: [B][Hkv][chunks], then [B][Hkv][g_max][chunks]; slots:
-    // partitions, then first-level groups
-    const size_t nbg = (size_t)s->batch * s->num_kv_heads;
-    const size_t slots = nbg * (p.p_max + p.g_max);
-    p.o_off = align_up(nbg * (1 + (size_t)p.g_max) * p.chunks * sizeof(uint32_t), 256);
-    p.lse_off = p.o_off + align_up(slots * p.rows * s->head_dim * sizeof(float), 256);
-    p.total = p.lse_off + align_up(slots * p.rows * sizeof(float), 256);
-  }
-  *out = p;
-  return true;
-}
-
 // Two tiles per chunk: rows that fit one tile run on the decode kernels.
 template <typename IO, typename KV, int D>
 static hipError_t launch_chunks(const Params& prm, dim3 grid, hipStream_t st) {
@@ -573,18 +528,14 @@ static hipError_t launch_d(int D, const Params& prm, dim3 grid, hipStream_t st) 
   return D == 64 ? launch_chunks<IO, KV, 64>(prm, grid, st) : launch_chunks<IO, KV, 128>(prm, grid, st);
 }
 
-static inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
-
 }  // namespace pa_mq
 
 extern "C" {
 
 size_t pa_decode_multi_workspace_bytes(const pa_shape* shape, int32_t q_len) {
-  if (shape && shape->num_kv_heads > 0 && q_len >= 1 && q_len <= pa_mq::kMaxQLen &&
-      (long long)(shape->num_q_heads / shape->num_kv_heads) * q_len <= pa::kTileRows)
-    return pa::decode_workspace_bytes(shape, q_len);
-  pa_mq::Plan p;
-  if (!pa_mq::plan(shape, q_len, &p)) return 0;
+  if (pa_host::multi_fits_one_tile(shape, q_len)) return pa::decode_workspace_bytes(shape, q_len);
+  pa_host::MultiPlan p;
+  if (!pa_host::multi_plan(shape, q_len, &p)) return 0;
   return p.total;
 }
 
@@ -596,27 +547,17 @@ pa_status pa_decode_multi(const pa_shape* shape, int32_t q_len, const void* q, c
                           void* stream) {
   using namespace pa_mq;
   if (!shape) return PA_ERR_NULL;
-  if (shape->num_kv_heads > 0 && q_len >= 1 && q_len <= kMaxQLen &&
-      (long long)(shape->num_q_heads / shape->num_kv_heads) * q_len <= pa::kTileRows)
+  if (pa_host::multi_fits_one_tile(shape, q_len))
     return pa::decode_call(shape, q_len, q, k_cache, v_cache, block_table, context_lens, scale,
                            io_dtype, kv_dtype, k_scale, v_scale, workspace, workspace_bytes, out,
                            lse_out, stream);
-  Plan pl;
-  if (!plan(shape, q_len, &pl)) return PA_ERR_SHAPE;
-  if (!q || !k_cache || !v_cache || !block_table || !context_lens || !out) return PA_ERR_NULL;
-  const bool io_ok = io_dtype == PA_F32 || io_dtype == PA_F16 || io_dtype == PA_BF16;
-  const bool kv_ok = kv_dtype == io_dtype || (kv_dtype == PA_FP8_E4M3 && io_dtype != PA_F32);
-  if (!io_ok || !kv_ok) return PA_ERR_DTYPE;
-  if (kv_dtype == PA_FP8_E4M3 && (!k_scale || !v_scale)) return PA_ERR_NULL;
-  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out))
-    return PA_ERR_ALIGN;
-  if (((uintptr_t)block_table & 3u) || ((uintptr_t)context_lens & 3u) ||
-      ((uintptr_t)lse_out & 3u))
-    return PA_ERR_ALIGN;
-  if (shape->partition_size != 0) {
-    if (!workspace || workspace_bytes < pl.total) return PA_ERR_WORKSPACE;
-    if ((uintptr_t)workspace & 255u) return PA_ERR_ALIGN;
-  }
+  pa_host::MultiPlan pl;
+  if (!pa_host::multi_plan(shape, q_len, &pl)) return PA_ERR_SHAPE;
+  pa_status status = pa_host::io_args_status(q, k_cache, v_cache, block_table, context_lens, io_dtype,
+                                             kv_dtype, k_scale, v_scale, out, lse_out);
+  if (status != PA_OK) return status;
+  status = pa_host::workspace_status(shape->partition_size, pl.total, 0, 0, workspace, workspace_bytes);
+  if (status != PA_OK) return status;
   if (shape->batch == 0) return PA_OK;
 
   Params prm;
@@ -649,8 +590,7 @@ pa_status pa_decode_multi(const pa_shape* shape, int32_t q_len, const void* q, c
   prm.g_max = pl.g_max;
   prm.p_max = pl.p_max;
 
-  const long long units = (long long)shape->batch * shape->num_kv_heads * pl.chunks * pl.p_max;
-  const dim3 grid((unsigned)units, 1, 1);
+  const dim3 grid(pa_host::multi_grid(shape, pl), 1, 1);
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int D = shape->head_dim;
   hipError_t e;
