@@ -267,9 +267,12 @@ def prepare(q, k_cache, v_cache, block_table, context_lens, scale, *, k_scale=No
     SPLIT_BALANCED = equal page shares per workgroup. `workspace` (uint8) is
     used when partition_size != 0; `workspace_bytes` gives its size. It must be
     zero-filled (reset_workspace) before first use and before a call whose
-    counters take more bytes than any earlier call's (include/padecode.h);
-    every completed call leaves the counters zero. Without a workspace a
-    zeroed one is allocated per call.
+    counters take more bytes than the smallest counter bytes of any call since
+    the last reset (a smaller call's partial results start right after its own
+    counters, over a larger call's); every completed call leaves the counters
+    it used zero, and a counter found stale makes that pair's rows NaN until
+    the next reset (include/padecode.h). Without a workspace a zeroed one is
+    allocated per call.
 
     q [B, T, Hq, D] selects the multi-token call (pa_decode_multi): T new
     tokens per sequence whose K/V are already in the cache, new token t seeing
