@@ -351,13 +351,13 @@ def bench_multi(args, torch, np, pkd, W):
                             partition_size=ps, out=out, workspace=ws, stream=stream)
                 for i in range(reps)]
 
-    # the workload's own split, one pass, and longer partitions (fewer partial
-    # results to write and merge when every row costs a partial: they win for
-    # several row counts and context mixes); the caller picks partition_size
+    # the workload's own split, one pass, longer partitions (fewer partial
+    # results to write and merge when every row costs a partial) and the
+    # balanced split (equal pages per CU: the decode kernels when the rows fit
+    # one tile, the wide-row balanced kernel otherwise); the caller picks
+    # partition_size
     modes = [args.partition_size] if args.partition_size is not None else \
-        [spec.partition_size, 0, 1024, 2048]
-    if args.partition_size is None and spec.num_q_heads // spec.num_kv_heads * T <= 16:
-        modes.append(pkd.SPLIT_BALANCED)   # rows of one tile: the decode kernels run the call
+        [spec.partition_size, 0, 1024, 2048, pkd.SPLIT_BALANCED]
     if args.pmc_pass:
         calls = make_calls(modes[0])
         src = torch.ones(1 << 28, dtype=torch.int32, device=dev)      # 1 GiB

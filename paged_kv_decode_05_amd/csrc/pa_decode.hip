@@ -1141,11 +1141,6 @@ __device__ __forceinline__ void decode_quarter(const Params& a, const BalSm<D>& 
     run_ring(std::integral_constant<bool, false>{});
 }
 
-// Workgroup barrier that orders LDS only: each wave waits for its own LDS
-// operations, not for its global stores (which __syncthreads() would wait
-// for as well).
-__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
-
 // Per candidate slot c = 2 * wave + slot, what the combine needs of the piece
 // it leads, one value per lane c < 2 * kWaves (taken with readlane).
 struct SlotFacts {
@@ -1411,7 +1406,7 @@ __global__ void fill_zero_kernel(uint8_t* p, size_t n) {
 constexpr int kWgPerCu = 1;
 
 // Shares of the balanced split on the current device, or -1.
-static int balanced_shares() {
+int balanced_shares() {
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess) return -1;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return -1;

@@ -148,6 +148,7 @@ inline unsigned decode_grid(const pa_shape* s, const DecodeLayout& w, int shares
 // ---------------------------------------------------------------------------
 struct MultiPlan {
   int rows, tiles, chunks, p_max, fan, g_max;
+  int shares;   // balanced split: workgroups (one share each); 0 otherwise
   size_t cnt_off, o_off, lse_off, total;
 };
 
@@ -157,7 +158,9 @@ inline bool multi_fits_one_tile(const pa_shape* s, int q_len) {
          (long long)(s->num_q_heads / s->num_kv_heads) * q_len <= pa::kTileRows;
 }
 
-inline bool multi_plan(const pa_shape* s, int q_len, MultiPlan* out) {
+// shares: the balanced split's workgroup count (partition_size ==
+// PA_SPLIT_BALANCED; ignored otherwise, and a balanced plan needs 1 .. 3 * 4096).
+inline bool multi_plan(const pa_shape* s, int q_len, MultiPlan* out, int shares = 0) {
   if (!s) return false;
   if (q_len < 1 || q_len > kMaxQLen) return false;
   if (s->batch < 0 || s->batch > 65535) return false;
@@ -170,11 +173,35 @@ inline bool multi_plan(const pa_shape* s, int q_len, MultiPlan* out) {
   if (s->block_size != kPageTokens) return false;
   if (s->max_blocks_per_seq < 1 || s->max_blocks_per_seq > (1 << 26)) return false;
   if (s->num_blocks < 1) return false;
-  if (s->partition_size < 0 || s->partition_size % kPageTokens != 0) return false;
+  const bool balanced = s->partition_size == PA_SPLIT_BALANCED;
+  if (balanced) {
+    // the workgroup-wide scan covers the batch, and line positions fit int32
+    if (s->batch > kBalancedMaxBatch || shares < 1 || shares > 3 * 4096) return false;
+    const long long line = (long long)s->batch * s->num_kv_heads * s->max_blocks_per_seq;
+    if (line + 4096LL * 3 >= kInt32Max) return false;
+  } else if (s->partition_size < 0 || s->partition_size % kPageTokens != 0) {
+    return false;
+  }
   MultiPlan p;
   p.rows = G * q_len;
   p.tiles = (p.rows + 15) / 16;
   p.chunks = (p.tiles + kChunkTiles - 1) / kChunkTiles;
+  p.shares = 0;
+  if (balanced) {
+    // counters: one per (sequence, KV head); partial slots: shares + pairs
+    // (piece k of a pair goes to slot first share of the pair + pair index + k)
+    const size_t nbg = (size_t)s->batch * s->num_kv_heads;
+    const size_t slots = (size_t)shares + nbg;
+    p.p_max = 0;
+    p.fan = p.g_max = 0;
+    p.shares = shares;
+    p.cnt_off = 0;
+    p.o_off = align_up(nbg * sizeof(uint32_t), 256);
+    p.lse_off = p.o_off + align_up(slots * p.rows * s->head_dim * sizeof(float), 256);
+    p.total = p.lse_off + align_up(slots * p.rows * sizeof(float), 256);
+    *out = p;
+    return true;
+  }
   const long long tokens = (long long)s->max_blocks_per_seq * kPageTokens;
   p.p_max = s->partition_size ? (int)((tokens + s->partition_size - 1) / s->partition_size) : 1;
   const long long units = (long long)s->batch * s->num_kv_heads * p.chunks * p.p_max;
@@ -196,7 +223,10 @@ inline bool multi_plan(const pa_shape* s, int q_len, MultiPlan* out) {
   return true;
 }
 
+// Workgroups: one per (sequence, KV head, partition, row chunk), or one per
+// share of the balanced split.
 inline unsigned multi_grid(const pa_shape* s, const MultiPlan& p) {
+  if (s->partition_size == PA_SPLIT_BALANCED) return (unsigned)p.shares;
   return (unsigned)((long long)s->batch * s->num_kv_heads * p.chunks * p.p_max);
 }
 

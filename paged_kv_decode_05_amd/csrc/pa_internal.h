@@ -30,6 +30,10 @@ inline int merge_fan(long long p_max) {
 // token t sees positions 0 .. L - q_len + t. Same argument rules, workspace
 // contract and statuses as pa_decode.
 size_t decode_workspace_bytes(const pa_shape* shape, int q_len);
+
+// Workgroups of a balanced split on the current device (one per CU), or -1
+// when the device cannot be queried.
+int balanced_shares();
 pa_status decode_call(const pa_shape* shape, int q_len, const void* q, const void* k_cache,
                       const void* v_cache, const int32_t* block_table,
                       const int32_t* context_lens, float scale, pa_dtype io_dtype,

@@ -44,6 +44,7 @@
 #include "padecode.h"
 #include "pa_host.h"
 #include "pa_internal.h"
+#include "pa_schedule.h"
 #include "pa_tiles.h"
 
 namespace pa_mq {
@@ -83,27 +84,29 @@ struct Params {
 };
 
 // Merge the n pieces of rows row0 .. row0 + rows_c - 1 of (b, g) stored in
-// workspace slots slot0 .. slot0 + n - 1 (partitions, or first-level groups
-// of partitions) in slot order, and write the final output of those rows
-// (dst < 0) or the merged piece to workspace slot dst. Threads take
-// (row, 4-float quad) items two at a time and issue the loads of kBatch
-// pieces of both before folding either (one memory round trip per batch for
-// both). A piece a row sees nothing of (lse = -inf) adds nothing; a row that
-// sees nothing in any piece gets out = 0 and lse = -inf; NaN in any piece
-// gives NaN.
+// workspace slots slot0 .. slot0 + n - 1 (partitions, first-level groups of
+// partitions, or pieces of the balanced split) in slot order, and write the
+// final output of those rows (dst < 0) or the merged piece to workspace slot
+// dst. Threads take (row, 4-float quad) items kU at a time and issue the
+// loads of kBatch pieces of all of them before folding any, so up to
+// kU * 256 items cost one memory round trip per kBatch pieces (a 56-row pair
+// at head_dim 128, 1,792 items, costs one). A piece a row sees nothing of
+// (lse = -inf) adds nothing; a row that sees nothing in any piece gets out = 0
+// and lse = -inf; NaN in any piece gives NaN.
 template <typename IO, int D>
 __device__ __forceinline__ void merge_rows(const Params& a, int b, int g, int row0, int rows_c,
                                            size_t slot0, int n, long long dst) {
-  constexpr int kBatch = 8;
+  constexpr int kBatch = 4;
+  constexpr int kU = 8;
   const int R = a.rows, G = a.group;
   const int items = rows_c * (D / 4);
-  for (int base = 0; base < items; base += 2 * kThreads) {
-    int rho[2], d[2];
-    bool on[2], nan[2];
-    float mr[2], wr[2];
-    f32x4 ar[2];
+  for (int base = 0; base < items; base += kU * kThreads) {
+    int rho[kU], d[kU];
+    bool on[kU], nan[kU];
+    float mr[kU], wr[kU];
+    f32x4 ar[kU];
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
+    for (int u = 0; u < kU; ++u) {
       const int i = base + u * kThreads + threadIdx.x;
       on[u] = i < items;
       const int r2 = i / (D / 4);
@@ -118,10 +121,10 @@ __device__ __forceinline__ void merge_rows(const Params& a, int b, int g, int ro
       const int nb = min(kBatch, n - q0);
       const brsrc ro = buffer_rsrc(a.ws_o + (slot0 + q0) * R * D, (uint32_t)(nb * R * D * sizeof(float)));
       const brsrc rl = buffer_rsrc(a.ws_lse + (slot0 + q0) * R, (uint32_t)(nb * R * sizeof(float)));
-      float lp[2][kBatch];
-      f32x4 ov[2][kBatch];
+      float lp[kU][kBatch];
+      f32x4 ov[kU][kBatch];
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
+      for (int u = 0; u < kU; ++u) {
         const uint32_t vo = (uint32_t)(((size_t)rho[u] * D + d[u]) * sizeof(float));
         const uint32_t vl = (uint32_t)(rho[u] * sizeof(float));
 #pragma unroll
@@ -133,7 +136,7 @@ __device__ __forceinline__ void merge_rows(const Params& a, int b, int g, int ro
         }
       }
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
+      for (int u = 0; u < kU; ++u) {
 #pragma unroll
         for (int q = 0; q < kBatch; ++q) {
           if (on[u] && q < nb) {
@@ -152,7 +155,7 @@ __device__ __forceinline__ void merge_rows(const Params& a, int b, int g, int ro
       }
     }
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
+    for (int u = 0; u < kU; ++u) {
       if (!on[u]) continue;
       f32x4 val = {0.f, 0.f, 0.f, 0.f};
       float lse2 = -INFINITY;   // base 2
@@ -187,6 +190,172 @@ struct MqSmem {
   int last;
 };
 
+// One wave's share of a unit: pages first, first + stride, ... (n of them)
+// of sequence b and KV head g, tokens before t1, against NT column tiles whose
+// query operands sit in LDS at qsm ([NT][KQ][64] chunks, lane order). lim[j]:
+// the last token the lane's column of tile j may see. Pages go through the
+// same register rings as decode; the steady blocks never hold the wave's last
+// tail_min pages (nor its last ring depth), and every page a mask can touch
+// is among those, so the steady blocks run unmasked: the causal mask reaches
+// at most a sequence's last two pages, the last two of a wave with stride 1
+// and the last of a wave with a larger stride. A column with nothing visible
+// yet keeps a zero state (running max -inf, exponentials taken against 0).
+// Leaves the wave's running max, its lanes' partial sums and the
+// accumulators; bad_blk: a block id outside the pool was met (block 0 read
+// instead).
+// Block ids of pages first + stride * (64 * chunk + lane), clamped into the
+// table row: the lane's id of one 64-page chunk.
+__device__ __forceinline__ int fetch_ids(const Params& a, int b, int first, int stride, int chunk) {
+  const int lane = threadIdx.x & 63;
+  return a.block_table[(size_t)b * a.max_blocks_per_seq +
+                       min(first + stride * (chunk * 64 + lane), a.max_blocks_per_seq - 1)];
+}
+
+// bt0: fetch_ids(a, b, first, stride, 0), loaded by the caller as early as it
+// can be.
+template <typename IO, typename KV, int D, int NT, bool KEEP>
+__device__ __forceinline__ void stream_pages(const Params& a, int b, int g, int first, int stride, int n,
+                                             int bt0, int t1, const int (&lim)[NT],
+                                             const typename TileOf<IO, KV, D>::type::QC* qsm, float kmul,
+                                             int tail_min, float (&mrow)[NT], float (&lrow)[NT],
+                                             f32x4 (&acc)[NT][D / 16], bool& bad_blk) {
+  using T = typename TileOf<IO, KV, D>::type;
+  constexpr int KQ = T::kQ;
+  constexpr size_t kPageBytes = (size_t)kBlock * D * ElemSize<KV>::v;
+  const int lane = threadIdx.x & 63;
+  const int jj = lane >> 4;
+
+  // Block ids of the wave's pages, 64 at a time.
+  auto fetch_bt = [&](int chunk) { return fetch_ids(a, b, first, stride, chunk); };
+  int bt_cur = bt0;
+  int bt_next = n > 64 ? fetch_bt(1) : 0;
+
+  const gptr kbase = uniform_ptr(a.k + (size_t)g * kPageBytes);
+  const gptr vbase = uniform_ptr(a.v + (size_t)g * kPageBytes);
+  const size_t block_stride = (size_t)a.num_kv_heads * kPageBytes;
+  const uint32_t ko = T::koff(lane), vo = T::voff(lane);
+
+  constexpr int kKS = T::kKStages, kVS = T::kVStages;
+  constexpr int dK = kKS - 1, dV = kVS - 1;
+  // a V load reuses the page offset its K load recorded, so V may not run
+  // ahead of K
+  static_assert(kKS >= 1 && kVS >= 1 && dV <= dK, "ring depths");
+  constexpr int kAhead = dK > 1 ? dK : 1;
+  constexpr int kTailMax = kAhead > 2 ? kAhead : 2;
+  const int tail = max(kAhead, tail_min);
+  typename T::KRegs ring_k[kKS];
+  typename T::VRegs ring_v[kVS];
+  size_t poff[kKS];
+
+  auto issue_k = [&](int slot, int i, auto refresh_tag) __attribute__((always_inline)) {
+    if constexpr (decltype(refresh_tag)::value) {
+      if (i > 0 && (i & 63) == 0) {
+        bt_cur = bt_next;
+        if (n > i + 64) bt_next = fetch_bt((i >> 6) + 1);
+      }
+    }
+    int phys = __builtin_amdgcn_readlane(bt_cur, i & 63);
+    if ((unsigned)phys >= (unsigned)a.num_blocks) {
+      bad_blk = true;
+      phys = 0;
+    }
+    poff[slot] = (size_t)phys * block_stride;
+    T::template load_k<KEEP>(ring_k[slot], kbase + poff[slot], ko);
+  };
+  auto issue_v = [&](int vslot, int kslot) __attribute__((always_inline)) {
+    T::template load_v<KEEP>(ring_v[vslot], vbase + poff[kslot], vo);
+  };
+
+#pragma unroll
+  for (int j = 0; j < NT; ++j) {
+    mrow[j] = -INFINITY;
+    lrow[j] = 0.f;
+#pragma unroll
+    for (int t = 0; t < D / 16; ++t) acc[j][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  // One page for all NT column tiles. kMasked: the page may hold tokens at
+  // or past t1, or tokens some column must not see.
+  auto compute = [&](int kslot, int vslot, int i, auto masked_tag) __attribute__((always_inline)) {
+    constexpr bool kMasked = decltype(masked_tag)::value;
+    const int pstart = (first + stride * i) * kBlock;
+    typename T::A4 va[D / 16];
+#pragma unroll
+    for (int t = 0; t < D / 16; ++t) {
+      va[t] = T::pvt(ring_v[vslot], t);
+      if constexpr (kMasked) va[t] = T::zero_tail(va[t], jj, t1 - pstart);
+    }
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+      typename T::Q qop;
+#pragma unroll
+      for (int cc = 0; cc < KQ; ++cc) qop.c[cc] = qsm[(j * KQ + cc) * 64 + lane];
+      const f32x4 s = T::scores(ring_k[kslot], qop);
+      float sc[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if constexpr (kMasked) {
+          const int tok = pstart + 4 * jj + e;
+          sc[e] = (tok <= lim[j] && tok < t1) ? s[e] * kmul : -INFINITY;
+        } else {
+          sc[e] = s[e] * kmul;
+        }
+      }
+      const float mx = wave_max_rows(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])));
+      const float mnew = fmaxf(mrow[j], mx);
+      float msafe = mnew;
+      if constexpr (kMasked) msafe = mnew == -INFINITY ? 0.f : mnew;
+      const float alpha = exp2_fast(mrow[j] - msafe);
+      float pr[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) pr[e] = exp2_fast(sc[e] - msafe);
+      const typename T::P pk = T::pack(pr);
+      lrow[j] = lrow[j] * alpha + T::psum(pk);
+      mrow[j] = mnew;
+      if (__any(alpha != 1.0f)) {
+#pragma unroll
+        for (int t = 0; t < D / 16; ++t) acc[j][t] *= alpha;
+      }
+#pragma unroll
+      for (int t = 0; t < D / 16; ++t) acc[j][t] = T::pv(va[t], pk, acc[j][t]);
+    }
+  };
+  using Full = std::integral_constant<bool, false>;
+  using Tail = std::integral_constant<bool, true>;
+
+  constexpr int kU = kKS * kVS / gcd_c(kKS, kVS);
+  auto run_ring = [&](auto refresh_tag) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < dK; ++j)
+      if (j < n) issue_k(j, j, refresh_tag);
+#pragma unroll
+    for (int j = 0; j < dV; ++j)
+      if (j < n) issue_v(j, j);
+    int i0 = 0;
+    for (; i0 + kU - 1 + tail < n; i0 += kU) {
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        issue_k((u + dK) % kKS, i0 + u + dK, refresh_tag);
+        issue_v((u + dV) % kVS, (u + dV) % kKS);
+        compute(u % kKS, u % kVS, i0 + u, Full{});
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kU + kTailMax; ++u) {
+      const int i = i0 + u;
+      if (i < n) {
+        if (i + dK < n) issue_k((u + dK) % kKS, i + dK, refresh_tag);
+        if (i + dV < n) issue_v((u + dV) % kVS, (u + dV) % kKS);
+        compute(u % kKS, u % kVS, i, Tail{});
+      }
+    }
+  };
+  if (n > 64)
+    run_ring(std::integral_constant<bool, true>{});
+  else
+    run_ring(std::integral_constant<bool, false>{});
+}
+
 // KEEP: the pair has three or more row chunks, so several other workgroups
 // read the same pages soon after: ordinary loads, which leave them in L2 for
 // those (non-temporal otherwise, as in decode). Measured on the
@@ -199,7 +368,6 @@ pa_multi_kernel(const Params a) {
   using QC = typename T::QC;
   constexpr int KQ = T::kQ;
   constexpr bool kFp8 = std::is_same<KV, FP8>::value;
-  constexpr size_t kPageBytes = (size_t)kBlock * D * ElemSize<KV>::v;
   constexpr int kRowsC = NT * 16;
   __shared__ MqSmem<QC, NT, KQ, D> sm;
 
@@ -220,13 +388,8 @@ pa_multi_kernel(const Params a) {
   const int page0 = PT > 0 ? p * (PT / kBlock) : 0;
   const int row0 = c * kRowsC;
 
-  // Block ids of this wave's first 64 pages (indices clamped into the row).
-  const int32_t* bt = a.block_table + (size_t)b * a.max_blocks_per_seq + w;
-  const int bt_last = a.max_blocks_per_seq - 1 - w;
-  auto fetch_bt = [&](int chunk) {
-    return bt[min(page0 + kWaves * (chunk * 64 + lane), bt_last)];
-  };
-  int bt_cur = fetch_bt(0);
+  // Block ids of this wave's first 64 pages, before the length is known.
+  const int bt0 = fetch_ids(a, b, page0 + w, kWaves, 0);
 
   // The chunk's query operand into LDS. Rows past R repeat row R-1: their
   // columns hold finite duplicates that are never stored.
@@ -276,136 +439,12 @@ pa_multi_kernel(const Params a) {
     kmul *= a.k_scale[g];
     vmul = a.v_scale[g];
   }
-  int bt_next = nmine > 64 ? fetch_bt(1) : 0;
-
-  const gptr kbase = uniform_ptr(a.k + (size_t)g * kPageBytes);
-  const gptr vbase = uniform_ptr(a.v + (size_t)g * kPageBytes);
-  const size_t block_stride = (size_t)a.num_kv_heads * kPageBytes;
-  const uint32_t ko = T::koff(lane), vo = T::voff(lane);
-  bool bad_blk = false;
-
-  constexpr int kKS = T::kKStages, kVS = T::kVStages;
-  constexpr int dK = kKS - 1, dV = kVS - 1;
-  // a V load reuses the page offset its K load recorded, so V may not run
-  // ahead of K
-  static_assert(kKS >= 1 && kVS >= 1 && dV <= dK, "ring depths");
-  constexpr int kAhead = dK > 1 ? dK : 1;
-  typename T::KRegs ring_k[kKS];
-  typename T::VRegs ring_v[kVS];
-  size_t poff[kKS];
-
-  auto issue_k = [&](int slot, int i, auto refresh_tag) __attribute__((always_inline)) {
-    if constexpr (decltype(refresh_tag)::value) {
-      if (i > 0 && (i & 63) == 0) {
-        bt_cur = bt_next;
-        if (nmine > i + 64) bt_next = fetch_bt((i >> 6) + 1);
-      }
-    }
-    int phys = __builtin_amdgcn_readlane(bt_cur, i & 63);
-    if ((unsigned)phys >= (unsigned)a.num_blocks) {
-      bad_blk = true;
-      phys = 0;
-    }
-    poff[slot] = (size_t)phys * block_stride;
-    T::template load_k<KEEP>(ring_k[slot], kbase + poff[slot], ko);
-  };
-  auto issue_v = [&](int vslot, int kslot) __attribute__((always_inline)) {
-    T::template load_v<KEEP>(ring_v[vslot], vbase + poff[kslot], vo);
-  };
-
+  __syncthreads();   // query operand in LDS
   float mrow[NT], lrow[NT];
   f32x4 acc[NT][D / 16];
-#pragma unroll
-  for (int j = 0; j < NT; ++j) {
-    mrow[j] = -INFINITY;
-    lrow[j] = 0.f;
-#pragma unroll
-    for (int t = 0; t < D / 16; ++t) acc[j][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-
-  // One page for all NT column tiles. kMasked: the page may hold tokens at
-  // or past the unit's end, or tokens some column must not see.
-  auto compute = [&](int kslot, int vslot, int i, auto masked_tag) __attribute__((always_inline)) {
-    constexpr bool kMasked = decltype(masked_tag)::value;
-    const int pstart = t0 + (w + kWaves * i) * kBlock;
-    typename T::A4 va[D / 16];
-#pragma unroll
-    for (int t = 0; t < D / 16; ++t) {
-      va[t] = T::pvt(ring_v[vslot], t);
-      if constexpr (kMasked) va[t] = T::zero_tail(va[t], jj, t1 - pstart);
-    }
-#pragma unroll
-    for (int j = 0; j < NT; ++j) {
-      typename T::Q qop;
-#pragma unroll
-      for (int cc = 0; cc < KQ; ++cc) qop.c[cc] = sm.q[j][cc][lane];
-      const f32x4 s = T::scores(ring_k[kslot], qop);
-      float sc[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        if constexpr (kMasked) {
-          const int tok = pstart + 4 * jj + e;
-          sc[e] = (tok <= lim[j] && tok < t1) ? s[e] * kmul : -INFINITY;
-        } else {
-          sc[e] = s[e] * kmul;
-        }
-      }
-      const float mx = wave_max_rows(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])));
-      const float mnew = fmaxf(mrow[j], mx);
-      float msafe = mnew;
-      if constexpr (kMasked) msafe = mnew == -INFINITY ? 0.f : mnew;
-      const float alpha = exp2_fast(mrow[j] - msafe);
-      float pr[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) pr[e] = exp2_fast(sc[e] - msafe);
-      const typename T::P pk = T::pack(pr);
-      lrow[j] = lrow[j] * alpha + T::psum(pk);
-      mrow[j] = mnew;
-      if (__any(alpha != 1.0f)) {
-#pragma unroll
-        for (int t = 0; t < D / 16; ++t) acc[j][t] *= alpha;
-      }
-#pragma unroll
-      for (int t = 0; t < D / 16; ++t) acc[j][t] = T::pv(va[t], pk, acc[j][t]);
-    }
-  };
-  using Full = std::integral_constant<bool, false>;
-  using Tail = std::integral_constant<bool, true>;
-
-  // Steady blocks never hold a wave's last kAhead pages; every page a mask
-  // can touch is the last page of its wave, so it runs in the peeled tail.
-  constexpr int kU = kKS * kVS / gcd_c(kKS, kVS);
-  __syncthreads();   // query operand in LDS
-  auto run_ring = [&](auto refresh_tag) __attribute__((always_inline)) {
-#pragma unroll
-    for (int j = 0; j < dK; ++j)
-      if (j < nmine) issue_k(j, j, refresh_tag);
-#pragma unroll
-    for (int j = 0; j < dV; ++j)
-      if (j < nmine) issue_v(j, j);
-    int i0 = 0;
-    for (; i0 + kU - 1 + kAhead < nmine; i0 += kU) {
-#pragma unroll
-      for (int u = 0; u < kU; ++u) {
-        issue_k((u + dK) % kKS, i0 + u + dK, refresh_tag);
-        issue_v((u + dV) % kVS, (u + dV) % kKS);
-        compute(u % kKS, u % kVS, i0 + u, Full{});
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < kU + kAhead; ++u) {
-      const int i = i0 + u;
-      if (i < nmine) {
-        if (i + dK < nmine) issue_k((u + dK) % kKS, i + dK, refresh_tag);
-        if (i + dV < nmine) issue_v((u + dV) % kVS, (u + dV) % kKS);
-        compute(u % kKS, u % kVS, i, Tail{});
-      }
-    }
-  };
-  if (nmine > 64)
-    run_ring(std::integral_constant<bool, true>{});
-  else
-    run_ring(std::integral_constant<bool, false>{});
+  bool bad_blk = false;
+  stream_pages<IO, KV, D, NT, KEEP>(a, b, g, page0 + w, kWaves, nmine, bt0, t1, lim, &sm.q[0][0][0], kmul,
+                                    1, mrow, lrow, acc, bad_blk);
 
   // ---- merge the waves through LDS, one column tile at a time -------------
   if (tid == 0) sm.bad = 0;
@@ -510,6 +549,290 @@ pa_multi_kernel(const Params a) {
   }
 }
 
+
+// ---------------------------------------------------------------------------
+// Balanced split for rows wider than one tile (partition_size ==
+// PA_SPLIT_BALANCED, G * T > 16): the work line and shares of the decode
+// balanced split (pa_schedule.h: all (sequence, KV head) pairs' pages end to
+// end, cut into one equal share per workgroup, one workgroup per CU), so a
+// long sequence no longer holds one workgroup for its whole length. Each
+// workgroup walks the pieces of its share in line order. Inside a piece its
+// waves split by row chunk (two column tiles each, as above): WC waves per
+// chunk take the piece's pages round-robin, the NCG = 4 / WC chunks of a pass
+// run side by side, so the waves of different chunks read the same pages at
+// about the same time and all but the first find them in L2 (ordinary loads
+// when a page has several readers, non-temporal when it has one). Pairs with
+// more than four chunks take several passes over the piece. The chunk's waves
+// merge through LDS; a piece that is a whole pair writes the output, any
+// other piece stores a partial result to workspace slot (first share of the
+// pair) + (pair index) + (piece index), and the piece that completes the
+// pair's count merges them (the same counter hand-off as the decode kernels).
+// Every value the piece loop and its barriers depend on is made wave-uniform
+// with readfirstlane, so every wave runs the same barriers.
+// ---------------------------------------------------------------------------
+struct MqBalLayout {
+  unsigned q, acc, m, l, badw, misc, len, pre, total;
+};
+// Tiles the waves merge through LDS at once: both of a chunk, except f32 at
+// head_dim 128, whose operands and accumulators would not fit beside the
+// largest batch's lengths.
+__host__ __device__ constexpr int mq_bal_merge_tiles(bool f32, int D) { return f32 && D == 128 ? 1 : kChunkTiles; }
+// LDS of pa_multi_bal_kernel for head_dim D, qbytes of query operand per tile,
+// ncg chunks per pass, mt tiles merged at once and B sequences (host and
+// device).
+__host__ __device__ inline MqBalLayout mq_bal_layout(int D, int qbytes, int ncg, int mt, int B) {
+  MqBalLayout o;
+  unsigned p = 0;
+  auto al = [](unsigned x) { return (x + 15u) & ~15u; };
+  o.q = p;    p = al(p + (unsigned)(ncg * kChunkTiles * qbytes));     // [chunk][tile][KQ][64]
+  o.acc = p;  p = al(p + (unsigned)(mt * kWaves * 16 * (D + 4) * 4)); // [tile][wave][row][D + 4]
+  o.m = p;    p = al(p + (unsigned)(mt * kWaves * 16 * 4));
+  o.l = p;    p = al(p + (unsigned)(mt * kWaves * 16 * 4));
+  o.badw = p; p = al(p + kWaves * 4);
+  o.misc = p; p = al(p + 8 * 4);                                   // scan sums, count flag
+  o.len = p;  p = al(p + (unsigned)B * 4);
+  o.pre = p;  p = al(p + (unsigned)(B + 1) * 4);
+  o.total = p;
+  return o;
+}
+
+// One workgroup per CU, one wave per SIMD: the whole register file is the
+// wave's (no waves-per-SIMD target).
+template <typename IO, typename KV, int D, int WC, bool KEEP>
+__global__ void __launch_bounds__(kThreads) pa_multi_bal_kernel(const Params a) {
+  using T = typename TileOf<IO, KV, D>::type;
+  using QC = typename T::QC;
+  constexpr int KQ = T::kQ;
+  constexpr int NT = kChunkTiles;      // column tiles per wave: one row chunk
+  constexpr int NCG = kWaves / WC;     // chunks of one pass
+  static_assert(WC == 1 || WC == 2 || WC == 4, "waves per chunk");
+  constexpr bool kFp8 = std::is_same<KV, FP8>::value;
+  constexpr int kMT = mq_bal_merge_tiles(std::is_same<IO, F32>::value, D);
+  extern __shared__ __attribute__((aligned(16))) uint8_t mqb_lds[];
+  const int B = a.batch, H = a.num_kv_heads, mbs = a.max_blocks_per_seq;
+  const MqBalLayout lay = mq_bal_layout(D, KQ * 64 * (int)sizeof(QC), NCG, kMT, B);
+  QC* const qsm = reinterpret_cast<QC*>(mqb_lds + lay.q);
+  float* const sacc = reinterpret_cast<float*>(mqb_lds + lay.acc);
+  float* const sm_m = reinterpret_cast<float*>(mqb_lds + lay.m);
+  float* const sm_l = reinterpret_cast<float*>(mqb_lds + lay.l);
+  int* const badw = reinterpret_cast<int*>(mqb_lds + lay.badw);
+  int* const misc = reinterpret_cast<int*>(mqb_lds + lay.misc);
+  int* const slen = reinterpret_cast<int*>(mqb_lds + lay.len);
+  int* const spre = reinterpret_cast<int*>(mqb_lds + lay.pre);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int rr = lane & 15, jj = lane >> 4;
+  const int G = a.group, TQ = a.q_len, R = a.rows;
+  const int NC = (R + 16 * NT - 1) / (16 * NT);   // row chunks of a pair
+  const int passes = (NC + NCG - 1) / NCG;
+  const int wi = w % WC, cg = w / WC;             // the wave's place in its chunk, its chunk in a pass
+
+  // Lengths into LDS and the exclusive prefix sums of their line positions
+  // (as in the decode balanced split).
+  const int per = (B + kThreads - 1) / kThreads;
+  const int bbeg = tid * per;
+  int mine = 0;
+  for (int i = 0; i < per; ++i) {
+    const int bb = bbeg + i;
+    if (bb < B) {
+      const int L = a.context_lens[bb];
+      slen[bb] = L;
+      mine += line_pages(L, mbs);
+    }
+  }
+  int incl = mine;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(incl, d);
+    if (lane >= d) incl += y;
+  }
+  if (lane == 63) misc[w] = incl;
+  __syncthreads();
+  int before = 0;
+#pragma unroll
+  for (int ww = 0; ww < kWaves; ++ww)
+    if (ww < w) before += misc[ww];
+  int pre = before + incl - mine;
+  for (int i = 0; i < per; ++i) {
+    const int bb = bbeg + i;
+    if (bb < B) {
+      spre[bb] = pre;
+      pre += line_pages(slen[bb], mbs);
+    }
+  }
+  if (tid == kThreads - 1) spre[B] = before + incl;
+  __syncthreads();
+
+  const int n = H * __builtin_amdgcn_readfirstlane(spre[B]);
+  const int S = share_count(n, gridDim.x);
+  const int wg = __builtin_amdgcn_readfirstlane(share_of_block(blockIdx.x, gridDim.x, S));
+  if (wg >= S) return;
+  const int x1 = __builtin_amdgcn_readfirstlane(share_start(wg + 1, n, S));
+  int x = __builtin_amdgcn_readfirstlane(share_start(wg, n, S));
+  // the sequence holding x
+  int b = 0;
+  {
+    int lo = 0, hi = B;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (H * __builtin_amdgcn_readfirstlane(spre[mid]) <= x) lo = mid; else hi = mid;
+    }
+    b = lo;
+  }
+  int seq_pre = __builtin_amdgcn_readfirstlane(spre[b]);
+
+  auto row_of = [&](int bb, int gg, int rho) {
+    const int t = rho / G, h = rho - t * G;
+    return ((size_t)bb * TQ + t) * a.num_q_heads + (size_t)gg * G + h;
+  };
+  auto fill_pair = [&](int bb, int gg, float v, float lse) {
+    for (int i = tid; i < R * D; i += kThreads) store_out<IO>(a.out, row_of(bb, gg, i / D) * D + i % D, v);
+    if (a.lse_out)
+      for (int rho = tid; rho < R; rho += kThreads) a.lse_out[row_of(bb, gg, rho)] = lse;
+  };
+
+  while (x < x1 && b < B) {
+    const int L = __builtin_amdgcn_readfirstlane(slen[b]);
+    const int cb = line_pages(L, mbs);
+    const int seq_first = H * seq_pre;
+    const LinePiece pc = line_piece(x, x1, seq_first, cb, b, H, n, S, wg);
+    const int g = __builtin_amdgcn_readfirstlane(pc.g);
+    const int pg_lo = __builtin_amdgcn_readfirstlane(pc.pg_lo);
+    const int pg_hi = __builtin_amdgcn_readfirstlane(pc.pg_hi);
+    const int k = __builtin_amdgcn_readfirstlane(pc.k);
+    const int nparts = __builtin_amdgcn_readfirstlane(pc.nparts);
+    const int slot0 = __builtin_amdgcn_readfirstlane(pc.slot0);
+    const int x_end = __builtin_amdgcn_readfirstlane(pc.x_end);
+
+    lds_barrier();   // the previous piece's LDS readers are done
+    const bool bad_len = L < 0 || L > mbs * kBlock;
+    if (bad_len || L == 0) {
+      // a placeholder position: the pair lies whole in this share
+      fill_pair(b, g, bad_len ? __builtin_nanf("") : 0.f, bad_len ? __builtin_nanf("") : -INFINITY);
+    } else {
+      float kmul = a.scale * kLog2e;
+      float vmul = 1.0f;
+      if constexpr (kFp8) {
+        kmul *= a.k_scale[g];
+        vmul = a.v_scale[g];
+      }
+      const int t1 = min(pg_hi * kBlock, L);
+      const int np = pg_hi - pg_lo;
+      const int nmine = np > wi ? (np - wi + WC - 1) / WC : 0;
+      const bool split = nparts > 1;
+      const size_t slot = (size_t)slot0 + k;
+      const brsrc wr_slot = buffer_rsrc(a.ws_o + slot * R * D, (uint32_t)(R * D * sizeof(float)));
+      for (int cp = 0; cp < passes; ++cp) {
+        const int c = cp * NCG + cg;   // this wave's row chunk
+        const bool active = c < NC;
+        const int bt0 = fetch_ids(a, b, pg_lo + wi, WC, 0);
+        if (cp > 0) lds_barrier();   // the previous pass's LDS readers are done
+        // the pass's query operands into LDS; rows past R repeat row R-1
+        // (finite duplicates, never stored)
+        for (int i = tid; i < NCG * NT * KQ * 64; i += kThreads) {
+          const int tj = i / (KQ * 64);
+          const int rem = i - tj * (KQ * 64);
+          const int cc = rem >> 6, ln = rem & 63;
+          const int rho = min(16 * (cp * NCG * NT + tj) + (ln & 15), R - 1);
+          const uint8_t* qrow = a.q + row_of(b, g, rho) * D * ElemSize<IO>::v;
+          qsm[i] = __builtin_bit_cast(QC, *reinterpret_cast<const u32x4*>(qrow + T::qoff(cc, ln >> 4)));
+        }
+        if (tid < kWaves) badw[tid] = 0;
+        lds_barrier();
+        int lim[NT];
+#pragma unroll
+        for (int j = 0; j < NT; ++j) lim[j] = L - TQ + min(16 * (NT * c + j) + rr, R - 1) / G;
+        float mrow[NT], lrow[NT];
+        f32x4 acc[NT][D / 16];
+        bool bad_blk = false;
+        stream_pages<IO, KV, D, NT, KEEP>(a, b, g, pg_lo + wi, WC, active ? nmine : 0, bt0, t1, lim,
+                                          qsm + (size_t)cg * NT * KQ * 64, kmul, WC == 1 ? 2 : 1, mrow,
+                                          lrow, acc, bad_blk);
+        if (bad_blk && lane == 0) badw[w] = 1;
+        // the WC waves of each chunk merge, kMT tiles at a time
+#pragma unroll
+        for (int j0 = 0; j0 < NT; j0 += kMT) {
+          float lsum[kMT];
+#pragma unroll
+          for (int jm = 0; jm < kMT; ++jm) lsum[jm] = wave_sum_rows(lrow[j0 + jm]);
+          lds_barrier();   // the previous tiles' readers are done (first: the bad flags are in)
+#pragma unroll
+          for (int jm = 0; jm < kMT; ++jm) {
+            const int sw = jm * kWaves + w;
+            if (jj == 0) {
+              sm_m[sw * 16 + rr] = mrow[j0 + jm];
+              sm_l[sw * 16 + rr] = lsum[jm];
+            }
+#pragma unroll
+            for (int t = 0; t < D / 16; ++t)
+              *reinterpret_cast<f32x4*>(&sacc[(sw * 16 + rr) * (D + 4) + 16 * t + 4 * jj]) = acc[j0 + jm][t];
+          }
+          lds_barrier();
+          for (int i = tid; i < kMT * NCG * 16 * (D / 4); i += kThreads) {   // (tile, chunk, row, quad)
+            const int jm = i / (NCG * 16 * (D / 4));
+            const int r1 = i - jm * (NCG * 16 * (D / 4));
+            const int cgi = r1 / (16 * (D / 4));
+            const int rem = r1 - cgi * (16 * (D / 4));
+            const int r2 = rem / (D / 4), d = 4 * (rem - r2 * (D / 4));
+            const int c2 = cp * NCG + cgi;
+            const int rho = 16 * (NT * c2 + j0 + jm) + r2;
+            if (c2 >= NC || rho >= R) continue;
+            float M = -INFINITY;
+            bool bad = false;
+#pragma unroll
+            for (int u = 0; u < WC; ++u) {
+              M = fmaxf(M, sm_m[(jm * kWaves + cgi * WC + u) * 16 + r2]);
+              bad |= badw[cgi * WC + u] != 0;
+            }
+            const float Ms = M == -INFINITY ? 0.f : M;
+            float W = 0.f;
+            f32x4 o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int u = 0; u < WC; ++u) {
+              const int sw = jm * kWaves + cgi * WC + u;
+              const float e = exp2_fast(sm_m[sw * 16 + r2] - Ms);
+              W += e * sm_l[sw * 16 + r2];
+              o += e * *reinterpret_cast<const f32x4*>(&sacc[(sw * 16 + r2) * (D + 4) + d]);
+            }
+            f32x4 val = {0.f, 0.f, 0.f, 0.f};
+            float lse2 = -INFINITY;
+            if (W > 0.f) {
+              val = o * (__builtin_amdgcn_rcpf(W) * vmul);
+              lse2 = M + log2_fast(W);
+            }
+            if (bad) {
+              val = f32x4{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
+              lse2 = __builtin_nanf("");
+            }
+            if (!split) {
+              const size_t orow = row_of(b, g, rho);
+              store_out4<IO>(a.out, orow * D + d, val);
+              if (d == 0 && a.lse_out) a.lse_out[orow] = lse2 * kLn2;
+            } else {
+              st_agent4(wr_slot, (uint32_t)(((size_t)rho * D + d) * sizeof(float)), val);
+              if (d == 0) st_agent(a.ws_lse + slot * R + rho, lse2);
+            }
+          }
+        }
+      }
+      if (split) {
+        const int c2 = last_to_finish(a.ws_cnt + (size_t)b * H + g, nparts, &misc[4]);
+        if (c2 == kCountLast)
+          merge_rows<IO, D>(a, b, g, 0, R, (size_t)slot0, nparts, -1);
+        else if (c2 == kCountStale && k == 0)
+          fill_pair(b, g, __builtin_nanf(""), __builtin_nanf(""));
+      }
+    }
+    x = x_end;
+    if (x == seq_first + H * cb) {
+      ++b;
+      seq_pre += cb;
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Host side.
 // ---------------------------------------------------------------------------
@@ -528,14 +851,45 @@ static hipError_t launch_d(int D, const Params& prm, dim3 grid, hipStream_t st) 
   return D == 64 ? launch_chunks<IO, KV, 64>(prm, grid, st) : launch_chunks<IO, KV, 128>(prm, grid, st);
 }
 
+// Balanced split: waves per chunk from the pair's row chunks (one chunk: all
+// four waves on it, pages read once, non-temporal; two: two waves each; more:
+// one wave per chunk, four chunks per pass), ordinary loads whenever several
+// waves read each page.
+template <typename IO, typename KV, int D, int WC>
+static hipError_t launch_bal_wc(const Params& prm, dim3 grid, hipStream_t st) {
+  using T = typename TileOf<IO, KV, D>::type;
+  const size_t lds = mq_bal_layout(D, T::kQ * 64 * (int)sizeof(typename T::QC), kWaves / WC,
+                                   mq_bal_merge_tiles(std::is_same<IO, F32>::value, D), prm.batch)
+                         .total;
+  hipLaunchKernelGGL((pa_multi_bal_kernel<IO, KV, D, WC, (WC < 4)>), grid, dim3(kThreads), lds, st, prm);
+  return hipGetLastError();
+}
+
+template <typename IO, typename KV, int D>
+static hipError_t launch_bal_d(const Params& prm, dim3 grid, hipStream_t st) {
+  if (prm.chunks == 1) return launch_bal_wc<IO, KV, D, 4>(prm, grid, st);
+  if (prm.chunks == 2) return launch_bal_wc<IO, KV, D, 2>(prm, grid, st);
+  return launch_bal_wc<IO, KV, D, 1>(prm, grid, st);
+}
+
+template <typename IO, typename KV>
+static hipError_t launch_bal(int D, const Params& prm, dim3 grid, hipStream_t st) {
+  return D == 64 ? launch_bal_d<IO, KV, 64>(prm, grid, st) : launch_bal_d<IO, KV, 128>(prm, grid, st);
+}
+
 }  // namespace pa_mq
 
 extern "C" {
 
 size_t pa_decode_multi_workspace_bytes(const pa_shape* shape, int32_t q_len) {
   if (pa_host::multi_fits_one_tile(shape, q_len)) return pa::decode_workspace_bytes(shape, q_len);
+  int shares = 0;
+  if (shape && shape->partition_size == PA_SPLIT_BALANCED) {
+    shares = pa::balanced_shares();
+    if (shares < 0) return 0;
+  }
   pa_host::MultiPlan p;
-  if (!pa_host::multi_plan(shape, q_len, &p)) return 0;
+  if (!pa_host::multi_plan(shape, q_len, &p, shares)) return 0;
   return p.total;
 }
 
@@ -551,11 +905,17 @@ pa_status pa_decode_multi(const pa_shape* shape, int32_t q_len, const void* q, c
     return pa::decode_call(shape, q_len, q, k_cache, v_cache, block_table, context_lens, scale,
                            io_dtype, kv_dtype, k_scale, v_scale, workspace, workspace_bytes, out,
                            lse_out, stream);
+  const bool balanced = shape->partition_size == PA_SPLIT_BALANCED;
   pa_host::MultiPlan pl;
-  if (!pa_host::multi_plan(shape, q_len, &pl)) return PA_ERR_SHAPE;
+  if (!pa_host::multi_plan(shape, q_len, &pl, balanced ? 1 : 0)) return PA_ERR_SHAPE;
   pa_status status = pa_host::io_args_status(q, k_cache, v_cache, block_table, context_lens, io_dtype,
                                              kv_dtype, k_scale, v_scale, out, lse_out);
   if (status != PA_OK) return status;
+  if (balanced) {
+    const int shares = pa::balanced_shares();
+    if (shares < 0) return PA_ERR_HIP;
+    if (!pa_host::multi_plan(shape, q_len, &pl, shares)) return PA_ERR_SHAPE;
+  }
   status = pa_host::workspace_status(shape->partition_size, pl.total, 0, 0, workspace, workspace_bytes);
   if (status != PA_OK) return status;
   if (shape->batch == 0) return PA_OK;
@@ -594,7 +954,16 @@ pa_status pa_decode_multi(const pa_shape* shape, int32_t q_len, const void* q, c
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int D = shape->head_dim;
   hipError_t e;
-  if (io_dtype == PA_F32)
+  if (balanced) {
+    if (io_dtype == PA_F32)
+      e = launch_bal<F32, F32>(D, prm, grid, st);
+    else if (io_dtype == PA_F16)
+      e = kv_dtype == PA_FP8_E4M3 ? launch_bal<F16, FP8>(D, prm, grid, st)
+                                  : launch_bal<F16, F16>(D, prm, grid, st);
+    else
+      e = kv_dtype == PA_FP8_E4M3 ? launch_bal<BF16, FP8>(D, prm, grid, st)
+                                  : launch_bal<BF16, BF16>(D, prm, grid, st);
+  } else if (io_dtype == PA_F32)
     e = launch_d<F32, F32>(D, prm, grid, st);
   else if (io_dtype == PA_F16)
     e = kv_dtype == PA_FP8_E4M3 ? launch_d<F16, FP8>(D, prm, grid, st)

@@ -122,6 +122,11 @@ __device__ __forceinline__ float ld_agent1(brsrc r, uint32_t off, uint32_t soff)
   return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, soff, kCpolSc1));
 }
 
+// Workgroup barrier that orders LDS only: each wave waits for its own LDS
+// (and scalar) operations, not for its global stores, which __syncthreads()
+// would wait for as well and the next LDS phase does not depend on.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 // Outcome of counting one piece of n on a workspace counter.
 constexpr int kCountMore = 0;    // other pieces are still to come
 constexpr int kCountLast = 1;    // this piece completed the count: merge, counter reset to 0

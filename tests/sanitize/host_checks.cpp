@@ -94,7 +94,8 @@ static pa_status multi_host(const pa_shape* s, int q_len, uintptr_t q, int io, i
   if (pa_host::multi_fits_one_tile(s, q_len))
     return decode_host(s, q_len, q, F, F, F, F, io, kv, ks, vs, ws, wsb, F, 0);
   pa_host::MultiPlan p;
-  if (!pa_host::multi_plan(s, q_len, &p)) return PA_ERR_SHAPE;
+  const bool balanced = s->partition_size == PA_SPLIT_BALANCED;
+  if (!pa_host::multi_plan(s, q_len, &p, balanced ? 256 : 0)) return PA_ERR_SHAPE;
   pa_status st = pa_host::io_args_status(P(q), P(F), P(F), PI(F), PI(F), (pa_dtype)io, (pa_dtype)kv,
                                          PF(ks), PF(vs), P(F), nullptr);
   if (st != PA_OK) return st;
@@ -182,7 +183,9 @@ static int mode_args() {
   {
     pa_shape t = base_shape();
     t.partition_size = PA_SPLIT_BALANCED;
-    CHECK(multi_host(&t, 5, F, 1, 1, 0, 0, 0, 0) == PA_ERR_SHAPE, "multi balanced wide");
+    CHECK(multi_host(&t, 5, F, 1, 1, 0, 0, 0, 0) == PA_ERR_WORKSPACE, "multi balanced wide");
+    t.batch = 4097;
+    CHECK(multi_host(&t, 5, F, 1, 1, 0, 0, 0, 0) == PA_ERR_SHAPE, "multi balanced batch");
     t = base_shape();
     t.partition_size = 24;
     CHECK(multi_host(&t, 4, F, 1, 1, 0, 0, 0, 0) == PA_ERR_SHAPE, "multi ps24");
@@ -357,7 +360,18 @@ static int mode_fuzz(long n, uint64_t seed) {
       CHECK(st == PA_ERR_SHAPE, "status %d", st);
     }
     pa_host::MultiPlan p;
-    if (pa_host::multi_plan(&s, q_len, &p)) {
+    const int msh = s.partition_size == PA_SPLIT_BALANCED ? shares : 0;
+    if (pa_host::multi_plan(&s, q_len, &p, msh) && s.partition_size == PA_SPLIT_BALANCED) {
+      ++ok_multi;
+      const u128 nbg = (u128)s.batch * s.num_kv_heads;
+      const u128 slots = (u128)shares + nbg;
+      auto up = [](u128 x) { return (x + 255) / 256 * 256; };
+      CHECK(s.batch <= 4096 && slots <= 0x7fffffffu, "balanced plan limits");
+      CHECK((u128)p.o_off == up(nbg * 4) && (u128)p.lse_off == p.o_off + up(slots * p.rows * s.head_dim * 4) &&
+                (u128)p.total == p.lse_off + up(slots * p.rows * 4),
+            "balanced plan layout");
+      CHECK(pa_host::multi_grid(&s, p) == (unsigned)shares, "balanced grid");
+    } else if (pa_host::multi_plan(&s, q_len, &p, msh)) {
       ++ok_multi;
       const int G = s.num_q_heads / s.num_kv_heads;
       CHECK(p.rows == G * q_len && p.tiles * 16 >= p.rows && p.chunks * 2 >= p.tiles, "plan rows");

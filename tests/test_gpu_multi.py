@@ -292,3 +292,108 @@ def test_tile_rows_split_modes_agree_and_t1_is_decode_in_every_mode():
                          float(wl.scale), partition_size=ps)
         torch.cuda.synchronize()
         assert torch.equal(got[:, 0].cpu().view(torch.int16), dec.cpu().view(torch.int16)), ps
+
+
+# ---- the balanced split for rows wider than one tile (G * T > 16) ----------
+# Cases by row chunks (two 16-row tiles each): one chunk (all four waves on
+# it), two chunks (two waves each), three and four chunks (a wave each), and
+# more than four (two passes over each piece).
+WIDE = [(4, 1, 8, 1), (8, 1, 8, 2), (28, 4, 8, 2), (8, 1, 12, 3), (28, 4, 16, 4), (16, 1, 16, 8)]
+
+
+@pytest.mark.parametrize("hq,hkv,T,chunks", WIDE)
+def test_balanced_wide_rows_every_chunk_count(hq, hkv, T, chunks):
+    G = hq // hkv
+    assert -(-(G * T) // 32) == chunks and G * T > 16
+    spec = spec_of(f"mq_balw_{hq}_{hkv}_{T}", "f16", "f16", 128, [1, 3, 17, 100, 700, 2047, 5000],
+                   hq=hq, hkv=hkv, ps=-1, seed=T + 3 * hq)
+    print(f"case {spec.name} chunks={chunks}", flush=True)
+    wl = W.make_workload(spec)
+    q = W.multi_query(wl, T)
+    out, lse = run_multi(wl, q, lse=True)
+    exp, rlse = ref_multi(wl, q, lse=True)
+    check(wl, to_f64(out), exp, label=spec.name)
+    l = lse.cpu().numpy().astype(np.float64)
+    assert np.array_equal(np.isneginf(l), np.isneginf(rlse))
+    fin = np.isfinite(rlse)
+    assert np.abs(l[fin] - rlse[fin]).max() <= 2e-3
+
+
+@pytest.mark.parametrize("io,kv", DTYPES)
+@pytest.mark.parametrize("D", [64, 128])
+def test_balanced_wide_rows_dtypes_and_head_dims(io, kv, D):
+    spec = spec_of(f"mq_balw_{io}_{kv}_{D}", io, kv, D, [2, 40, 333, 1200, 2900], hq=8, hkv=2,
+                   ps=-1, seed=11)
+    print(f"case {spec.name}", flush=True)
+    wl = W.make_workload(spec)
+    q = W.multi_query(wl, 7)        # 28 rows: two tiles
+    check(wl, to_f64(run_multi(wl, q)), ref_multi(wl, q), label=spec.name)
+    q = W.multi_query(wl, 16)       # 64 rows: two chunks
+    check(wl, to_f64(run_multi(wl, q)), ref_multi(wl, q), label=spec.name + "-T16")
+
+
+def test_balanced_wide_rows_one_pair_over_many_shares_and_many_short_pairs():
+    # one sequence far longer than the rest (its pairs are cut into many
+    # pieces, each share merging partials) and a batch of short sequences
+    # (a share walks many whole pairs)
+    lens = [30000, 7] + [int(x) for x in np.random.default_rng(5).integers(1, 120, 150)]
+    spec = spec_of("mq_balw_mix", "bf16", "bf16", 128, lens, hq=16, hkv=2, ps=-1, seed=21)
+    print(f"case {spec.name}", flush=True)
+    wl = W.make_workload(spec)
+    q = W.multi_query(wl, 5)        # 40 rows: two chunks
+    out = to_f64(run_multi(wl, q))
+    seqs = [0, 1, 2, 50, 151]
+    check(wl, out, ref_multi(wl, q, seqs=seqs), seqs=seqs, label=spec.name)
+    assert np.isfinite(out).all()
+
+
+def test_balanced_wide_rows_metadata_and_determinism():
+    spec = spec_of("mq_balw_meta", "f16", "fp8_e4m3", 128, [0, 100, 200, 3000, 50], ps=-1, seed=9)
+    wl = W.make_workload(spec)
+    t = to_device(wl)
+    t["context_lens"][1] = wl.block_table.shape[1] * 16 + 1       # beyond the table
+    t["block_table"][2, 3] = wl.num_blocks + 1000                  # beyond the pool
+    q = W.multi_query(wl, 6)        # 24 rows
+    out, lse = run_multi(wl, q, t=t, lse=True)
+    got = to_f64(out)
+    l = lse.cpu().numpy()
+    assert (got[0] == 0).all() and np.isneginf(l[0]).all()
+    assert np.isnan(got[1]).all() and np.isnan(got[2]).all()
+    check(wl, got, ref_multi(wl, q, seqs=[3, 4]), seqs=[3, 4], label="balw-meta-ok-seqs")
+    for i in range(5):
+        again = run_multi(wl, q, t=t)
+        assert torch.equal(out.cpu().view(torch.int16), again.cpu().view(torch.int16)), i
+
+
+def test_balanced_wide_rows_stale_counter_gives_nan_rows_until_reset():
+    spec = spec_of("mq_balw_stale", "f16", "f16", 128, [6000, 700], hq=8, hkv=2, ps=-1, seed=4)
+    wl = W.make_workload(spec)
+    t = to_device(wl)
+    q = W.multi_query(wl, 8)        # 32 rows
+    qt = storage_tensor(q, "f16").cuda()
+    ws = torch.zeros(pkd.workspace_bytes(qt, t["k_cache"], t["block_table"], -1),
+                     dtype=torch.uint8, device="cuda")
+    exp = ref_multi(wl, q)
+    ws.view(torch.int32)[0] = 1000          # counter of pair (0, 0): far beyond its pieces
+    G = spec.num_q_heads // spec.num_kv_heads
+    for rep in range(2):
+        out = to_f64(run_multi(wl, q, t=t, workspace=ws))
+        assert np.isnan(out[0, :, :G]).all(), rep                      # pair (0, 0), every new token
+        assert np.isfinite(out[0, :, G:]).all() and np.isfinite(out[1]).all()
+        assert np.abs(out[1] - exp[1]).max() <= 1e-2
+    pkd.reset_workspace(ws)
+    check(wl, to_f64(run_multi(wl, q, t=t, workspace=ws)), exp, label="balw stale after reset")
+
+
+def test_balanced_wide_rows_full_size_qwen7b_shape_sampled():
+    # the Qwen2.5-7B-shaped workload with 8 and 16 new tokens per sequence in
+    # the balanced split (the mode bench.py times for it)
+    spec = W.SPECS[3]
+    wl = W.make_workload(spec)
+    for T in (8, 16):
+        q = W.multi_query(wl, T)
+        print(f"case full {spec.name} T={T} balanced", flush=True)
+        out = to_f64(run_multi(wl, q, ps=-1))
+        assert np.isfinite(out).all()
+        seqs = [0, 7, 19, 31]
+        check(wl, out, ref_multi(wl, q, seqs=seqs), seqs=seqs, label=f"full-T{T}-bal")
