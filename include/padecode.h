@@ -199,14 +199,18 @@ pa_status pa_decode_noalloc(const pa_shape* shape, const void* q, const void* k_
  *   lse_out     float32 [batch][q_len][num_q_heads] (natural log) or NULL
  *   q_len       1 .. 16
  *   shape       as for pa_decode; partition_size 0, a positive multiple of
- *               16, or PA_SPLIT_BALANCED when G * q_len <= 16
- *               (G = num_q_heads / num_kv_heads)
+ *               16, or PA_SPLIT_BALANCED (batch <= 4096) for any q_len
+ *               (G = num_q_heads / num_kv_heads; rows per (sequence, KV
+ *               head) G * q_len). With PA_SPLIT_BALANCED every CU gets an
+ *               equal share of the pages of all (sequence, KV head) pairs,
+ *               whatever the row count
  *   workspace   pa_decode_multi_workspace_bytes(shape, q_len) bytes when
  *               partition_size != 0; same counter-first contract and
  *               two-level merge as pa_decode, with one counter per
  *               (sequence, KV head) and merge level-1 group when
- *               G * q_len <= 16, else ceil(ceil(G*q_len/16)/2) (one per
- *               chunk of 32 rows)
+ *               G * q_len <= 16 or the split is balanced, else
+ *               ceil(ceil(G*q_len/16)/2) (one per chunk of 32 rows); the
+ *               balanced split's size depends on the device's CU count
  * Everything else (dtypes, scales, alignment, errors) as for pa_decode. */
 size_t pa_decode_multi_workspace_bytes(const pa_shape* shape, int32_t q_len);
 pa_status pa_decode_multi(const pa_shape* shape, int32_t q_len, const void* q,

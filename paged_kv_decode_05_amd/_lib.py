@@ -277,7 +277,8 @@ def prepare(q, k_cache, v_cache, block_table, context_lens, scale, *, k_scale=No
     q [B, T, Hq, D] selects the multi-token call (pa_decode_multi): T new
     tokens per sequence whose K/V are already in the cache, new token t seeing
     positions 0 .. L-T+t; out [B, T, Hq, D], lse_out [B, T, Hq].
-    SPLIT_BALANCED needs G * T <= 16 there (G = Hq / Hkv).
+    SPLIT_BALANCED works for any T there (equal pages per CU whatever the
+    G * T rows per (sequence, KV head), G = Hq / Hkv).
     """
     import torch
     lib = load_library()
