@@ -13,11 +13,14 @@ the 256 MiB Infinity Cache cannot serve repeats.
 Two ways of splitting the work are timed, each over K calls: the workload's
 own partitioning (512-token split-K partitions for workloads 3-5, one pass for
 1-2) and the balanced split (equal page shares per workgroup, pieces merged by
-log-sum-exp); both are reported under "modes". They compute the same result
-up to float rounding and meet the same parity bar. `value` is the faster of
-the two (--split auto, the default), or the one --split names.
+log-sum-exp); both are reported under "modes". A workload whose sequences
+share a prompt prefix also times the shared-prefix call (the balanced split
+with the prefix pages read once for all sequences, pa_decode_prefix, mode
+"balanced_prefix"). They compute the same result up to float rounding and
+meet the same parity bar. `value` is the fastest (--split auto, the default),
+or the one --split names.
 
-    python bench.py [--steps K] [--warmup W] [--workload 1..5] [--split auto|spec|balanced]
+    python bench.py [--steps K] [--warmup W] [--workload 1..5] [--split auto|spec|balanced|prefix]
 
 Prints one JSON line. `value` is KV-read GB/s: the K and V bytes of every
 (sequence, cached token, KV head) the call attends, divided by the time per
@@ -54,9 +57,10 @@ def parse():
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", type=int, default=3, choices=[1, 2, 3, 4, 5])
-    ap.add_argument("--split", choices=["auto", "spec", "balanced"], default="auto",
+    ap.add_argument("--split", choices=["auto", "spec", "balanced", "prefix"], default="auto",
                     help="mode reported as `value`: the faster one, the workload's own "
-                         "partition size, or the balanced split")
+                         "partition size, the balanced split, or the balanced split with "
+                         "the shared prefix read once (workloads with a shared prefix)")
     ap.add_argument("--partition-size", type=int, default=None,
                     help="time only this partition size (0 = one pass, -1 = balanced)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
@@ -92,8 +96,18 @@ def kernel_sha256(kernel="decode"):
     return h.hexdigest()
 
 
+# mode value of the shared-prefix call (pa_decode_prefix: the balanced split
+# with the workload's shared prefix pages read once for all sequences)
+PREFIX = -100
+
+
 def mode_name(ps):
-    return {0: "one_pass", -1: "balanced"}.get(ps, f"partition{ps}")
+    return {0: "one_pass", -1: "balanced", PREFIX: "balanced_prefix"}.get(ps, f"partition{ps}")
+
+
+def mode_partition(ps):
+    """The pa_shape partition_size a mode runs with."""
+    return -1 if ps == PREFIX else ps
 
 
 def traffic_from_profile(wl_name, ps, kernel="decode", q_len=None):
@@ -584,15 +598,18 @@ class DecodeBench:
     def calls(self, ps):
         pkd, t, torch = self.pkd, self.t, self.torch
         ws = None
+        prefix = self.spec.shared_prefix_tokens // 16 if ps == PREFIX else None
         if ps:
-            need = pkd.workspace_bytes(t["q"], t["k_cache"], t["block_table"], ps)
+            need = (pkd.prefix_workspace_bytes(t["q"], t["k_cache"], t["block_table"]) if prefix is not None
+                    else pkd.workspace_bytes(t["q"], t["k_cache"], t["block_table"], ps))
             if need <= 0:
-                raise SystemExit(f"no workspace size for partition_size={ps}")
+                raise SystemExit(f"no workspace size for mode {mode_name(ps)}")
             ws = torch.empty(need, dtype=torch.uint8, device=self.dev)
             pkd.reset_workspace(ws)
         return [pkd.prepare(t["q"], self.kcs[i], self.vcs[i], t["block_table"], t["context_lens"],
                             float(self.wl.scale), k_scale=t["k_scale"], v_scale=t["v_scale"],
-                            partition_size=ps, out=self.out, workspace=ws, stream=self.stream)
+                            partition_size=mode_partition(ps), out=self.out, workspace=ws,
+                            stream=self.stream, prefix_blocks=prefix)
                 for i in range(self.reps)]
 
     def time(self, ps, steps, warmup):
@@ -713,7 +730,8 @@ def config_record(args, torch, np, pkd, W, k):
     one's numbers, and its output against the float64 oracle."""
     spec = W.SPECS[k]
     bench = DecodeBench(torch, np, pkd, W, spec)
-    modes = [spec.partition_size, pkd.SPLIT_BALANCED] + ([512] if spec.partition_size == 0 else [])
+    modes = [spec.partition_size, pkd.SPLIT_BALANCED] + ([512] if spec.partition_size == 0 else []) \
+        + ([PREFIX] if spec.shared_prefix_tokens else [])
     steps = max(50, args.steps // 4)
     timed = {m: bench.time(m, steps, max(10, args.warmup // 2)) for m in modes}
     best = min(timed, key=lambda m: timed[m][0])
@@ -748,12 +766,18 @@ def bench_decode(args, torch, np, pkd, W):
         modes = [args.partition_size]
     elif args.split == "balanced":
         modes = [pkd.SPLIT_BALANCED, spec.partition_size]
+    elif args.split == "prefix":
+        if not spec.shared_prefix_tokens:
+            raise SystemExit(f"workload {args.workload} has no shared prefix")
+        modes = [PREFIX, pkd.SPLIT_BALANCED, spec.partition_size]
     else:
         modes = [spec.partition_size, pkd.SPLIT_BALANCED]
         if spec.partition_size == 0:
             # one pass leaves a long sequence to one workgroup, which streams
             # at a per-CU rate; 512-token partitions are timed beside it
             modes.append(512)
+        if spec.shared_prefix_tokens:
+            modes.append(PREFIX)
     ps = modes[0]   # --pmc-pass profiles this one
 
     if args.pmc_pass:
@@ -807,7 +831,8 @@ def bench_decode(args, torch, np, pkd, W):
             "sum_context_tokens": sum_tokens,
             "spec_partition_size": spec.partition_size,
             "split": mode_name(ps),
-            "partition_size": ps,
+            "partition_size": mode_partition(ps),
+            "prefix_blocks": spec.shared_prefix_tokens // 16 if ps == PREFIX else None,
             "split_choice": ("the faster of the modes timed (listed under modes), all of which "
                              "compute the same result and meet the same parity bar"
                              if args.split == "auto" and args.partition_size is None
@@ -835,7 +860,7 @@ def bench_decode(args, torch, np, pkd, W):
         "flush_check": None if flushed_us is None else {
             "us_median_single_call_after_cache_eviction": round(flushed_us, 2),
             "GBps": round(kv_bytes / (flushed_us / 1e6) / 1e9, 2), "mode": mode_name(ps)},
-        "modes": {mode_name(m): {"partition_size": m, "ms_per_step": round(v[0], 6),
+        "modes": {mode_name(m): {"partition_size": mode_partition(m), "ms_per_step": round(v[0], 6),
                                  "GBps": round(kv_bytes / (v[0] / 1e3) / 1e9, 2),
                                  "max_abs_vs_value_mode": float(np.abs(v[1] - gpu_out).max())}
                   for m, v in timed.items()},

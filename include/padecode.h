@@ -157,6 +157,38 @@ pa_status pa_decode(const pa_shape* shape, const void* q, const void* k_cache,
                     size_t workspace_bytes, void* out, float* lse_out,
                     void* stream);
 
+/* Decode attention over a batch whose sequences begin with the same cached
+ * prefix ("Litellama", section "Features", Prefix Caching: requests with a
+ * common prompt prefix share its physical blocks). Same arguments, results
+ * and errors as pa_decode with shape->partition_size == PA_SPLIT_BALANCED
+ * (any other value: PA_ERR_SHAPE), plus
+ *   prefix_blocks  0 <= prefix_blocks <= max_blocks_per_seq: the number of
+ *                  leading block-table entries the rows share.
+ * With P = min(prefix_blocks, floor(longest in-contract length / 16)),
+ * sequence b takes its first P_b = min(P, floor(context_lens[b] / 16)) pages
+ * from the shared prefix: the caller declares that block_table[b][j] is the
+ * same block for every b and every j < P_b. Those pages are read once for
+ * the query rows of all sequences (per 64 query rows at most, i.e. per four
+ * groups of 16 / G sequences) instead of once per sequence; each
+ * sequence's remaining tokens go through the balanced split as in
+ * pa_decode, and the two parts are merged by log-sum-exp. The result equals
+ * pa_decode's up to float rounding. The declaration is checked as the pages
+ * are read: a sequence whose row differs from the row the prefix is read
+ * from (a longest sequence) at some j < P_b, or whose prefix holds a block
+ * id outside the pool, gets NaN outputs.
+ * workspace: at least pa_decode_prefix_workspace_bytes(shape) bytes, 256-byte
+ * aligned, with the same counter region (4 * batch * num_kv_heads bytes
+ * first) and reset rule as pa_decode's balanced split; its partial slots are
+ * (shares + 9 * batch * num_kv_heads) pieces of G rows. Calls whose partial
+ * outputs would pass 4 GiB return PA_ERR_SHAPE. */
+size_t pa_decode_prefix_workspace_bytes(const pa_shape* shape);
+pa_status pa_decode_prefix(const pa_shape* shape, int32_t prefix_blocks, const void* q,
+                           const void* k_cache, const void* v_cache, const int32_t* block_table,
+                           const int32_t* context_lens, float scale, pa_dtype io_dtype,
+                           pa_dtype kv_dtype, const float* k_scale, const float* v_scale,
+                           void* workspace, size_t workspace_bytes, void* out, float* lse_out,
+                           void* stream);
+
 /* pa_decode for callers that cannot allocate device memory or pass a
  * workspace: code under HIP graph capture, tight serving loops, harnesses
  * that forbid allocation. Same arguments, results and errors as pa_decode

@@ -5,9 +5,9 @@ Python side only marshals torch tensors into its C ABI. Importing this package
 does not load the library; `decode()` does, and raises if it is missing.
 """
 from ._lib import (SPLIT_BALANCED, BlockPool, PaError, Prepared, decode, decode_noalloc, kv_append,
-                   library_path, load_library, lse_merge, prepare, reset_workspace,
-                   workspace_bytes)
+                   library_path, load_library, lse_merge, prefix_workspace_bytes, prepare,
+                   reset_workspace, workspace_bytes)
 
 __all__ = ["SPLIT_BALANCED", "BlockPool", "PaError", "Prepared", "decode", "decode_noalloc",
-           "kv_append", "library_path", "load_library", "lse_merge", "prepare", "reset_workspace",
-           "workspace_bytes"]
+           "kv_append", "library_path", "load_library", "lse_merge", "prefix_workspace_bytes",
+           "prepare", "reset_workspace", "workspace_bytes"]

@@ -15,7 +15,8 @@ SPLIT_BALANCED = -1   # partition_size value of the balanced split (PA_SPLIT_BAL
 DTYPE_CODE = {"f32": PA_F32, "f16": PA_F16, "bf16": PA_BF16, "fp8_e4m3": PA_FP8_E4M3}
 
 EXPORTED = ("pa_decode", "pa_decode_workspace_bytes", "pa_decode_noalloc", "pa_decode_multi",
-            "pa_decode_multi_workspace_bytes", "pa_kv_append", "pa_lse_merge",
+            "pa_decode_multi_workspace_bytes", "pa_decode_prefix", "pa_decode_prefix_workspace_bytes",
+            "pa_kv_append", "pa_lse_merge",
             "pa_workspace_reset", "pa_status_str", "pa_pool_create", "pa_pool_destroy",
             "pa_pool_add_sequence", "pa_pool_append_token", "pa_pool_free_sequence",
             "pa_pool_num_free", "pa_pool_block_table")
@@ -69,6 +70,12 @@ def load_library(path=None):
                                     ctypes.c_float, ctypes.c_int, ctypes.c_int, vp, vp, vp,
                                     ctypes.c_size_t, vp, vp, vp]
     lib.pa_decode_multi.restype = ctypes.c_int
+    lib.pa_decode_prefix_workspace_bytes.argtypes = [ctypes.POINTER(PaShape)]
+    lib.pa_decode_prefix_workspace_bytes.restype = ctypes.c_size_t
+    lib.pa_decode_prefix.argtypes = [ctypes.POINTER(PaShape), ctypes.c_int32, vp, vp, vp, vp, vp,
+                                     ctypes.c_float, ctypes.c_int, ctypes.c_int, vp, vp, vp,
+                                     ctypes.c_size_t, vp, vp, vp]
+    lib.pa_decode_prefix.restype = ctypes.c_int
     lib.pa_kv_append.argtypes = [ctypes.POINTER(PaShape), vp, vp, vp, vp, ctypes.c_int,
                                  ctypes.c_int, vp, vp, vp, vp, vp]
     lib.pa_kv_append.restype = ctypes.c_int
@@ -130,6 +137,12 @@ def workspace_bytes(q, k_cache, block_table, partition_size):
     return int(lib.pa_decode_workspace_bytes(ctypes.byref(shape)))
 
 
+def prefix_workspace_bytes(q, k_cache, block_table):
+    """Workspace bytes for a shared-prefix decode call (pa_decode_prefix)."""
+    shape = make_shape(q, k_cache, block_table, SPLIT_BALANCED)
+    return int(load_library().pa_decode_prefix_workspace_bytes(ctypes.byref(shape)))
+
+
 def reset_workspace(workspace, stream=None):
     import torch
     s = stream if stream is not None else torch.cuda.current_stream()
@@ -139,10 +152,11 @@ def reset_workspace(workspace, stream=None):
 
 def decode(q, k_cache, v_cache, block_table, context_lens, scale, *, k_scale=None,
            v_scale=None, partition_size=0, out=None, workspace=None, lse_out=None,
-           stream=None):
+           stream=None, prefix_blocks=None):
     return prepare(q, k_cache, v_cache, block_table, context_lens, scale, k_scale=k_scale,
                    v_scale=v_scale, partition_size=partition_size, out=out,
-                   workspace=workspace, lse_out=lse_out, stream=stream)()
+                   workspace=workspace, lse_out=lse_out, stream=stream,
+                   prefix_blocks=prefix_blocks)()
 
 
 def decode_noalloc(q, k_cache, v_cache, block_table, context_lens, scale, *, k_scale=None,
@@ -256,7 +270,7 @@ def check_buffers(q, inputs, *, out=None, lse_out=None, workspace=None, k_scale=
 
 def prepare(q, k_cache, v_cache, block_table, context_lens, scale, *, k_scale=None,
             v_scale=None, partition_size=0, out=None, workspace=None, lse_out=None,
-            stream=None):
+            stream=None, prefix_blocks=None):
     """out[b, h] = softmax(scale * q[b, h] . K^T) V over sequence b's paged cache.
 
     q [B, Hq, D] (float32 | float16 | bfloat16); k_cache [nb, Hkv, D/X, 16, X];
@@ -279,6 +293,13 @@ def prepare(q, k_cache, v_cache, block_table, context_lens, scale, *, k_scale=No
     positions 0 .. L-T+t; out [B, T, Hq, D], lse_out [B, T, Hq].
     SPLIT_BALANCED works for any T there (equal pages per CU whatever the
     G * T rows per (sequence, KV head), G = Hq / Hkv).
+
+    prefix_blocks (an int, q [B, Hq, D] and SPLIT_BALANCED only) selects the
+    shared-prefix call (pa_decode_prefix): the rows' first prefix_blocks
+    block-table entries are declared the same blocks (for a sequence, those
+    among its full pages), and those pages are read once for all sequences; a
+    row that breaks the declaration gets NaN outputs. Its workspace size is
+    prefix_workspace_bytes.
     """
     import torch
     lib = load_library()
@@ -296,6 +317,8 @@ def prepare(q, k_cache, v_cache, block_table, context_lens, scale, *, k_scale=No
         raise PaError(2, "expected q [B,Hq,D] or [B,T,Hq,D], k_cache [nb,Hkv,D/X,16,X], "
                          "v_cache [nb,Hkv,D,16]")
     multi = q.dim() == 4
+    if prefix_blocks is not None and (multi or partition_size != SPLIT_BALANCED):
+        raise PaError(2, "prefix_blocks needs q [B, Hq, D] and partition_size=SPLIT_BALANCED")
     B, Hq, D = q.shape[0], q.shape[-2], q.shape[-1]
     nb, Hkv = k_cache.shape[0], k_cache.shape[1]
     if (tuple(v_cache.shape) != (nb, Hkv, D, k_cache.shape[3])
@@ -309,7 +332,8 @@ def prepare(q, k_cache, v_cache, block_table, context_lens, scale, *, k_scale=No
     shape = make_shape(q, k_cache, block_table, partition_size)
     ws_ptr, ws_bytes = None, 0
     if partition_size:
-        need = workspace_bytes(q, k_cache, block_table, partition_size)
+        need = (prefix_workspace_bytes(q, k_cache, block_table) if prefix_blocks is not None
+                else workspace_bytes(q, k_cache, block_table, partition_size))
         if workspace is None:
             workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
         ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
@@ -322,6 +346,8 @@ def prepare(q, k_cache, v_cache, block_table, context_lens, scale, *, k_scale=No
             lse_out.data_ptr() if lse_out is not None else None, s.cuda_stream)
     if multi:
         fn, args = lib.pa_decode_multi, (ctypes.byref(shape), q.shape[1]) + tail
+    elif prefix_blocks is not None:
+        fn, args = lib.pa_decode_prefix, (ctypes.byref(shape), int(prefix_blocks)) + tail
     else:
         fn, args = lib.pa_decode, (ctypes.byref(shape),) + tail
     keep = (shape, q, k_cache, v_cache, block_table, context_lens, k_scale, v_scale,

@@ -83,6 +83,7 @@ struct Params {
                         // B * Hkv * p_max partition slots
   int32_t q_len;        // new tokens per sequence (1: decode)
   int32_t gq;           // query heads per KV head (group = gq * q_len rows)
+  int32_t prefix_pages; // shared prefix: block-table entries every row shares (0: none)
 };
 
 // Several new tokens per sequence (MQ, the multi-token call when its rows fit
@@ -737,7 +738,7 @@ constexpr int kMetaPfeShift = 24;  // MQ: bit 24 set for the second-to-last page
 // quarter), slot 1 for the piece it ends with (the pair goes on past it).
 
 struct BalLayout {
-  uint32_t acc, m, l, bad, pm, red, len, pre, misc, split, total;   // byte offsets
+  uint32_t acc, m, l, bad, pm, red, len, pre, misc, split, full, pfx, total;   // byte offsets
 };
 // Per (wave, slot), recorded when the wave flushes the piece it holds: the
 // pair's sequence and KV head, its end line position, the output multiplier
@@ -748,12 +749,22 @@ constexpr int kPmB = 0, kPmG = 1, kPmEnd = 2, kPmVmul = 3, kPmParts = 4, kPmK = 
 constexpr int kPieceMeta = 8;
 constexpr int kPmUsed = 1, kPmLead = 2;
 __host__ __device__ inline uint32_t lds_align(uint32_t x) { return (x + 15u) & ~15u; }
-__host__ __device__ inline BalLayout bal_layout(int G, int D, int B) {
+// Shared prefix (pfx): the prefix shares keep one 16-row tile per wave in the
+// same acc / m / l regions ([kWaves][16][D + 4], [kWaves][16]), so each wave
+// gets max(2G, 16) rows; full holds the sequences' whole lengths (len then
+// holds their suffixes) and pfx the prefix shares' flags and counts.
+constexpr int kPfxBad = 0;                    // [kWaves][16] rows that met a bad or foreign block id
+constexpr int kPfxDone = kWaves * 16;         // [2]: sequences whose count a prefix piece completed
+constexpr int kPfxKey = kPfxDone + 2;         // [kWaves][2]: longest sequence, per wave
+constexpr int kPfxJob = kPfxKey + 2 * kWaves; // [3][64]: pairs a workgroup merges (pair, pieces, slot0)
+constexpr int kPfxInts = kPfxJob + 3 * 64;
+__host__ __device__ inline BalLayout bal_layout(int G, int D, int B, bool pfx = false) {
   BalLayout o;
   uint32_t p = 0;
-  o.acc = p;  p = lds_align(p + 4u * kWaves * 2 * G * (D + 4));   // [kWaves][2][G][D + 4]
-  o.m = p;    p = lds_align(p + 4u * kWaves * 2 * G);             // [kWaves][2][G]
-  o.l = p;    p = lds_align(p + 4u * kWaves * 2 * G);
+  const int rw = pfx && 2 * G < 16 ? 16 : 2 * G;   // rows per wave
+  o.acc = p;  p = lds_align(p + 4u * kWaves * rw * (D + 4));      // [kWaves][2][G][D + 4]
+  o.m = p;    p = lds_align(p + 4u * kWaves * rw);                // [kWaves][2][G]
+  o.l = p;    p = lds_align(p + 4u * kWaves * rw);
   o.bad = p;  p = lds_align(p + 4u * kWaves * 2);                 // [kWaves][2]
   o.pm = p;   p = lds_align(p + 4u * kWaves * 2 * kPieceMeta);    // [kWaves][2][kPieceMeta]
   o.red = p;  p = lds_align(p + 4u * kMergeScratch);
@@ -761,6 +772,8 @@ __host__ __device__ inline BalLayout bal_layout(int G, int D, int B) {
   o.pre = p;  p = lds_align(p + 4u * (B + 1));                    // [B + 1]
   o.misc = p; p = lds_align(p + 4u * kWaves);                     // wsum[kWaves]
   o.split = p; p = lds_align(p + 4u * 2 * kWaves);               // [0]: completed pairs, [1]: stale ones
+  o.full = p; p = lds_align(p + (pfx ? 4u * B : 0u));            // [B]
+  o.pfx = p;  p = lds_align(p + (pfx ? 4u * kPfxInts : 0u));
   o.total = p;
   return o;
 }
@@ -780,9 +793,11 @@ struct BalSm {
   int* misc;
   int* split;   // bit c set when the workgroup completed candidate slot c's pair ([0]) or
                 // found its counter stale and reports it ([1])
+  int* full;    // shared prefix: whole lengths (len holds the suffixes)
+  int* pfx;
   int G;
-  __device__ BalSm(int G_, int B) : G(G_) {
-    const BalLayout o = bal_layout(G_, D, B);
+  __device__ BalSm(int G_, int B, bool pfx_ = false) : G(G_) {
+    const BalLayout o = bal_layout(G_, D, B, pfx_);
     acc = reinterpret_cast<float*>(bal_lds + o.acc);
     m = reinterpret_cast<float*>(bal_lds + o.m);
     l = reinterpret_cast<float*>(bal_lds + o.l);
@@ -793,6 +808,8 @@ struct BalSm {
     pre = reinterpret_cast<int*>(bal_lds + o.pre);
     misc = reinterpret_cast<int*>(bal_lds + o.misc);
     split = reinterpret_cast<int*>(bal_lds + o.split);
+    full = reinterpret_cast<int*>(bal_lds + o.full);
+    pfx = reinterpret_cast<int*>(bal_lds + o.pfx);
   }
   __device__ float* acc_row(int w, int slot, int h) const { return acc + ((w * 2 + slot) * G + h) * (D + 4); }
   __device__ int mi(int w, int slot, int h) const { return (w * 2 + slot) * G + h; }
@@ -824,14 +841,14 @@ struct QCursor {
   int pair_first, pair_end;  // the pair's line positions
 };
 
-// The piece at line position x (uniform).
+// The piece at line position x (uniform); P: shared prefix pages (0: none).
 template <int D>
 __device__ __forceinline__ void qcursor_at(QCursor& c, const Params& a, const BalSm<D>& sm, int x,
-                                           int y1) {
+                                           int y1, int P) {
   const int H = a.num_kv_heads;
   c.b = seq_of_uniform(sm.pre, a.batch, H, x);
   c.L = __builtin_amdgcn_readfirstlane(sm.len[c.b]);
-  const int cb = line_pages(c.L, a.max_blocks_per_seq);
+  const int cb = pfx_positions(P, c.L, a.max_blocks_per_seq);
   const int sf = H * __builtin_amdgcn_readfirstlane(sm.pre[c.b]);
   c.g = (x - sf) / cb;
   c.pg_lo = x - sf - c.g * cb;
@@ -845,10 +862,15 @@ struct ShareOf {
   int wg, n, s;
 };
 
+
 // One wave's quarter [y0, y1) of share sh.
-template <typename IO, typename KV, int D, bool MQ>
+// PFX: the line holds the pairs' suffixes (len: suffix length, -1 for an
+// out-of-contract sequence), whose pages start at page (full - len) / 16 of
+// the sequence; every piece goes through a workspace slot, since the pair's
+// prefix pieces are merged with it.
+template <typename IO, typename KV, int D, bool MQ, bool PFX>
 __device__ __forceinline__ void decode_quarter(const Params& a, const BalSm<D>& sm, const ShareOf& sh,
-                                               const int y0, const int y1) {
+                                               const int y0, const int y1, const PfxGeo& pg) {
   using T = typename TileOf<IO, KV, D>::type;
   constexpr bool kFp8 = std::is_same<KV, FP8>::value;
   constexpr size_t kPageBytes = (size_t)kBlock * D * ElemSize<KV>::v;
@@ -860,6 +882,9 @@ __device__ __forceinline__ void decode_quarter(const Params& a, const BalSm<D>& 
   const int rr = lane & 15, jj = lane >> 4;
   const bool head_ok = rr < G;
   const int n = y1 - y0;
+  const int P = PFX ? pg.P : 0;
+  if constexpr (PFX)
+    if (n <= 0) return;   // a short suffix line leaves some quarters empty
 
   // ---- block ids and position facts, 64 positions per chunk ---------------
   auto fetch_chunk = [&](int c0, int& blk, int& meta) {
@@ -869,15 +894,19 @@ __device__ __forceinline__ void decode_quarter(const Params& a, const BalSm<D>& 
     if (xp < y1) {
       const int bl = seq_of(sm.pre, B, H, xp);
       const int L = sm.len[bl];
-      const int cb = line_pages(L, mbs);
+      const int cb = pfx_positions(P, L, mbs);
       const int sf = H * sm.pre[bl];
       const int g = (xp - sf) / cb;
       const int page = xp - sf - g * cb;
       const int pair_end = sf + (g + 1) * cb;
       const bool valid = L > 0 && L <= mbs * kBlock;
-      if (valid) blk = a.block_table[(size_t)bl * mbs + page];
+      int first = 0;   // PFX: the suffix's first page in the sequence
+      if constexpr (PFX) first = valid ? (sm.full[bl] - L) / kBlock : 0;
+      if (valid) blk = a.block_table[(size_t)bl * mbs + first + page];
       meta = (valid ? min(kBlock, L - page * kBlock) : 0) | (xp + 1 == min(y1, pair_end) ? kMetaEnd : 0) |
              (g << kMetaHeadShift);
+      if constexpr (PFX)
+        if (L < 0) meta |= kMetaBad;   // out-of-contract length: NaN rows
       if constexpr (MQ) {
         const int pfe = cb - 1 - page;   // pages from the end of the sequence
         if (valid && pfe <= 1) meta |= kMetaNear | (pfe << kMetaPfeShift);
@@ -890,9 +919,9 @@ __device__ __forceinline__ void decode_quarter(const Params& a, const BalSm<D>& 
 
   // ---- the pieces, in order: the current one and the next ----------------
   QCursor cur, nxt;
-  qcursor_at(cur, a, sm, y0, y1);
+  qcursor_at(cur, a, sm, y0, y1, P);
   bool has_nxt = cur.pair_end < y1;
-  if (has_nxt) qcursor_at(nxt, a, sm, cur.pair_end, y1);
+  if (has_nxt) qcursor_at(nxt, a, sm, cur.pair_end, y1, P);
   auto q_row = [&](const QCursor& c) {
     if constexpr (MQ) return (gptr)(a.q + mq_row<MQ>(a, c.b, c.g, head_ok ? rr : 0) * D * ElemSize<IO>::v);
     else return (gptr)(a.q + ((size_t)c.b * a.num_q_heads + c.g * G + (head_ok ? rr : 0)) * D * ElemSize<IO>::v);
@@ -1001,7 +1030,23 @@ __device__ __forceinline__ void decode_quarter(const Params& a, const BalSm<D>& 
   auto flush = [&]() {
     const float l = wave_sum_rows(lsum);
     const bool direct = cur.pair_first >= y0 && cur.pair_end <= y1;
-    if (direct) {
+    if (PFX && direct) {
+      // the whole suffix of the pair is here (one share, piece 0): its partial
+      // goes straight to the pair's first slot; the workgroup counts it once
+      // every wave's stores are complete
+      const int slot = share_of(cur.pair_first, sh.n, sh.s) + (cur.b * H + cur.g) * (1 + kPfxPieces);
+      if (head_ok) {
+        const bool none = !(l > 0.f);
+        const float inv = bad ? __builtin_nanf("") : (none ? 0.f : vmul_cur / l);
+        const brsrc wr = buffer_rsrc(a.ws_o + (size_t)slot * G * D, (uint32_t)(G * D * sizeof(float)));
+#pragma unroll
+        for (int t = 0; t < D / 16; ++t)
+          st_agent4(wr, (uint32_t)((rr * D + 16 * t + 4 * jj) * sizeof(float)), acc[t] * inv);
+        if (jj == 0)
+          st_agent(a.ws_lse + (size_t)slot * G + rr,
+                   bad ? __builtin_nanf("") : (none ? -INFINITY : m + log2_fast(l)));
+      }
+    } else if (direct) {
       const size_t row0 = (size_t)cur.b * a.num_q_heads + (size_t)cur.g * G;
       const bool bad_len = cur.L < 0 || cur.L > mbs * kBlock;
       if (bad_len || cur.L == 0) {
@@ -1038,15 +1083,20 @@ __device__ __forceinline__ void decode_quarter(const Params& a, const BalSm<D>& 
       const int slot = cur.pair_first <= y0 ? 0 : 1;
       const int s_first = share_of(cur.pair_first, sh.n, sh.s);
       const int s_last = share_of(cur.pair_end - 1, sh.n, sh.s);
+      int parts = s_last - s_first + 1, slot0 = s_first + cur.b * H + cur.g;
+      if constexpr (PFX) {
+        parts += pfx_pieces(pg, pfx_unit(pg, cur.b, cur.g));
+        slot0 = s_first + (cur.b * H + cur.g) * (1 + kPfxPieces);
+      }
       if (lane == 0) {
         int* e = sm.pm + (w * 2 + slot) * kPieceMeta;
         e[kPmB] = cur.b;
         e[kPmG] = cur.g;
         e[kPmEnd] = cur.pair_end;
         e[kPmVmul] = __builtin_bit_cast(int, vmul_cur);
-        e[kPmParts] = s_last - s_first + 1;
+        e[kPmParts] = parts;
         e[kPmK] = sh.wg - s_first;
-        e[kPmSlot0] = s_first + cur.b * H + cur.g;
+        e[kPmSlot0] = slot0;
         e[kPmFlags] = kPmUsed | (slot == 1 || w == 0 || cur.pair_first == y0 ? kPmLead : 0);
       }
       if (head_ok) {
@@ -1073,7 +1123,7 @@ __device__ __forceinline__ void decode_quarter(const Params& a, const BalSm<D>& 
       if constexpr (MQ) lim_cur = cur.L - a.q_len + t_rr;
       has_nxt = cur.pair_end < y1;
       if (has_nxt) {
-        qcursor_at(nxt, a, sm, cur.pair_end, y1);
+        qcursor_at(nxt, a, sm, cur.pair_end, y1, P);
         T::load_q(q_nxt, q_row(nxt), jj);
         if constexpr (kFp8) {
           kmul_nxt = a.scale * kLog2e * a.k_scale[nxt.g];
@@ -1086,6 +1136,8 @@ __device__ __forceinline__ void decode_quarter(const Params& a, const BalSm<D>& 
   auto compute = [&](int kslot, int vslot) {
     const int mk = meta_k[kslot];
     const int nvalid = mk & kMetaValid;
+    if constexpr (PFX)
+      if (nvalid == 0 && (mk & kMetaBad)) bad = true;   // placeholder of an out-of-contract length
     if (nvalid != 0) {
       if (mk & kMetaBad) bad = true;
       bool masked = nvalid != kBlock;
@@ -1159,9 +1211,10 @@ struct SlotFacts {
 // the workgroup; its G x D/4 (row, 4-float quad) items at most two per
 // thread (G <= 16), every LDS read of both issued before any arithmetic, so a
 // piece costs one LDS round trip.
-template <typename IO, typename KV, int D, bool MQ>
+template <typename IO, typename KV, int D, bool MQ, bool PFX>
 __device__ __forceinline__ void combine_pieces(const Params& a, const BalSm<D>& sm, uint32_t lead,
                                                const SlotFacts& f) {
+  constexpr bool kMayBeEmpty = MQ || PFX;   // a row may see nothing in the piece
   constexpr int kQuads = D / 4;
   static_assert(kMaxGroup * kQuads <= 2 * kThreads, "two items per thread cover a piece");
   const int tid = threadIdx.x;
@@ -1210,7 +1263,7 @@ __device__ __forceinline__ void combine_pieces(const Params& a, const BalSm<D>& 
         if ((hold >> ww) & 1) M = fmaxf(M, mv[u][ww]);
       float W = 0.f;
       f32x4 o = {0.f, 0.f, 0.f, 0.f};
-      const float Ms = (MQ && M == -INFINITY) ? 0.f : M;   // MQ: a row may see nothing here
+      const float Ms = (kMayBeEmpty && M == -INFINITY) ? 0.f : M;
 #pragma unroll
       for (int ww = 0; ww < kWaves; ++ww) {
         if ((hold >> ww) & 1) {
@@ -1221,7 +1274,7 @@ __device__ __forceinline__ void combine_pieces(const Params& a, const BalSm<D>& 
       }
       f32x4 val = o * (__builtin_amdgcn_rcpf(W) * vmul);
       float lse2 = M + log2_fast(W);
-      if constexpr (MQ) {
+      if constexpr (kMayBeEmpty) {
         if (!(W > 0.f)) {
           val = f32x4{0.f, 0.f, 0.f, 0.f};
           lse2 = -INFINITY;
@@ -1245,14 +1298,384 @@ __device__ __forceinline__ void combine_pieces(const Params& a, const BalSm<D>& 
   }
 }
 
-template <typename IO, typename KV, int D, bool MQ>
+// One wave's pages q0 .. q1 - 1 of a prefix unit (KV head g), for the query
+// rows of its tile: lane row rr sees the first vis pages (vis_min / vis_max:
+// the least and the most over the wave's rows). Block ids are read from row
+// r_star; each lane also reads its own row's id of every page it sees
+// (brow's) and marks the row bad when the two differ or the id is outside
+// the pool. Then the tail pages `tails` (bit l: the tile's sequence l, whose
+// block id and token count lane l holds in tblk / ttok) for that sequence's
+// rows alone (lane row of sequence mrow). The state (m, lsum, acc) is this
+// wave's online softmax over the pages it read. KEEP: ordinary loads (other
+// tiles read the same pages).
+template <typename IO, typename KV, int D, bool KEEP>
+__device__ __forceinline__ void prefix_stream(const Params& a, int g, int r_star, int q0, int q1,
+                                              const typename TileOf<IO, KV, D>::type::Q& q, float kmul,
+                                              int vis, int vis_min, int vis_max, int brow, uint64_t tails,
+                                              int tblk, int ttok, int mrow, float& m, float& lsum,
+                                              f32x4 (&acc)[D / 16], bool& bad) {
+  using T = typename TileOf<IO, KV, D>::type;
+  constexpr size_t kPageBytes = (size_t)kBlock * D * ElemSize<KV>::v;
+  const int lane = threadIdx.x & 63;
+  const int jj = lane >> 4;
+  const int H = a.num_kv_heads, mbs = a.max_blocks_per_seq;
+  const int n = q1 - q0;
+  const int32_t* const ref = a.block_table + (size_t)r_star * mbs;
+  const int32_t* const own = a.block_table + (size_t)brow * mbs;
+  auto fetch = [&](int c0) {
+    const int pp = q0 + c0 + lane;
+    return pp < q1 ? ref[pp] : 0;
+  };
+  int bt_cur = fetch(0), bt_nxt = n > 64 ? fetch(64) : 0;
+
+  const gptr kbase = uniform_ptr(a.k);
+  const gptr vbase = uniform_ptr(a.v);
+  const uint32_t ko = T::koff(lane), vo = T::voff(lane);
+  constexpr int kKS = T::kKStages, kVS = T::kVStages;
+  constexpr int dK = kKS - 1, dV = kVS - 1;
+  static_assert(kKS >= 1 && kVS >= 1 && dV <= dK, "ring depths");
+  constexpr int kAhead = dK > 1 ? dK : 1;
+  typename T::KRegs ring_k[kKS];
+  typename T::VRegs ring_v[kVS];
+  size_t poff[kKS];
+  int rid[kKS], oid[kKS];
+
+  auto issue_k = [&](int slot, int i, auto refresh_tag) {
+    if constexpr (decltype(refresh_tag)::value) {
+      if (i > 0 && (i & 63) == 0) {
+        bt_cur = bt_nxt;
+        if (n > i + 64) bt_nxt = fetch(i + 64);
+      }
+    }
+    const int raw = __builtin_amdgcn_readlane(bt_cur, i & 63);
+    const int phys = (unsigned)raw < (unsigned)a.num_blocks ? raw : 0;
+    poff[slot] = ((size_t)phys * H + g) * kPageBytes;
+    T::template load_k<KEEP>(ring_k[slot], kbase + poff[slot], ko);
+    rid[slot] = raw;
+    oid[slot] = own[q0 + i];
+  };
+  auto issue_v = [&](int vslot, int kslot) { T::template load_v<KEEP>(ring_v[vslot], vbase + poff[kslot], vo); };
+
+  auto page_math = [&](int kslot, int vslot, bool sees, auto masked_tag) {
+    constexpr bool kMasked = decltype(masked_tag)::value;
+    const f32x4 s = T::scores(ring_k[kslot], q);
+    float sc[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) sc[e] = (!kMasked || sees) ? s[e] * kmul : -INFINITY;
+    const float mx = wave_max_rows(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])));
+    const float mnew = fmaxf(m, mx);
+    const float msafe = (kMasked && mnew == -INFINITY) ? 0.f : mnew;
+    const float alpha = exp2_fast(m - msafe);
+    float pr[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) pr[e] = exp2_fast(sc[e] - msafe);
+    const typename T::P pk = T::pack(pr);
+    lsum = lsum * alpha + T::psum(pk);
+    m = mnew;
+    if (__any(alpha != 1.0f)) {
+#pragma unroll
+      for (int t = 0; t < D / 16; ++t) acc[t] *= alpha;
+    }
+#pragma unroll
+    for (int t = 0; t < D / 16; ++t) acc[t] = T::pv(T::pvt(ring_v[vslot], t), pk, acc[t]);
+  };
+  auto compute = [&](int kslot, int vslot, int i) {
+    const int pg_i = q0 + i;
+    const bool sees = pg_i < vis;
+    if (sees && ((unsigned)rid[kslot] >= (unsigned)a.num_blocks || oid[kslot] != rid[kslot])) bad = true;
+    if (pg_i < vis_min)
+      page_math(kslot, vslot, true, std::integral_constant<bool, false>{});
+    else if (pg_i < vis_max)
+      page_math(kslot, vslot, sees, std::integral_constant<bool, true>{});
+  };
+
+  auto run_ring = [&](auto refresh_tag) {
+#pragma unroll
+    for (int j = 0; j < dK; ++j)
+      if (j < n) issue_k(j, j, refresh_tag);
+#pragma unroll
+    for (int j = 0; j < dV; ++j)
+      if (j < n) issue_v(j, j);
+    constexpr int kU = kKS * kVS / gcd_c(kKS, kVS);
+    int i0 = 0;
+    for (; i0 + kU - 1 + kAhead < n; i0 += kU) {
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        issue_k((u + dK) % kKS, i0 + u + dK, refresh_tag);
+        issue_v((u + dV) % kVS, (u + dV) % kKS);
+        compute(u % kKS, u % kVS, i0 + u);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kU + kAhead; ++u) {
+      const int i = i0 + u;
+      if (i < n) {
+        if (i + dK < n) issue_k((u + dK) % kKS, i + dK, refresh_tag);
+        if (i + dV < n) issue_v((u + dV) % kVS, (u + dV) % kKS);
+        compute(u % kKS, u % kVS, i);
+      }
+    }
+  };
+  if (n > 64)
+    run_ring(std::integral_constant<bool, true>{});
+  else
+    run_ring(std::integral_constant<bool, false>{});
+
+  // tail pages, one at a time (a few per unit): tokens past the sequence's
+  // length and every other sequence's rows masked, V past it zeroed
+  for (uint64_t mk = tails; mk; mk &= mk - 1) {
+    const int ml = __builtin_ctzll(mk);
+    const int raw = __builtin_amdgcn_readlane(tblk, ml);
+    const int tok = __builtin_amdgcn_readlane(ttok, ml);
+    const bool sees = mrow == ml;
+    const int phys = (unsigned)raw < (unsigned)a.num_blocks ? raw : 0;
+    if (sees && phys != raw) bad = true;
+    const size_t off = ((size_t)phys * H + g) * kPageBytes;
+    T::load_k(ring_k[0], kbase + off, ko);
+    T::load_v(ring_v[0], vbase + off, vo);
+    const f32x4 sv = T::scores(ring_k[0], q);
+    float sc[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) sc[e] = (sees && 4 * jj + e < tok) ? sv[e] * kmul : -INFINITY;
+    const float mx = wave_max_rows(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])));
+    const float mnew = fmaxf(m, mx);
+    const float msafe = mnew == -INFINITY ? 0.f : mnew;
+    const float alpha = exp2_fast(m - msafe);
+    float pr[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) pr[e] = exp2_fast(sc[e] - msafe);
+    const typename T::P pk = T::pack(pr);
+    lsum = lsum * alpha + T::psum(pk);
+    m = mnew;
+#pragma unroll
+    for (int t = 0; t < D / 16; ++t) {
+      acc[t] *= alpha;
+      acc[t] = T::pv(T::zero_tail(T::pvt(ring_v[0], t), jj, tok), pk, acc[t]);
+    }
+  }
+}
+
+// Own pieces and first slot of pair (b, g) under the shared prefix: the
+// shares its suffix spans on the suffix line (n_s positions, s_n shares).
+template <int D>
+__device__ __forceinline__ PfxSlots pfx_pair_slots(const Params& a, const BalSm<D>& sm, const PfxGeo& pg,
+                                                   int b, int g, int n_s, int s_n) {
+  const int H = a.num_kv_heads;
+  const int cb = pfx_positions(pg.P, sm.len[b], a.max_blocks_per_seq);
+  return pfx_slots(H * sm.pre[b] + g * cb, cb, b * H + g, n_s, s_n);
+}
+
+// Prefix share k: its pieces of the prefix line in order. Per piece (unit u
+// = (g, pass), pages p_lo .. p_hi - 1): the pass's nt tiles run side by side,
+// wc = 4 / nt waves per tile (one wave idle when nt = 3) splitting the pages;
+// the tile's waves merge through LDS into one partial result per (sequence,
+// head) row, stored to the sequence's prefix slot; then one lane per sequence
+// of the pass counts the piece on its pair's counter, and the pairs this
+// piece completes are merged here. Control flow around the barriers depends
+// only on uniform values.
+template <typename IO, typename KV, int D>
+__device__ __forceinline__ void prefix_share(const Params& a, const BalSm<D>& sm, const PfxGeo& pg, int k,
+                                             int n_s, int s_n) {
+  using T = typename TileOf<IO, KV, D>::type;
+  constexpr bool kFp8 = std::is_same<KV, FP8>::value;
+  constexpr int kQuads = D / 4;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int rr = lane & 15, jj = lane >> 4;
+  const int G = a.group, H = a.num_kv_heads, B = a.batch, mbs = a.max_blocks_per_seq;
+  const int P = pg.P, mpt = pg.mpt;
+  const int x1 = share_start(k + 1, pg.np, pg.sp);
+  int x = share_start(k, pg.np, pg.sp);
+  const brsrc wo = buffer_rsrc(a.ws_o, 0xfffffff0u);
+  while (x < x1) {
+    const int u = x / P;
+    const int p_lo = x - u * P;
+    const int p_hi = min(P, x1 - u * P);
+    const int g = u / pg.passes, pass = u - g * pg.passes;
+    const int nt = min(4, pg.ntile - 4 * pass);
+    const int wc = nt == 1 ? 4 : (nt == 2 ? 2 : 1);
+    const int tile = w / wc, wi = w - tile * wc;
+    const bool active = tile < nt;
+    const int span = p_hi - p_lo;
+    const int q0 = p_lo + span * wi / wc, q1 = p_lo + span * (wi + 1) / wc;
+    const int b_tile = (4 * pass + (active ? tile : 0)) * mpt;   // first sequence of the tile
+    const int mrow = rr / G, h = rr - mrow * G;
+    const int bq = b_tile + mrow;
+    const bool row_ok = active && mrow < mpt && bq < B;
+    int vis = P;   // rows that hold no sequence see everything (never stored)
+    bool bad = false;
+    if (row_ok) {
+      const int L = sm.full[bq];
+      const bool in = L >= 0 && L <= mbs * kBlock;
+      vis = in ? min(P, L / kBlock) : 0;
+      bad = !in;   // an out-of-contract length: NaN rows (it has no line positions)
+    }
+    float kmul = a.scale * kLog2e, vmul = 1.0f;
+    if constexpr (kFp8) {
+      kmul *= a.k_scale[g];
+      vmul = a.v_scale[g];
+    }
+
+    // the unit's last piece also reads the tails of its sequences (suffixes
+    // of one page at most), the j-th tail of a tile by its wave j % wc
+    const int kk = k - share_of(u * P, pg.np, pg.sp);   // this piece among the unit's
+    const int pp = pfx_pieces(pg, u);
+    uint64_t tails = 0;
+    int tblk = 0, ttok = 0;
+    if (active && kk == pp - 1) {
+      const int bm = b_tile + lane;
+      bool has = false;
+      if (lane < mpt && bm < B) {
+        const int Sb = sm.len[bm];
+        if (pfx_tail(P, Sb)) {
+          has = true;
+          ttok = Sb;
+          tblk = a.block_table[(size_t)bm * mbs + (sm.full[bm] - Sb) / kBlock];
+        }
+      }
+      const uint64_t hm = __ballot(has);
+      const int rank = __builtin_amdgcn_mbcnt_hi((uint32_t)(hm >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)hm, 0u));
+      tails = __ballot(has && rank % wc == wi);
+    }
+
+    float m = -INFINITY, lsum = 0.f;
+    f32x4 acc[D / 16];
+#pragma unroll
+    for (int t = 0; t < D / 16; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (active && (q1 > q0 || tails != 0)) {
+      int vmin = vis, vmax = row_ok ? vis : 0;
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        vmin = min(vmin, __shfl_xor(vmin, d));
+        vmax = max(vmax, __shfl_xor(vmax, d));
+      }
+      vmin = __builtin_amdgcn_readfirstlane(vmin);
+      vmax = __builtin_amdgcn_readfirstlane(vmax);
+      const size_t qrow = (size_t)(row_ok ? bq : b_tile) * a.num_q_heads + (size_t)g * G + (row_ok ? h : 0);
+      typename T::Q q;
+      T::load_q(q, (gptr)(a.q + qrow * D * ElemSize<IO>::v), jj);
+      const int brow = row_ok ? bq : pg.r_star;
+      const int mr = row_ok ? mrow : -1;
+      if (nt > 1)
+        prefix_stream<IO, KV, D, true>(a, g, pg.r_star, q0, q1, q, kmul, vis, vmin, vmax, brow, tails, tblk,
+                                       ttok, mr, m, lsum, acc, bad);
+      else
+        prefix_stream<IO, KV, D, false>(a, g, pg.r_star, q0, q1, q, kmul, vis, vmin, vmax, brow, tails, tblk,
+                                        ttok, mr, m, lsum, acc, bad);
+    }
+    // the wave's state into LDS: [w][16][D + 4], m / l / bad [w][16]
+    const float l = wave_sum_rows(lsum);
+    {
+      float* row = sm.acc + (w * 16 + rr) * (D + 4);
+#pragma unroll
+      for (int t = 0; t < D / 16; ++t) *reinterpret_cast<f32x4*>(row + 16 * t + 4 * jj) = acc[t];
+      if (jj == 0) {
+        sm.m[w * 16 + rr] = m;
+        sm.l[w * 16 + rr] = l;
+        sm.pfx[kPfxBad + w * 16 + rr] = bad ? 1 : 0;
+      }
+    }
+    lds_barrier();
+
+    // one partial per (tile, row, quad) item, to the row's sequence's slot
+    const int rows_t = mpt * G;
+    const int items = nt * rows_t * kQuads;
+    for (int i = tid; i < items; i += kThreads) {
+      const int t = i / (rows_t * kQuads);
+      const int r1 = i - t * rows_t * kQuads;
+      const int r = r1 / kQuads, dq = r1 - r * kQuads;
+      const int b = (4 * pass + t) * mpt + r / G, hh = r % G;
+      if (b >= B) continue;
+      float M = -INFINITY;
+      int bd = 0;
+      for (int v = 0; v < wc; ++v) {
+        const int ww = t * wc + v;
+        M = fmaxf(M, sm.m[ww * 16 + r]);
+        bd |= sm.pfx[kPfxBad + ww * 16 + r];
+      }
+      const float Ms = M == -INFINITY ? 0.f : M;
+      float W = 0.f;
+      f32x4 o = {0.f, 0.f, 0.f, 0.f};
+      for (int v = 0; v < wc; ++v) {
+        const int ww = t * wc + v;
+        const float e = exp2_fast(sm.m[ww * 16 + r] - Ms);
+        W += e * sm.l[ww * 16 + r];
+        o += e * *reinterpret_cast<const f32x4*>(sm.acc + (ww * 16 + r) * (D + 4) + 4 * dq);
+      }
+      f32x4 val = {0.f, 0.f, 0.f, 0.f};
+      float lse2 = -INFINITY;
+      if (bd) {
+        val = f32x4{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
+        lse2 = __builtin_nanf("");
+      } else if (W > 0.f) {
+        val = o * (__builtin_amdgcn_rcpf(W) * vmul);
+        lse2 = M + log2_fast(W);
+      }
+      const PfxSlots ps = pfx_pair_slots(a, sm, pg, b, g, n_s, s_n);
+      const size_t slot = (size_t)ps.slot0 + ps.own + kk;
+      st_agent4(wo, (uint32_t)(((slot * G + hh) * D + 4 * dq) * sizeof(float)), val);
+      if (dq == 0) st_agent(a.ws_lse + slot * G + hh, lse2);
+    }
+    // the partials are complete; count this piece for every sequence of the pass
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    const int b_pass = 4 * pass * mpt;
+    const int nseq = min(4 * mpt, B - b_pass);
+    if (w == 0) {
+      int outcome = kCountMore;
+      bool first = false;   // the pair's first piece: its own piece 0, else this unit's piece 0
+      if (lane < nseq) {
+        const int b = b_pass + lane;
+        const PfxSlots ps = pfx_pair_slots(a, sm, pg, b, g, n_s, s_n);
+        outcome = count_piece(a.ws_cnt + (size_t)b * H + g, ps.own + pp);
+        first = ps.own == 0 && kk == 0;
+      }
+      const uint64_t dm = __ballot(outcome == kCountLast);
+      const uint64_t st = __ballot(outcome == kCountStale && first);
+      if (lane == 0) {
+        sm.pfx[kPfxDone] = (int)(uint32_t)dm;
+        sm.pfx[kPfxDone + 1] = (int)(uint32_t)(dm >> 32);
+        sm.pfx[kPfxKey] = (int)(uint32_t)st;
+        sm.pfx[kPfxKey + 1] = (int)(uint32_t)(st >> 32);
+      }
+    }
+    lds_barrier();
+    // a stale counter: the pair's first piece makes its rows NaN
+    const uint64_t stale = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane(sm.pfx[kPfxKey + 1]) << 32) |
+                           (uint32_t)__builtin_amdgcn_readfirstlane(sm.pfx[kPfxKey]);
+    for (uint64_t mk = stale; mk; mk &= mk - 1)
+      fill_rows<IO, D, false>(a, b_pass + __builtin_ctzll(mk), g, __builtin_nanf(""));
+    const uint64_t done = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane(sm.pfx[kPfxDone + 1]) << 32) |
+                          (uint32_t)__builtin_amdgcn_readfirstlane(sm.pfx[kPfxDone]);
+    if (done) {   // uniform
+      const int nm = __builtin_popcountll(done);
+      int npm = 0;
+      for (uint64_t mk = done; mk; mk &= mk - 1) {
+        const PfxSlots ps = pfx_pair_slots(a, sm, pg, b_pass + __builtin_ctzll(mk), g, n_s, s_n);
+        npm = max(npm, ps.own + pp);
+      }
+      merge_jobs<IO, D>(a, sm.red, nm, npm, [&](int j) {
+        uint64_t mk = done;   // the j-th completed sequence
+        for (int i = 0; i < j && i < nm - 1; ++i) mk &= mk - 1;
+        const int b = b_pass + __builtin_ctzll(mk);
+        const PfxSlots ps = pfx_pair_slots(a, sm, pg, b, g, n_s, s_n);
+        return MergeJob{b, g, ps.own + pp, (size_t)ps.slot0, -1};
+      });
+    }
+    __syncthreads();   // LDS state and flags are reused by the next piece
+    x = u * P + p_hi;
+  }
+}
+
+template <typename IO, typename KV, int D, bool MQ, bool PFX>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 pa_decode_balanced_kernel(const Params a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = tid >> 6;
   const int B = a.batch, H = a.num_kv_heads, mbs = a.max_blocks_per_seq;
-  const BalSm<D> sm(a.group, B);
+  const BalSm<D> sm(a.group, B, PFX);
   // this wave's piece slots start unused (their use is recorded when flushed)
   if (lane == 0) {
     sm.pm[(w * 2) * kPieceMeta + kPmFlags] = 0;
@@ -1264,12 +1687,60 @@ pa_decode_balanced_kernel(const Params a) {
   const int per = (B + kThreads - 1) / kThreads;
   const int bbeg = tid * per;
   int mine = 0;
-  for (int i = 0; i < per; ++i) {
-    const int bb = bbeg + i;
-    if (bb < B) {
-      const int L = a.context_lens[bb];
-      sm.len[bb] = L;
-      mine += line_pages(L, mbs);
+  PfxGeo pg{0, 1, 0, 0, 0, 0, 0};
+  if constexpr (PFX) {
+    // whole lengths, and the longest in-contract sequence (the lowest index
+    // among equals): key = L * 2^32 + (2^32 - 1 - b)
+    uint64_t key = 0;
+    for (int i = 0; i < per; ++i) {
+      const int bb = bbeg + i;
+      if (bb < B) {
+        const int L = a.context_lens[bb];
+        sm.full[bb] = L;
+        if (L >= 0 && L <= mbs * kBlock) {
+          const uint64_t kb = ((uint64_t)(uint32_t)L << 32) | (uint32_t)(0xffffffffu - (uint32_t)bb);
+          key = kb > key ? kb : key;
+        }
+      }
+    }
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)key, d);
+      const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(key >> 32), d);
+      const uint64_t o = ((uint64_t)hi << 32) | lo;
+      key = o > key ? o : key;
+    }
+    if (lane == 0) {
+      sm.pfx[kPfxKey + 2 * w] = (int)(uint32_t)key;
+      sm.pfx[kPfxKey + 2 * w + 1] = (int)(uint32_t)(key >> 32);
+    }
+    __syncthreads();
+    uint64_t best = 0;
+#pragma unroll
+    for (int ww = 0; ww < kWaves; ++ww) {
+      const uint64_t o = ((uint64_t)(uint32_t)sm.pfx[kPfxKey + 2 * ww + 1] << 32) | (uint32_t)sm.pfx[kPfxKey + 2 * ww];
+      best = o > best ? o : best;
+    }
+    const int lmax = (int)(best >> 32);
+    pg.P = best ? min(a.prefix_pages, lmax / kBlock) : 0;
+    pg.r_star = best ? (int)(0xffffffffu - (uint32_t)best) : 0;
+    // suffixes: -1 for an out-of-contract length
+    for (int i = 0; i < per; ++i) {
+      const int bb = bbeg + i;
+      if (bb < B) {
+        const int S = pfx_suffix(pg.P, sm.full[bb], mbs);
+        sm.len[bb] = S;
+        mine += pfx_positions(pg.P, S, mbs);
+      }
+    }
+  } else {
+    for (int i = 0; i < per; ++i) {
+      const int bb = bbeg + i;
+      if (bb < B) {
+        const int L = a.context_lens[bb];
+        sm.len[bb] = L;
+        mine += line_pages(L, mbs);
+      }
     }
   }
   int incl = mine;
@@ -1289,7 +1760,7 @@ pa_decode_balanced_kernel(const Params a) {
     const int bb = bbeg + i;
     if (bb < B) {
       sm.pre[bb] = pre;
-      pre += line_pages(sm.len[bb], mbs);
+      pre += pfx_positions(PFX ? pg.P : 0, sm.len[bb], mbs);
     }
   }
   if (tid == kThreads - 1) sm.pre[B] = before + incl;
@@ -1297,18 +1768,35 @@ pa_decode_balanced_kernel(const Params a) {
 
   const int total = __builtin_amdgcn_readfirstlane(sm.pre[B]);
   const int N = total * H;
-  const int S = share_count(N, (int)gridDim.x);
-  // shares numbered XCD by XCD (pa_schedule.h); a workgroup left without one
-  // returns
-  const int wg = share_of_block((int)blockIdx.x, (int)gridDim.x, S);
-  if (wg >= S) return;   // uniform
+  int S, wg;
+  if constexpr (PFX) {
+    // the prefix line, and the shares split between it and the suffix line
+    pg.P = __builtin_amdgcn_readfirstlane(pg.P);
+    pg.r_star = __builtin_amdgcn_readfirstlane(pg.r_star);
+    const int sn = pfx_split(pg, B, H, a.group, N, (int)gridDim.x);
+    const int sp = pg.sp;
+    const int wall = share_of_block((int)blockIdx.x, (int)gridDim.x, sp + sn);
+    if (wall >= sp + sn) return;   // uniform
+    if (wall < sp) {
+      prefix_share<IO, KV, D>(a, sm, pg, wall, N, sn);
+      return;
+    }
+    S = sn;
+    wg = wall - sp;
+  } else {
+    S = share_count(N, (int)gridDim.x);
+    // shares numbered XCD by XCD (pa_schedule.h); a workgroup left without one
+    // returns
+    wg = share_of_block((int)blockIdx.x, (int)gridDim.x, S);
+    if (wg >= S) return;   // uniform
+  }
   const int x0 = share_start(wg, N, S);
   const int x1 = share_start(wg + 1, N, S);
 
   // this wave's quarter of the share
   const int wu = __builtin_amdgcn_readfirstlane(w);
   auto yq = [&](int ww) { return x0 + share_start(ww, x1 - x0, kWaves); };
-  decode_quarter<IO, KV, D, MQ>(a, sm, ShareOf{wg, N, S}, yq(wu), yq(wu + 1));
+  decode_quarter<IO, KV, D, MQ, PFX>(a, sm, ShareOf{wg, N, S}, yq(wu), yq(wu + 1), pg);
   __syncthreads();
 
   // Pieces of the share whose state went through LDS, in three steps:
@@ -1329,7 +1817,7 @@ pa_decode_balanced_kernel(const Params a) {
   const int rb = rec[kPmB], rg = rec[kPmG], rs0 = rec[kPmSlot0];
   const uint32_t lead = (uint32_t)__ballot(lane < 2 * kWaves && (fl & kPmLead)) & 0xffu;
   const uint32_t split = (uint32_t)__ballot(lane < 2 * kWaves && (fl & kPmLead) && parts > 1) & 0xffu;
-  if (lead == 0) return;   // uniform
+  if (!PFX && lead == 0) return;   // uniform
   SlotFacts facts;
   facts.b = rb;
   facts.g = rg;
@@ -1347,43 +1835,154 @@ pa_decode_balanced_kernel(const Params a) {
       if (ww > wa && pend > yqv[ww]) hold |= 1 << ww;
     facts.hold = hold;
   }
-  combine_pieces<IO, KV, D, MQ>(a, sm, lead, facts);
-  if (split == 0) return;   // uniform
-  __builtin_amdgcn_s_waitcnt(0);   // this wave's partial stores are complete
-  __syncthreads();
-  if (wu == 0) {
-    int outcome = kCountMore;
-    if (lane < 2 * kWaves && ((split >> lane) & 1u))
-      outcome = count_piece(a.ws_cnt + (size_t)rb * H + rg, parts);
-    const uint32_t dm = (uint32_t)__ballot(outcome == kCountLast) & 0xffu;
-    // a stale counter: the pair's first piece makes its rows NaN
-    const uint32_t sm_ = (uint32_t)__ballot(outcome == kCountStale && rec[kPmK] == 0) & 0xffu;
-    if (lane == 0) {
-      sm.split[0] = (int)dm;
-      sm.split[1] = (int)sm_;
+  // steps 2 and 3 for the split pieces
+  auto settle_split = [&]() {
+    if (wu == 0) {
+      int outcome = kCountMore;
+      if (lane < 2 * kWaves && ((split >> lane) & 1u))
+        outcome = count_piece(a.ws_cnt + (size_t)rb * H + rg, parts);
+      const uint32_t dm = (uint32_t)__ballot(outcome == kCountLast) & 0xffu;
+      // a stale counter: the pair's first piece makes its rows NaN
+      const uint32_t sm_ = (uint32_t)__ballot(outcome == kCountStale && rec[kPmK] == 0) & 0xffu;
+      if (lane == 0) {
+        sm.split[0] = (int)dm;
+        sm.split[1] = (int)sm_;
+      }
+    }
+    lds_barrier();
+    const uint32_t stale = (uint32_t)__builtin_amdgcn_readfirstlane(sm.split[1]);
+    for (uint32_t mk = stale; mk; mk &= mk - 1) {
+      const int c = __builtin_ctz(mk);
+      fill_rows<IO, D, MQ>(a, __builtin_amdgcn_readlane(rb, c), __builtin_amdgcn_readlane(rg, c),
+                           __builtin_nanf(""));
+    }
+    // the pairs this workgroup completes, all merged in one pass
+    const uint32_t done = (uint32_t)__builtin_amdgcn_readfirstlane(sm.split[0]);
+    if (done == 0) return;   // uniform
+    int npm = 0;
+    for (uint32_t mk = done; mk; mk &= mk - 1)
+      npm = max(npm, __builtin_amdgcn_readlane(parts, __builtin_ctz(mk)));
+    const int m = __builtin_popcount(done);
+    merge_jobs<IO, D>(a, sm.red, m, npm, [&](int j) {
+      uint32_t mk = done;   // the j-th completed pair
+      for (int i = 0; i < j && i < m - 1; ++i) mk &= mk - 1;
+      const int c = __builtin_ctz(mk);
+      return MergeJob{__builtin_amdgcn_readlane(rb, c), __builtin_amdgcn_readlane(rg, c),
+                      __builtin_amdgcn_readlane(parts, c), (size_t)__builtin_amdgcn_readlane(rs0, c), -1};
+    });
+  };
+  if constexpr (!PFX) {
+    combine_pieces<IO, KV, D, MQ, PFX>(a, sm, lead, facts);
+    if (split == 0) return;   // uniform
+    __builtin_amdgcn_s_waitcnt(0);   // this wave's partial stores are complete
+    __syncthreads();
+    settle_split();
+  } else {
+    if (lead) combine_pieces<IO, KV, D, MQ, PFX>(a, sm, lead, facts);
+    __builtin_amdgcn_s_waitcnt(0);   // every partial store of this wave is complete
+    __syncthreads();
+    // Count every piece this workgroup holds at once, one lane each: the
+    // split pieces (lanes 0 .. 7, candidate slots) and the pairs whose
+    // suffix lies wholly inside a quarter (they stored their partial during
+    // the stream as piece 0 of one; per quarter a contiguous range of pair
+    // indices), 64 lanes a round; then merge every pair a round completed
+    // in one pass.
+    int qlo[kWaves], qn[kWaves];
+    int ndirect = 0;
+#pragma unroll
+    for (int ww = 0; ww < kWaves; ++ww) {
+      const int y0 = yqv[ww], y1 = yqv[ww + 1];
+      qlo[ww] = 0;
+      qn[ww] = 0;
+      if (y0 < y1) {
+        auto pair_at = [&](int x, int* first, int* end) {
+          const int b = seq_of_uniform(sm.pre, B, H, x);
+          const int cb = pfx_positions(pg.P, __builtin_amdgcn_readfirstlane(sm.len[b]), mbs);
+          const int sf = H * __builtin_amdgcn_readfirstlane(sm.pre[b]);
+          const int g = (x - sf) / cb;
+          *first = sf + g * cb;
+          *end = *first + cb;
+          return b * H + g;
+        };
+        int f0, e0, f1, e1;
+        int lo = pair_at(y0, &f0, &e0);
+        if (f0 < y0) ++lo;
+        int hi = pair_at(y1 - 1, &f1, &e1) + 1;
+        if (e1 > y1) --hi;
+        qlo[ww] = lo;
+        qn[ww] = max(0, hi - lo);
+      }
+      ndirect += qn[ww];
+    }
+    const int nitems = 2 * kWaves + ndirect;
+    int* const jpi = sm.pfx + kPfxJob;
+    int* const jnp = jpi + 64;
+    int* const js0 = jnp + 64;
+    for (int c0 = 0; c0 < nitems; c0 += 64) {
+      if (c0 > 0) __syncthreads();   // the previous round's list and merge scratch are consumed
+      if (wu == 0) {
+        const int item = c0 + lane;
+        int outcome = kCountMore, pi = 0, np = 0, s0 = 0;
+        bool first_piece = true;
+        if (item < 2 * kWaves) {
+          if ((split >> lane) & 1u) {
+            pi = rb * H + rg;
+            np = parts;
+            s0 = rs0;
+            first_piece = rec[kPmK] == 0;
+            outcome = count_piece(a.ws_cnt + (size_t)pi, np);
+          }
+        } else if (item < nitems) {
+          int d = item - 2 * kWaves, ww = 0;
+          while (d >= qn[ww]) d -= qn[ww++];
+          pi = qlo[ww] + d;
+          const int b = pi / H, g = pi - b * H;
+          // sequences without line positions inside the range are the prefix pass's
+          if (pfx_positions(pg.P, sm.len[b], mbs) > 0) {
+            const PfxSlots ps = pfx_pair_slots(a, sm, pg, b, g, N, S);
+            np = ps.own + pfx_pieces(pg, pfx_unit(pg, b, g));
+            s0 = ps.slot0;
+            outcome = count_piece(a.ws_cnt + (size_t)pi, np);
+          }
+        }
+        const uint64_t dm = __ballot(outcome == kCountLast);
+        // a stale counter: the pair's first piece makes its rows NaN
+        const uint64_t st = __ballot(outcome == kCountStale && first_piece);
+        jpi[lane] = pi;
+        jnp[lane] = np;
+        js0[lane] = s0;
+        if (lane == 0) {
+          sm.pfx[kPfxDone] = (int)(uint32_t)dm;
+          sm.pfx[kPfxDone + 1] = (int)(uint32_t)(dm >> 32);
+          sm.pfx[kPfxKey] = (int)(uint32_t)st;
+          sm.pfx[kPfxKey + 1] = (int)(uint32_t)(st >> 32);
+        }
+      }
+      lds_barrier();
+      const uint64_t done = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane(sm.pfx[kPfxDone + 1]) << 32) |
+                            (uint32_t)__builtin_amdgcn_readfirstlane(sm.pfx[kPfxDone]);
+      const uint64_t stale = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane(sm.pfx[kPfxKey + 1]) << 32) |
+                             (uint32_t)__builtin_amdgcn_readfirstlane(sm.pfx[kPfxKey]);
+      for (uint64_t mk = stale; mk; mk &= mk - 1) {
+        const int pi = __builtin_amdgcn_readfirstlane(jpi[__builtin_ctzll(mk)]);
+        fill_rows<IO, D, MQ>(a, pi / H, pi % H, __builtin_nanf(""));
+      }
+      if (done) {   // uniform
+        const int nm = __builtin_popcountll(done);
+        auto job = [&](int j) {
+          uint64_t mk = done;   // the j-th completed pair
+          for (int i = 0; i < j && i < nm - 1; ++i) mk &= mk - 1;
+          const int l = __builtin_ctzll(mk);
+          const int pi = __builtin_amdgcn_readfirstlane(jpi[l]);
+          return MergeJob{pi / H, pi % H, __builtin_amdgcn_readfirstlane(jnp[l]),
+                          (size_t)__builtin_amdgcn_readfirstlane(js0[l]), -1};
+        };
+        int npm = 0;
+        for (int j = 0; j < nm; ++j) npm = max(npm, job(j).np);
+        merge_jobs<IO, D>(a, sm.red, nm, npm, job);
+      }
     }
   }
-  lds_barrier();
-  const uint32_t stale = (uint32_t)__builtin_amdgcn_readfirstlane(sm.split[1]);
-  for (uint32_t mk = stale; mk; mk &= mk - 1) {
-    const int c = __builtin_ctz(mk);
-    fill_rows<IO, D, MQ>(a, __builtin_amdgcn_readlane(rb, c), __builtin_amdgcn_readlane(rg, c),
-                         __builtin_nanf(""));
-  }
-  // the pairs this workgroup completes, all merged in one pass
-  const uint32_t done = (uint32_t)__builtin_amdgcn_readfirstlane(sm.split[0]);
-  if (done == 0) return;   // uniform
-  int npm = 0;
-  for (uint32_t mk = done; mk; mk &= mk - 1)
-    npm = max(npm, __builtin_amdgcn_readlane(parts, __builtin_ctz(mk)));
-  const int m = __builtin_popcount(done);
-  merge_jobs<IO, D>(a, sm.red, m, npm, [&](int j) {
-    uint32_t mk = done;   // the j-th completed pair
-    for (int i = 0; i < j && i < m - 1; ++i) mk &= mk - 1;
-    const int c = __builtin_ctz(mk);
-    return MergeJob{__builtin_amdgcn_readlane(rb, c), __builtin_amdgcn_readlane(rg, c),
-                    __builtin_amdgcn_readlane(parts, c), (size_t)__builtin_amdgcn_readlane(rs0, c), -1};
-  });
 }
 
 __global__ void fill_zero_kernel(uint8_t* p, size_t n) {
@@ -1417,7 +2016,7 @@ int balanced_shares() {
 template <typename IO, typename KV, int D, bool MQ>
 static hipError_t launch(const Params& prm, dim3 grid, bool balanced, hipStream_t stream) {
   if (balanced)
-    hipLaunchKernelGGL((pa_decode_balanced_kernel<IO, KV, D, MQ>), grid, dim3(kThreads),
+    hipLaunchKernelGGL((pa_decode_balanced_kernel<IO, KV, D, MQ, false>), grid, dim3(kThreads),
                        bal_layout(prm.group, D, prm.batch).total, stream, prm);
   else
     hipLaunchKernelGGL((pa_decode_kernel<IO, KV, D, MQ>), grid, dim3(kThreads), 0, stream, prm);
@@ -1429,6 +2028,18 @@ static hipError_t launch_d(int D, const Params& prm, dim3 grid, bool balanced, h
   return D == 64 ? launch<IO, KV, 64, MQ>(prm, grid, balanced, stream)
                  : launch<IO, KV, 128, MQ>(prm, grid, balanced, stream);
 }
+
+template <typename IO, typename KV>
+static hipError_t launch_prefix(int D, const Params& prm, dim3 grid, hipStream_t stream) {
+  if (D == 64)
+    hipLaunchKernelGGL((pa_decode_balanced_kernel<IO, KV, 64, false, true>), grid, dim3(kThreads),
+                       bal_layout(prm.group, 64, prm.batch, true).total, stream, prm);
+  else
+    hipLaunchKernelGGL((pa_decode_balanced_kernel<IO, KV, 128, false, true>), grid, dim3(kThreads),
+                       bal_layout(prm.group, 128, prm.batch, true).total, stream, prm);
+  return hipGetLastError();
+}
+static_assert(kPfxPieces == pa_host::kPrefixPieces, "prefix slots per pair");
 
 }  // namespace pa
 
@@ -1447,13 +2058,16 @@ size_t decode_workspace_bytes(const pa_shape* shape, int q_len) {
 
 // cnt_region: 0 for a caller's workspace (counters packed first), else the
 // fixed counter region of the no-allocation scratch (see decode_layout).
+// prefix_blocks >= 0: the shared-prefix call (balanced split only).
 static pa_status decode_launch(const pa_shape* shape, int q_len, const void* q, const void* k_cache,
                                const void* v_cache, const int32_t* block_table,
                                const int32_t* context_lens, float scale, pa_dtype io_dtype,
                                pa_dtype kv_dtype, const float* k_scale, const float* v_scale,
                                void* workspace, size_t workspace_bytes, size_t cnt_region,
-                               void* out, float* lse_out, void* stream) {
-  pa_status st = pa_host::decode_shape_status(shape, q_len);
+                               void* out, float* lse_out, void* stream, int prefix_blocks = -1) {
+  const bool prefix = prefix_blocks >= 0;
+  pa_status st = prefix ? pa_host::prefix_shape_status(shape, prefix_blocks)
+                        : pa_host::decode_shape_status(shape, q_len);
   if (st != PA_OK) return st;
   st = pa_host::io_args_status(q, k_cache, v_cache, block_table, context_lens, io_dtype, kv_dtype,
                                k_scale, v_scale, out, lse_out);
@@ -1465,7 +2079,12 @@ static pa_status decode_launch(const pa_shape* shape, int q_len, const void* q, 
     shares = balanced_shares();
     if (shares < 0) return PA_ERR_HIP;
   }
-  const pa_host::DecodeLayout wl = pa_host::decode_layout(shape, shares, q_len, cnt_region);
+  if (prefix) {
+    st = pa_host::prefix_shares_status(shape, shares);
+    if (st != PA_OK) return st;
+  }
+  const pa_host::DecodeLayout wl = prefix ? pa_host::prefix_layout(shape, shares)
+                                          : pa_host::decode_layout(shape, shares, q_len, cnt_region);
   st = pa_host::workspace_status(shape->partition_size, wl.total, wl.cnt_bytes, cnt_region, workspace,
                                  workspace_bytes);
   if (st != PA_OK) return st;
@@ -1499,13 +2118,23 @@ static pa_status decode_launch(const pa_shape* shape, int q_len, const void* q, 
   prm.g_max = wl.g_max;
   prm.q_len = q_len;
   prm.gq = G;
+  prm.prefix_pages = prefix ? prefix_blocks : 0;
 
   // 1-D grid: one workgroup per unit, or one per share (see the kernels)
   const dim3 grid(pa_host::decode_grid(shape, wl, shares), 1, 1);
   hipStream_t hs = static_cast<hipStream_t>(stream);
   hipError_t e;
   const int D = shape->head_dim;
-  if (q_len == 1) {
+  if (prefix) {
+    if (io_dtype == PA_F32)
+      e = launch_prefix<F32, F32>(D, prm, grid, hs);
+    else if (io_dtype == PA_F16)
+      e = kv_dtype == PA_FP8_E4M3 ? launch_prefix<F16, FP8>(D, prm, grid, hs)
+                                  : launch_prefix<F16, F16>(D, prm, grid, hs);
+    else
+      e = kv_dtype == PA_FP8_E4M3 ? launch_prefix<BF16, FP8>(D, prm, grid, hs)
+                                  : launch_prefix<BF16, BF16>(D, prm, grid, hs);
+  } else if (q_len == 1) {
     if (io_dtype == PA_F32)
       e = launch_d<F32, F32, false>(D, prm, grid, balanced, hs);
     else if (io_dtype == PA_F16)
@@ -1613,6 +2242,26 @@ pa_status pa_decode_noalloc(const pa_shape* shape, const void* q, const void* k_
   return pa::decode_launch(shape, 1, q, k_cache, v_cache, block_table, context_lens, scale, io_dtype,
                            kv_dtype, k_scale, v_scale, ws, pa::kScratchBytes, pa::kScratchCounterBytes,
                            out, lse_out, stream);
+}
+
+size_t pa_decode_prefix_workspace_bytes(const pa_shape* shape) {
+  if (pa_host::prefix_shape_status(shape, 0) != PA_OK) return 0;
+  const int shares = pa::balanced_shares();
+  if (shares < 0 || pa_host::prefix_shares_status(shape, shares) != PA_OK) return 0;
+  return pa_host::prefix_layout(shape, shares).total;
+}
+
+pa_status pa_decode_prefix(const pa_shape* shape, int32_t prefix_blocks, const void* q,
+                           const void* k_cache, const void* v_cache, const int32_t* block_table,
+                           const int32_t* context_lens, float scale, pa_dtype io_dtype,
+                           pa_dtype kv_dtype, const float* k_scale, const float* v_scale,
+                           void* workspace, size_t workspace_bytes, void* out, float* lse_out,
+                           void* stream) {
+  if (!shape) return PA_ERR_NULL;
+  if (prefix_blocks < 0) return PA_ERR_SHAPE;
+  return pa::decode_launch(shape, 1, q, k_cache, v_cache, block_table, context_lens, scale, io_dtype,
+                           kv_dtype, k_scale, v_scale, workspace, workspace_bytes, 0, out, lse_out, stream,
+                           prefix_blocks);
 }
 
 pa_status pa_workspace_reset(void* workspace, size_t workspace_bytes, void* stream) {

@@ -136,6 +136,54 @@ inline pa_status workspace_status(int partition_size, size_t need, size_t cnt_by
   return PA_OK;
 }
 
+// ---------------------------------------------------------------------------
+// Shared-prefix decode (pa_decode_prefix): the balanced split with the first
+// prefix_blocks pages read once for every sequence.
+// ---------------------------------------------------------------------------
+constexpr int kPrefixPieces = 8;   // pieces of one prefix unit, at most (slots per pair beyond its own)
+
+// Workspace: one counter per (sequence, KV head), then partial slots for
+// shares + pairs * (1 + kPrefixPieces) pieces of G rows each.
+inline DecodeLayout prefix_layout(const pa_shape* s, int shares) {
+  DecodeLayout w{0, 0, 0, 0, 0, 0, 0, 0};
+  const size_t nbg = (size_t)s->batch * s->num_kv_heads;
+  const size_t slots = (size_t)shares + nbg * (1 + kPrefixPieces);
+  const size_t rows = slots * (size_t)(s->num_q_heads / s->num_kv_heads);
+  w.cnt_bytes = nbg * sizeof(uint32_t);
+  w.o_off = align_up(w.cnt_bytes, 256);
+  w.lse_off = w.o_off + align_up(rows * s->head_dim * sizeof(float), 256);
+  w.total = w.lse_off + align_up(rows * sizeof(float), 256);
+  return w;
+}
+
+// Shape checks of pa_decode_prefix that need no device: a balanced-split
+// decode shape, 0 <= prefix_blocks <= max_blocks_per_seq, and a prefix line
+// whose work (H * passes * prefix_blocks positions of cost up to 4, passes =
+// groups of four 16-row tiles of 16 / G sequences) fits int32 beside the
+// suffix line.
+inline pa_status prefix_shape_status(const pa_shape* s, int prefix_blocks) {
+  const pa_status st = decode_shape_status(s, 1);
+  if (st != PA_OK) return st;
+  if (s->partition_size != PA_SPLIT_BALANCED) return PA_ERR_SHAPE;
+  if (prefix_blocks < 0 || prefix_blocks > s->max_blocks_per_seq) return PA_ERR_SHAPE;
+  const int G = s->num_q_heads / s->num_kv_heads;
+  const long long mpt = pa::kTileRows / G;
+  const long long ntile = (s->batch + mpt - 1) / mpt;
+  const long long passes = (ntile + 3) / 4;
+  const long long line = (long long)s->batch * s->num_kv_heads * s->max_blocks_per_seq;
+  if (4LL * s->num_kv_heads * passes * prefix_blocks + line >= kInt32Max) return PA_ERR_SHAPE;
+  return PA_OK;
+}
+
+// With `shares` workgroups: at least two (one prefix share, one suffix
+// share), and partial outputs addressable with 32-bit byte offsets.
+inline pa_status prefix_shares_status(const pa_shape* s, int shares) {
+  if (shares < 2) return PA_ERR_SHAPE;
+  const DecodeLayout w = prefix_layout(s, shares);
+  if (w.lse_off - w.o_off > 0xfffffff0ull) return PA_ERR_SHAPE;
+  return PA_OK;
+}
+
 // Workgroups of a single-tile launch: one per (sequence, KV head, partition)
 // unit, or one per share of the balanced split.
 inline unsigned decode_grid(const pa_shape* s, const DecodeLayout& w, int shares) {

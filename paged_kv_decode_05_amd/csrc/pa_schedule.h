@@ -124,6 +124,128 @@ __host__ __device__ inline void walk_share(int wg, int x0, int x1, int b, int pr
   }
 }
 
+// ---------------------------------------------------------------------------
+// Shared prefix ("Litellama", "Features", Prefix Caching: sequences whose
+// prompts begin alike hold the same physical blocks for that beginning).
+// With P shared pages, sequence b takes its first P_b = min(P, floor(L_b / 16))
+// pages from the prefix and the rest, tokens 16 P_b .. L_b - 1, as its
+// suffix; the suffixes form the work line above. The prefix is read once per
+// pass: the batch's query rows are cut into 16-row tiles of 16 / G
+// sequences, four tiles make a pass, and a unit u = g * passes + pass (KV
+// head g) is the P prefix pages read for the pass's rows; units lie end to
+// end on a prefix line of np positions cut into sp prefix shares, taken by
+// the first sp workgroups, the suffix line by the next sn.
+// A piece of a unit leaves one partial result per sequence of its pass in
+// the slots of that sequence's pair: pair (b, g) owns slots slot0 .. slot0 +
+// own + pp - 1 with slot0 = (first suffix share of the pair) + (b * H + g) *
+// (1 + kPfxPieces), its own suffix pieces first (none for a pair without
+// line positions), then the pp pieces of its unit; every slot is below
+// sn + B * H * (1 + kPfxPieces).
+// ---------------------------------------------------------------------------
+constexpr int kPfxPieces = 8;   // pieces a unit is cut into, at most
+// Weight of prefix work against suffix work in the share split.
+constexpr int kPfxCostNum = 1, kPfxCostDen = 1;
+
+struct PfxGeo {
+  int P;        // shared pages read once (clamped to the longest sequence's full pages)
+  int mpt;      // sequences per tile: 16 / G
+  int ntile;    // tiles over the batch
+  int passes;   // units per KV head
+  int np;       // prefix line positions: H * passes * P
+  int sp;       // prefix shares
+  int r_star;   // the row the prefix block ids are read from (a longest sequence)
+};
+
+// The suffix length of a sequence of length L under P shared pages, or -1
+// for a length outside 0 .. 16 * max_blocks (NaN rows).
+__host__ __device__ inline int pfx_suffix(int P, int L, int max_blocks) {
+  if (L < 0 || L > max_blocks * kLineBlock) return -1;
+  const int pb = L / kLineBlock < P ? L / kLineBlock : P;
+  return L - kLineBlock * pb;
+}
+
+// Line positions of a pair whose suffix has S tokens (-1: out of contract).
+// With a prefix (P > 0) a suffix of at most one page takes none: the last
+// piece of its prefix unit reads that page (its tail) for the sequence's
+// rows, and an out-of-contract sequence gets its NaN rows from the prefix
+// pieces, so short suffixes never become tiny pairs on the line. Without one
+// it is the plain line's count (one placeholder for an empty or
+// out-of-contract sequence).
+__host__ __device__ inline int pfx_positions(int P, int S, int max_blocks) {
+  if (P > 0 && S <= kLineBlock) return 0;
+  return line_pages(S, max_blocks);
+}
+// 1 when the prefix pass reads the sequence's suffix as its tail page.
+__host__ __device__ inline int pfx_tail(int P, int S) { return P > 0 && S > 0 && S <= kLineBlock ? 1 : 0; }
+
+// Fill the prefix geometry for B sequences, H KV heads, G query heads per
+// KV head (pg.P set), a suffix line of n positions and `grid` workgroups
+// (at least 2): the shares are split between the prefix and the suffix line
+// in proportion to their work, a suffix position being one page for one
+// wave and a prefix position one page for each tile of its pass, of which a
+// workgroup runs 4 / nt at once, with a share for every unit (up to an
+// eighth of the grid); a unit stays within kPfxPieces pieces and no share of
+// either line is empty. Returns sn, the suffix shares (sp + sn <=
+// grid).
+__host__ __device__ inline int pfx_split(PfxGeo& pg, int B, int H, int G, int n, int grid) {
+  pg.mpt = 16 / G;
+  pg.ntile = (B + pg.mpt - 1) / pg.mpt;
+  pg.passes = (pg.ntile + 3) / 4;
+  pg.np = H * pg.passes * pg.P;
+  const int nt_last = pg.ntile - 4 * (pg.passes - 1);
+  const int c_last = nt_last == 1 ? 1 : (nt_last == 2 ? 2 : 4);
+  const long long wp = (long long)H * pg.P * (4LL * (pg.passes - 1) + c_last) * kPfxCostNum / kPfxCostDen;
+  const long long tot = (long long)n + wp;
+  const int st = share_count(tot < 0x7fffffffLL ? (int)tot : 0x7fffffff, grid);
+  int sp = 0;
+  if (pg.P > 0) {
+    sp = floor_div(2LL * st * wp + tot, 2LL * tot);   // rounded share of the work
+    // a unit of P positions meets at most ceil((P - 1) / len) + 1 shares of
+    // len positions or more
+    const int minlen = (pg.P - 1 + kPfxPieces - 2) / (kPfxPieces - 1);
+    const int most = pg.np / (minlen > 1 ? minlen : 1);
+    // a piece pays fixed costs (its ring's first pages, the merge of its
+    // waves, a partial per sequence, the counting): one share per unit at
+    // least, up to an eighth of the grid, so that no share runs many units
+    // of a short prefix one after another
+    const int units = H * pg.passes;
+    const int least = units < grid / 8 ? units : grid / 8;
+    sp = sp > least ? sp : least;
+    sp = sp < most ? sp : most;
+    sp = sp > grid - 1 ? grid - 1 : sp;
+    sp = sp < 1 ? 1 : sp;
+  }
+  pg.sp = sp;
+  // the suffix line keeps at least kMinSharePages positions per share, so no
+  // share is empty (a pair counts every share its pages span as a piece)
+  const int fit = share_count(n, grid - sp);
+  const int sn = st - sp < fit ? st - sp : fit;
+  return sn > 1 ? sn : 1;
+}
+
+// Own pieces and first slot of pair index `pair` = b * H + g whose suffix
+// takes cb positions from line position `first` of a suffix line of n
+// positions in s shares (a pair without positions: no own pieces, slots
+// after every share's).
+struct PfxSlots {
+  int own, slot0;
+};
+__host__ __device__ inline PfxSlots pfx_slots(int first, int cb, int pair, int n, int s) {
+  const int s_first = first < n ? share_of(first, n, s) : s;
+  const int own = cb > 0 ? share_of(first + cb - 1, n, s) - s_first + 1 : 0;
+  return PfxSlots{own, s_first + pair * (1 + kPfxPieces)};
+}
+
+// Pieces of unit u (0 without a prefix).
+__host__ __device__ inline int pfx_pieces(const PfxGeo& pg, int u) {
+  if (pg.P == 0) return 0;
+  return share_of(u * pg.P + pg.P - 1, pg.np, pg.sp) - share_of(u * pg.P, pg.np, pg.sp) + 1;
+}
+// The unit holding pair (b, g)'s prefix rows.
+__host__ __device__ inline int pfx_unit(const PfxGeo& pg, int b, int g) {
+  return g * pg.passes + (b / pg.mpt) / 4;
+}
+
 }  // namespace pa
 
 #endif  // PA_SCHEDULE_H

@@ -9,6 +9,9 @@
 //                   checked against 128-bit arithmetic of its own;
 //   line N SEED     N random batches: the shares of the work line cover every
 //                   position once, pieces and slots agree;
+//   prefix N SEED   N random batches under a shared prefix: the prefix and
+//                   suffix shares cover every page once, each pair's slots
+//                   are its pieces', disjoint from every other pair's;
 //   pool            block-pool operations read from stdin, one result line
 //                   each (compared with the oracle's pool by the caller).
 // Any failed check prints "FAIL ..." and exits 1; a sanitizer report aborts.
@@ -20,6 +23,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <algorithm>
 #include <string>
 #include <vector>
 
@@ -246,6 +250,26 @@ static int mode_args() {
   CHECK(mrg(2, 4, 128, F, F + 2, 1, F) == PA_ERR_ALIGN, "merge lse align");
   CHECK(mrg(2, 0, 128, F, F, 1, F) == PA_OK && grid == 0, "merge empty");
   CHECK(mrg(2, 0x7fffffff, 1024, F, F, 1, F) == PA_OK && grid == 0x7fffffffu + 0u, "merge max");
+  // shared prefix: balanced split only, 0 <= prefix_blocks <= max_blocks_per_seq
+  {
+    pa_shape b = base_shape();
+    b.partition_size = PA_SPLIT_BALANCED;
+    CHECK(pa_host::prefix_shape_status(nullptr, 0) == PA_ERR_NULL, "prefix null");
+    CHECK(pa_host::prefix_shape_status(&b, 0) == PA_OK && pa_host::prefix_shape_status(&b, 32) == PA_OK,
+          "prefix ok");
+    CHECK(pa_host::prefix_shape_status(&b, -1) == PA_ERR_SHAPE, "prefix negative");
+    CHECK(pa_host::prefix_shape_status(&b, 33) == PA_ERR_SHAPE, "prefix beyond the table");
+    pa_shape f = base_shape();
+    f.partition_size = 512;
+    CHECK(pa_host::prefix_shape_status(&f, 4) == PA_ERR_SHAPE, "prefix fixed partitions");
+    CHECK(pa_host::prefix_shares_status(&b, 1) == PA_ERR_SHAPE && pa_host::prefix_shares_status(&b, 256) == PA_OK,
+          "prefix shares");
+    const pa_host::DecodeLayout w = pa_host::prefix_layout(&b, 256);
+    const size_t slots = 256 + 4 * 9, rows = slots * 4;
+    CHECK(w.cnt_bytes == 16 && w.o_off == 256 && w.lse_off == 256 + rows * 128 * 4 &&
+              w.total == w.lse_off + (rows * 4 + 255) / 256 * 256,
+          "prefix layout");
+  }
   printf("args: %s\n", g_fail ? "FAILED" : "ok");
   return g_fail ? 1 : 0;
 }
@@ -469,6 +493,219 @@ static int mode_line(long n, uint64_t seed) {
   return g_fail ? 1 : 0;
 }
 
+// The shared-prefix schedule over a random batch, walked the way the kernel
+// walks it: the prefix shares cover every (unit, page) once and cut no unit
+// into more than kPfxPieces pieces; the suffix shares cover every suffix page
+// once; each pair's slots -- its own suffix pieces, then its unit's prefix
+// pieces -- are the range slot0 .. slot0 + own + pp - 1, each used once, and
+// no slot is used by two pieces or lies beyond sn + B * H * (1 + kPfxPieces).
+static int mode_prefix(long n, uint64_t seed) {
+  Rng r{seed};
+  long long ppos = 0, spos = 0, skipped = 0;
+  for (long it = 0; it < n && !g_fail; ++it) {
+    const int B = (int)r.range(1, it % 10 == 0 ? 4096 : 40);
+    const int H = (int)r.range(1, 8);
+    const int G = (int)r.range(1, 16);
+    const int mbs = (int)r.range(1, B > 40 ? 64 : 400);
+    const int preq = r.next() % 4 ? (int)r.range(0, mbs) : (int)r.range(0, 3);
+    pa_shape shp = base_shape();
+    shp.batch = B;
+    shp.num_kv_heads = H;
+    shp.num_q_heads = G * H;
+    shp.max_blocks_per_seq = mbs;
+    shp.partition_size = PA_SPLIT_BALANCED;
+    if (pa_host::prefix_shape_status(&shp, preq) != PA_OK) {
+      ++skipped;
+      continue;
+    }
+    std::vector<int> L(B);
+    for (int b = 0; b < B; ++b) {
+      const int k = (int)(r.next() % 8);
+      L[b] = k == 0 ? 0
+             : k == 1 ? (int)r.range(-3, -1)
+             : k == 2 ? mbs * 16 + (int)r.range(1, 20)
+             : k == 3 ? 16 * preq
+             : k == 4 ? std::min(mbs * 16, 16 * preq + (int)r.range(1, 40))
+                      : (int)r.range(1, mbs * 16);
+    }
+    // the kernel's scan: the longest in-contract length, lowest index first
+    int lmax = -1, rstar = 0;
+    for (int b = 0; b < B; ++b)
+      if (L[b] >= 0 && L[b] <= mbs * 16 && L[b] > lmax) {
+        lmax = L[b];
+        rstar = b;
+      }
+    pa::PfxGeo pg{};
+    pg.P = lmax >= 0 ? std::min(preq, lmax / 16) : 0;
+    pg.r_star = rstar;
+    CHECK(pg.P == 0 || (pg.P * 16 <= L[rstar] && L[rstar] <= mbs * 16), "prefix pages of the read row");
+    std::vector<int> S(B);
+    std::vector<long long> pre(B + 1, 0);
+    for (int b = 0; b < B; ++b) {
+      S[b] = pa::pfx_suffix(pg.P, L[b], mbs);
+      const bool in = L[b] >= 0 && L[b] <= mbs * 16;
+      CHECK(in ? (S[b] >= 0 && (L[b] - S[b]) % 16 == 0 && (L[b] - S[b]) / 16 == std::min(pg.P, L[b] / 16))
+               : S[b] == -1,
+            "suffix of %d", L[b]);
+      pre[b + 1] = pre[b] + pa::pfx_positions(pg.P, S[b], mbs);
+      CHECK(pa::pfx_positions(pg.P, S[b], mbs) == (pg.P > 0 && S[b] <= 16 ? 0 : pa::line_pages(S[b], mbs)),
+            "positions");
+    }
+    const long long N = pre[B] * H;
+    const int grid = (int)r.range(2, 3 * 256);
+    const int sn = pa::pfx_split(pg, B, H, G, (int)N, grid);
+    const int sp = pg.sp;
+    CHECK(sn >= 1 && sp + sn <= grid, "shares %d + %d of %d", sp, sn, grid);
+    CHECK((sp > 0) == (pg.P > 0), "prefix shares %d with P %d", sp, pg.P);
+    CHECK(pg.mpt == 16 / G && pg.ntile * pg.mpt >= B && (pg.ntile - 1) * pg.mpt < B, "tiles");
+    CHECK(pg.passes * 4 >= pg.ntile && (pg.passes - 1) * 4 < pg.ntile, "passes");
+    const int units = H * pg.passes;
+    CHECK((long long)pg.np == (long long)units * pg.P, "prefix line");
+    for (int u = 0; u < units && pg.P > 0; ++u)
+      CHECK(pa::pfx_pieces(pg, u) >= 1 && pa::pfx_pieces(pg, u) <= pa::kPfxPieces, "unit %d pieces %d", u,
+            pa::pfx_pieces(pg, u));
+    const long long nslots = (long long)sn + (long long)B * H * (1 + pa::kPfxPieces);
+    std::vector<uint8_t> used((size_t)nslots, 0);
+    auto own_of = [&](int b, int g, int* slot0) {
+      const int cb = pa::pfx_positions(pg.P, S[b], mbs);
+      const pa::PfxSlots ps = pa::pfx_slots((int)(H * pre[b]) + g * cb, cb, b * H + g, (int)N, sn);
+      *slot0 = ps.slot0;
+      return ps.own;
+    };
+    auto use = [&](long long slot) {
+      CHECK(slot >= 0 && slot < nslots, "slot %lld of %lld", slot, nslots);
+      if (slot >= 0 && slot < nslots) {
+        CHECK(used[(size_t)slot] == 0, "slot %lld used twice", slot);
+        used[(size_t)slot] = 1;
+      }
+    };
+    // prefix shares; the last piece of a unit reads its sequences' tails
+    std::vector<uint8_t> pseen((size_t)pg.np, 0);
+    std::vector<int> tail_seen((size_t)B * H, 0);
+    for (int k = 0; k < sp; ++k) {
+      const int x1 = pa::share_start(k + 1, pg.np, sp);
+      int x = pa::share_start(k, pg.np, sp);
+      while (x < x1) {
+        const int u = x / pg.P, p_lo = x - u * pg.P, p_hi = std::min(pg.P, x1 - u * pg.P);
+        CHECK(p_lo < p_hi, "empty prefix piece");
+        for (int p = p_lo; p < p_hi; ++p) {
+          uint8_t& v = pseen[(size_t)u * pg.P + p];
+          CHECK(v == 0, "prefix position visited twice");
+          v = 1;
+        }
+        ppos += p_hi - p_lo;
+        const int kk = k - pa::share_of(u * pg.P, pg.np, sp);
+        CHECK(kk >= 0 && kk < pa::pfx_pieces(pg, u), "piece %d of unit %d", kk, u);
+        const int g = u / pg.passes, pass = u - g * pg.passes;
+        const int b0 = 4 * pass * pg.mpt, nseq = std::min(4 * pg.mpt, B - b0);
+        CHECK(nseq >= 1 && nseq <= 64, "sequences of a pass %d", nseq);
+        for (int b = b0; b < b0 + nseq; ++b) {
+          CHECK(pa::pfx_unit(pg, b, g) == u, "unit of (%d, %d)", b, g);
+          int slot0;
+          const int own = own_of(b, g, &slot0);
+          use((long long)slot0 + own + kk);
+          if (kk == pa::pfx_pieces(pg, u) - 1 && pa::pfx_tail(pg.P, S[b])) ++tail_seen[(size_t)b * H + g];
+        }
+        x = u * pg.P + p_hi;
+      }
+    }
+    for (uint8_t v : pseen) CHECK(v == 1, "prefix position never visited");
+    for (int b = 0; b < B; ++b)
+      for (int g = 0; g < H; ++g)
+        CHECK(tail_seen[(size_t)b * H + g] == pa::pfx_tail(pg.P, S[b]), "tail of (%d, %d) read %d times", b, g,
+              tail_seen[(size_t)b * H + g]);
+    // the sequence holding suffix-line position x: the largest b with
+    // H * pre[b] <= x (sequences without positions share their successor's
+    // start and are passed over)
+    auto seq_at = [&](int x) {
+      int b = 0;
+      while (b + 1 < B && pre[b + 1] * H <= x) ++b;
+      return b;
+    };
+    // suffix shares, walked piece by piece as the waves of the kernel do
+    std::vector<std::vector<uint8_t>> seen(B);
+    for (int b = 0; b < B; ++b) seen[b].assign((size_t)H * pa::pfx_positions(pg.P, S[b], mbs), 0);
+    for (int w = 0; w < sn; ++w) {
+      const int x0 = pa::share_start(w, (int)N, sn), x1 = pa::share_start(w + 1, (int)N, sn);
+      int x = x0;
+      while (x < x1) {
+        const int bb = seq_at(x);
+        const int cb = pa::pfx_positions(pg.P, S[bb], mbs);
+        CHECK(cb > 0, "position %d in a sequence without positions", x);
+        if (cb <= 0) break;
+        const int g = (x - (int)(H * pre[bb])) / cb;
+        const int first = (int)(H * pre[bb]) + g * cb, end = first + cb;
+        const int x_end = std::min(x1, end);
+        int slot0;
+        const int own = own_of(bb, g, &slot0);
+        const int k = w - pa::share_of(first, (int)N, sn);
+        CHECK(k >= 0 && k < own, "own piece %d of %d", k, own);
+        use((long long)slot0 + k);
+        spos += x_end - x;
+        for (int q = x - first; q < x_end - first; ++q) {
+          uint8_t& v = seen[bb][(size_t)g * cb + q];
+          CHECK(v == 0, "suffix page visited twice");
+          v = 1;
+        }
+        x = x_end;
+      }
+    }
+    for (int b = 0; b < B; ++b)
+      for (uint8_t v : seen[b]) CHECK(v == 1, "suffix page never visited (b %d)", b);
+    // the pairs wholly inside a quarter of a suffix share (their partial is
+    // stored by the wave and counted by the workgroup afterwards) are the
+    // contiguous range of pair indices the kernel computes from the
+    // quarter's ends
+    auto pair_at = [&](int x, int* first, int* end) {
+      const int b = seq_at(x);
+      const int cb = pa::pfx_positions(pg.P, S[b], mbs);
+      const int sf = (int)(H * pre[b]);
+      const int g = (x - sf) / cb;
+      *first = sf + g * cb;
+      *end = *first + cb;
+      return b * H + g;
+    };
+    for (int w = 0; w < sn && B <= 64; ++w) {
+      const int x0 = pa::share_start(w, (int)N, sn), x1 = pa::share_start(w + 1, (int)N, sn);
+      for (int q = 0; q < 4; ++q) {
+        const int y0 = x0 + pa::share_start(q, x1 - x0, 4), y1 = x0 + pa::share_start(q + 1, x1 - x0, 4);
+        if (y0 >= y1) continue;
+        int f0, e0, f1, e1;
+        int lo = pair_at(y0, &f0, &e0);
+        if (f0 < y0) ++lo;
+        int hi = pair_at(y1 - 1, &f1, &e1) + 1;
+        if (e1 > y1) --hi;
+        for (int b = 0; b < B; ++b)
+          for (int g = 0; g < H; ++g) {
+            const int cb = pa::pfx_positions(pg.P, S[b], mbs);
+            const long long first = H * pre[b] + (long long)g * cb;
+            const bool inside = cb > 0 && first >= y0 && first + cb <= y1;
+            const int pi = b * H + g;
+            // the kernel skips pairs without positions inside the range
+            CHECK(inside == (pi >= lo && pi < hi && cb > 0), "direct range of quarter [%d, %d): pair %d", y0,
+                  y1, pi);
+          }
+      }
+    }
+    // each pair's slots are exactly its own and its unit's pieces, contiguous
+    long long expect = 0;
+    for (int b = 0; b < B; ++b)
+      for (int g = 0; g < H; ++g) {
+        int slot0;
+        const int parts = own_of(b, g, &slot0) + pa::pfx_pieces(pg, pa::pfx_unit(pg, b, g));
+        expect += parts;
+        for (int j = 0; j < parts; ++j)
+          CHECK(slot0 + j < nslots && used[(size_t)(slot0 + j)] == 1, "pair (%d, %d) slot %d unused", b, g, j);
+      }
+    long long total = 0;
+    for (uint8_t v : used) total += v;
+    CHECK(total == expect, "slots used %lld, pieces %lld", total, expect);
+  }
+  printf("prefix: %ld batches (%lld outside the limits), %lld prefix and %lld suffix positions: %s\n", n,
+         skipped, ppos, spos, g_fail ? "FAILED" : "ok");
+  return g_fail ? 1 : 0;
+}
+
 // Block-pool script: one operation per line, one result line each.
 //   C nb seed | A sid n tok... | P sid tok | F sid | N | T pad mbs k sid... | D
 static int mode_pool() {
@@ -543,7 +780,7 @@ static int mode_pool() {
 
 int main(int argc, char** argv) {
   if (argc < 2) {
-    fprintf(stderr, "usage: %s args|fuzz N SEED|line N SEED|pool\n", argv[0]);
+    fprintf(stderr, "usage: %s args|fuzz N SEED|line N SEED|prefix N SEED|pool\n", argv[0]);
     return 2;
   }
   const std::string m = argv[1];
@@ -552,6 +789,7 @@ int main(int argc, char** argv) {
   if (m == "args") return mode_args();
   if (m == "fuzz") return mode_fuzz(n, seed);
   if (m == "line") return mode_line(n, seed);
+  if (m == "prefix") return mode_prefix(n, seed);
   if (m == "pool") return mode_pool();
   fprintf(stderr, "unknown mode %s\n", m.c_str());
   return 2;

@@ -232,6 +232,44 @@ def test_multi_token_balanced_split_of_wide_rows_passes_validation():
     assert call_multi(shape(partition_size=-2), q_len=5) == 2
 
 
+def call_prefix(s, prefix_blocks, io=1, kv=1, ws=None, wsb=0, q=FAKE, out=FAKE, bt=FAKE):
+    lib = _lib.load_library()
+    sp = ctypes.byref(s) if s is not None else None
+    return lib.pa_decode_prefix(sp, prefix_blocks, q, FAKE, FAKE, bt, FAKE, 0.1, io, kv, None, None,
+                                ws, wsb, out, None, None)
+
+
+def test_shared_prefix_call_validates_before_the_device_query():
+    bal = dict(partition_size=-1)
+    assert call_prefix(None, 4) == 1
+    assert call_prefix(shape(**bal), -1) == 2
+    assert call_prefix(shape(**bal), 33) == 2                   # beyond max_blocks_per_seq
+    assert call_prefix(shape(partition_size=0), 4) == 2         # balanced split only
+    assert call_prefix(shape(partition_size=512), 4) == 2
+    assert call_prefix(shape(partition_size=-1, batch=4097), 4) == 2
+    assert call_prefix(shape(partition_size=-1, head_dim=96), 4) == 2
+    assert call_prefix(shape(**bal), 4, q=None) == 1
+    assert call_prefix(shape(**bal), 4, bt=None) == 1
+    assert call_prefix(shape(**bal), 4, io=0, kv=3) == 3        # f32 q with an fp8 cache
+    lib = _lib.load_library()
+    assert lib.pa_decode_prefix_workspace_bytes(ctypes.byref(shape(partition_size=512))) == 0
+    assert lib.pa_decode_prefix_workspace_bytes(None) == 0
+
+
+def test_shared_prefix_call_passes_validation():
+    # Without a GPU a valid call stops at the device query (PA_ERR_HIP,
+    # nothing launched) and the workspace size is unknown (0); with a GPU it
+    # would launch on the fake pointers, so it is left to the GPU tests.
+    import torch
+    if torch.cuda.device_count() > 0:
+        pytest.skip("a GPU is present: valid shapes would launch")
+    lib = _lib.load_library()
+    s = shape(partition_size=-1)
+    assert call_prefix(s, 0, ws=FAKE, wsb=1 << 30) == 6
+    assert call_prefix(s, 32, ws=FAKE, wsb=1 << 30) == 6
+    assert lib.pa_decode_prefix_workspace_bytes(ctypes.byref(s)) == 0
+
+
 def test_multi_token_workspace_size_arithmetic():
     lib = _lib.load_library()
 

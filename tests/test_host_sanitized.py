@@ -1,8 +1,9 @@
 """The library's host code built for the CPU alone under AddressSanitizer and
 UndefinedBehaviorSanitizer (g++, no HIP, no GPU): the argument checks and
 workspace layouts every entry point runs before a launch (csrc/pa_host.h,
-the same header the library compiles), the balanced split's work line
-(csrc/pa_schedule.h) and the block pool (csrc/block_pool.cpp).
+the same header the library compiles), the balanced split's work line and
+the shared-prefix schedule (csrc/pa_schedule.h) and the block pool
+(csrc/block_pool.cpp).
 tests/sanitize/host_checks.cpp holds the checks; here it is built and run,
 and its block-pool results are compared with the oracle's pool on the
 operation sequences the pool tests use. Any sanitizer report fails the test."""
@@ -68,6 +69,12 @@ def test_layouts_of_random_shapes_around_every_limit(exe, seed):
 @pytest.mark.parametrize("seed", [1, 2])
 def test_balanced_work_line_covers_every_page_once(exe, seed):
     assert run(exe, "line", 400, seed).strip().endswith("ok")
+
+
+@pytest.mark.parametrize("seed", [1, 2, 3])
+def test_shared_prefix_schedule_covers_every_page_once(exe, seed):
+    out = run(exe, "prefix", 300, seed)
+    assert out.strip().endswith("ok"), out
 
 
 class Script:
