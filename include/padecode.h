@@ -364,6 +364,15 @@ pa_status pa_pool_block_table(const pa_block_pool* pool, const int64_t* seq_ids,
                               int32_t num_seqs, int32_t max_blocks_per_seq, int32_t pad_block,
                               int32_t* block_table, int32_t* context_lens);
 
+/* The prefix of blocks the given sequences share, for pa_decode_prefix's
+ * prefix_blocks over a batch of exactly these sequences (in any order):
+ * the largest P such that every sequence holds the same blocks as the
+ * longest one (the first among equals) at each of its own full blocks below
+ * P, P at most the longest one's full blocks. 0 for num_seqs == 0.
+ * PA_ERR_STATE for an unknown seq_id; PA_ERR_SHAPE for num_seqs < 0. */
+pa_status pa_pool_shared_prefix(const pa_block_pool* pool, const int64_t* seq_ids,
+                                int32_t num_seqs, int32_t* prefix_blocks);
+
 /* Zero-fill a workspace on `stream` with a fill kernel (safe to capture in a
  * HIP graph). */
 pa_status pa_workspace_reset(void* workspace, size_t workspace_bytes,

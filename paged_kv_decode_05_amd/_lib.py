@@ -19,7 +19,7 @@ EXPORTED = ("pa_decode", "pa_decode_workspace_bytes", "pa_decode_noalloc", "pa_d
             "pa_kv_append", "pa_lse_merge",
             "pa_workspace_reset", "pa_status_str", "pa_pool_create", "pa_pool_destroy",
             "pa_pool_add_sequence", "pa_pool_append_token", "pa_pool_free_sequence",
-            "pa_pool_num_free", "pa_pool_block_table")
+            "pa_pool_num_free", "pa_pool_block_table", "pa_pool_shared_prefix")
 PA_ERR_CAPACITY, PA_ERR_STATE, PA_ERR_SCRATCH = 7, 8, 9
 NOALLOC_SCRATCH_BYTES = 16 << 20    # PA_NOALLOC_SCRATCH_BYTES
 NOALLOC_COUNTER_BYTES = 256 << 10   # PA_NOALLOC_COUNTER_BYTES
@@ -101,6 +101,8 @@ def load_library(path=None):
     lib.pa_pool_num_free.restype = i32
     lib.pa_pool_block_table.argtypes = [vp, vp, i32, i32, i32, vp, vp]
     lib.pa_pool_block_table.restype = ctypes.c_int
+    lib.pa_pool_shared_prefix.argtypes = [vp, vp, i32, ctypes.POINTER(i32)]
+    lib.pa_pool_shared_prefix.restype = ctypes.c_int
     if path is None:
         _lib = lib
     return lib
@@ -506,6 +508,16 @@ class BlockPool:
 
     def num_free(self):
         return self._lib.pa_pool_num_free(self._h)
+
+    def shared_prefix(self, seq_ids):
+        """Blocks the given sequences share from the start (prefix_blocks for
+        a shared-prefix decode of exactly these sequences)."""
+        import numpy as np
+        ids = np.ascontiguousarray(seq_ids, dtype=np.int64).reshape(-1)
+        out = ctypes.c_int32(0)
+        _check(self._lib.pa_pool_shared_prefix(self._h, ids.ctypes.data if ids.size else None, ids.size,
+                                               ctypes.byref(out)))
+        return int(out.value)
 
     def block_table(self, seq_ids, max_blocks, pad=0):
         """-> (int32 [len(seq_ids), max_blocks] block table, int32 context lengths)."""

@@ -259,4 +259,35 @@ pa_status pa_pool_block_table(const pa_block_pool* p, const int64_t* seq_ids, in
   return PA_OK;
 }
 
+pa_status pa_pool_shared_prefix(const pa_block_pool* p, const int64_t* seq_ids, int32_t num_seqs,
+                                int32_t* prefix_blocks) {
+  if (!p || !prefix_blocks || (num_seqs > 0 && !seq_ids)) return PA_ERR_NULL;
+  if (num_seqs < 0) return PA_ERR_SHAPE;
+  const Seq* ref = nullptr;   // the longest sequence, the first among equals
+  for (int32_t i = 0; i < num_seqs; ++i) {
+    auto it = p->seqs.find(seq_ids[i]);
+    if (it == p->seqs.end()) return PA_ERR_STATE;
+    if (!ref || it->second.tokens.size() > ref->tokens.size()) ref = &it->second;
+  }
+  if (!ref) {
+    *prefix_blocks = 0;
+    return PA_OK;
+  }
+  // every sequence must agree with the longest on each of its own full
+  // blocks below the answer: one that differs at block j < its full blocks
+  // bounds the answer by j
+  size_t shared = ref->tokens.size() / kBlock;
+  for (int32_t i = 0; i < num_seqs; ++i) {
+    const Seq& s = p->seqs.find(seq_ids[i])->second;
+    const size_t full = s.tokens.size() / kBlock;
+    for (size_t j = 0; j < full && j < shared; ++j)
+      if (s.blocks[j] != ref->blocks[j]) {
+        shared = j;
+        break;
+      }
+  }
+  *prefix_blocks = (int32_t)shared;
+  return PA_OK;
+}
+
 }  // extern "C"

@@ -707,7 +707,7 @@ static int mode_prefix(long n, uint64_t seed) {
 }
 
 // Block-pool script: one operation per line, one result line each.
-//   C nb seed | A sid n tok... | P sid tok | F sid | N | T pad mbs k sid... | D
+//   C nb seed | A sid n tok... | P sid tok | F sid | N | T pad mbs k sid... | S k sid... | D
 static int mode_pool() {
   pa_block_pool* pool = nullptr;
   char op[4];
@@ -759,6 +759,18 @@ static int mode_pool() {
         for (int i = 0; i < k; ++i) printf(" %d", lens[i]);
       }
       printf("\n");
+    } else if (op[0] == 'S') {
+      int k;
+      if (scanf("%d", &k) != 1 || k < 0) return 2;
+      std::vector<int64_t> ids(k + 1);
+      for (int i = 0; i < k; ++i) {
+        long long v;
+        if (scanf("%lld", &v) != 1) return 2;
+        ids[i] = v;
+      }
+      int32_t pb = -1;
+      const pa_status st = pa_pool_shared_prefix(pool, k ? ids.data() : nullptr, k, &pb);
+      printf("S %d %d\n", (int)st, st == PA_OK ? pb : -1);
     } else if (op[0] == 'D') {
       pa_pool_destroy(pool);
       pool = nullptr;
@@ -771,7 +783,8 @@ static int mode_pool() {
   int32_t c = 0;
   if (pa_pool_create(0, 1, &pool) != PA_ERR_SHAPE || pa_pool_create(4, 1, nullptr) != PA_ERR_NULL ||
       pa_pool_add_sequence(nullptr, 1, nullptr, 0, &c) != PA_ERR_NULL || pa_pool_num_free(nullptr) != -1 ||
-      pa_pool_block_table(nullptr, nullptr, 0, 1, 0, nullptr, nullptr) != PA_ERR_NULL)
+      pa_pool_block_table(nullptr, nullptr, 0, 1, 0, nullptr, nullptr) != PA_ERR_NULL ||
+      pa_pool_shared_prefix(nullptr, nullptr, 0, &c) != PA_ERR_NULL)
     printf("FAIL null pool arguments\n");
   pa_pool_destroy(nullptr);
   pa_pool_destroy(pool);

@@ -140,3 +140,32 @@ def test_pool_tables_speculative_verify_steps(io, kv, ps):
         exp = oracle.multi_query_ref(q, wl.k_cache, wl.v_cache, table, lens, wl.scale, io, kv,
                                      ks, vs)
         check(wl, to_f64(out), exp, label=f"verify step {step} {io}/{kv} ps{ps}")
+
+
+def _rows(wl, rows):
+    """The workload restricted to some of its sequences (same caches)."""
+    import dataclasses
+    rows = list(rows)
+    spec = dataclasses.replace(wl.spec, batch=len(rows),
+                               lens=("fixed", [int(wl.context_lens[r]) for r in rows]))
+    return dataclasses.replace(wl, spec=spec, context_lens=wl.context_lens[rows].copy(),
+                               block_table=wl.block_table[rows].copy(), q=wl.q[rows].copy())
+
+
+@pytest.mark.parametrize("io,kv", [("bf16", "bf16"), ("f16", "fp8_e4m3")])
+def test_shared_prefix_decode_with_the_pools_prefix(io, kv):
+    # the pool reports the blocks a set of its sequences shares; declared to
+    # the shared-prefix decode, they are read once for the whole batch
+    wl, pool = pool_workload(io, kv, pkd.SPLIT_BALANCED, 41)
+    for rows in (range(6), (1, 2, 4, 5)):
+        sub = _rows(wl, rows)
+        P = pool.shared_prefix(list(rows))
+        assert P >= (32 if len(sub.context_lens) == 4 else 18)
+        print(f"case pool shared prefix {io}/{kv} rows {list(rows)} P={P}", flush=True)
+        t = W.to_device(sub)
+        out = pkd.decode(t["q"], t["k_cache"], t["v_cache"], t["block_table"], t["context_lens"],
+                         float(sub.scale), k_scale=t["k_scale"], v_scale=t["v_scale"],
+                         partition_size=pkd.SPLIT_BALANCED, prefix_blocks=P)
+        torch.cuda.synchronize()
+        check(sub, to_f64(out), ref(sub), label=f"pool prefix {list(rows)}")
+    pool.close()

@@ -120,6 +120,16 @@ class Script:
             flat = [x for r in rows for x in r]
             self.want.append("T 0 " + " ".join(map(str, flat)) + " | " + " ".join(map(str, lens)))
 
+    def shared(self, sids):
+        """The shared prefix of sids, expected from the oracle's pool state
+        by the definition (tests/test_pool.py)."""
+        from tests.test_pool import expected_shared_prefix
+        self.ops.append(f"S {len(sids)} " + " ".join(map(str, sids)))
+        if all(sid in self.ref.seqs for sid in sids):
+            self.want.append(f"S 0 {expected_shared_prefix(self.ref, list(sids))}")
+        else:
+            self.want.append(("err", "S", PA_ERR_STATE))
+
     def check(self, exe):
         out = run(exe, "pool", stdin="\n".join(self.ops + ["D"]) + "\n").splitlines()
         assert len(out) == len(self.want) + 1 and out[-1] == "D", out[-3:]
@@ -179,6 +189,8 @@ def test_pool_random_operation_sequences(exe, seed):
                 live.remove(sid)
         if i % 50 == 0:
             s.snapshot()
+        if i % 25 == 0 and live:
+            s.shared(rnd.sample(live, rnd.randint(1, len(live))) + ([10 ** 6] if i % 100 == 0 else []))
     for sid in list(live):
         assert s.free(sid)
     s.snapshot()
@@ -195,5 +207,7 @@ def test_pool_long_shared_prefix(exe):
     for _ in range(20):
         for q in range(8):
             assert s.append(q, int(rng.integers(0, 32000)))
+    s.shared(list(range(8)))
+    s.shared([100, 3, 5])
     s.snapshot()
     s.check(exe)

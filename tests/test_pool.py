@@ -62,6 +62,29 @@ class Pair:
         table, got_lens = self.nat.block_table(sids, self.mbs, -1)
         assert table.tolist() == rows
         assert got_lens.tolist() == lens
+        # the shared prefix of the whole set and of a few subsets
+        rnd = random.Random(len(sids) * 31 + int(self.nat.num_free()))
+        subsets = [sids] + [rnd.sample(sids, rnd.randint(1, len(sids))) for _ in range(3)]
+        for sub in subsets:
+            assert self.nat.shared_prefix(sub) == expected_shared_prefix(self.ref, sub), sub
+
+
+def expected_shared_prefix(ref, sids):
+    """The definition, tried for every P from the largest down: each
+    sequence holds the longest one's blocks at each of its own full blocks
+    below P (the longest: the first among equals in `sids`)."""
+    if not sids:
+        return 0
+    longest = sids[0]
+    for sid in sids:
+        if len(ref.seqs[sid]["tokens"]) > len(ref.seqs[longest]["tokens"]):
+            longest = sid
+    top = ref.seqs[longest]
+    for P in range(len(top["tokens"]) // 16, -1, -1):
+        if all(ref.seqs[sid]["blocks"][j] == top["blocks"][j]
+               for sid in sids for j in range(min(P, len(ref.seqs[sid]["tokens"]) // 16))):
+            return P
+    return 0
 
 
 def test_hand_worked_scenario_matches():
@@ -122,6 +145,27 @@ def test_error_statuses_and_nothing_written():
             p.append_token(5, tok)
     assert e.value.status == _lib.PA_ERR_CAPACITY
     assert p.block_table([5], 4)[1].tolist() == [48]           # 34 + 14 accepted
+
+
+def test_shared_prefix_of_requests_behind_common_prompts():
+    pool = pkd.BlockPool(200, 3)
+    base = list(range(100, 164))                     # 64 tokens: 4 full blocks
+    pool.add_sequence(0, base + [1, 2, 3])           # 4 full blocks + 3 tokens
+    pool.add_sequence(1, base + [7] * 20)            # shares 4 blocks, 5 full
+    pool.add_sequence(2, base[:40])                  # shares 2 full blocks, private partial third
+    pool.add_sequence(3, list(range(500, 540)))      # nothing shared
+    pool.add_sequence(4, base[:48] + [9] * 30)       # shares 3 blocks, its 4th full block differs
+    # the longest (1) has 5 full blocks; 0 uses 4 of them, all shared
+    assert pool.shared_prefix([0, 1]) == 5
+    assert pool.shared_prefix([0, 1, 2]) == 5        # 2 agrees on its 2 full blocks
+    assert pool.shared_prefix([2]) == 2
+    assert pool.shared_prefix([0, 1, 4]) == 3        # 4 differs at its block 3
+    assert pool.shared_prefix([0, 1, 3]) == 0
+    assert pool.shared_prefix([]) == 0
+    with pytest.raises(pkd.PaError) as e:
+        pool.shared_prefix([0, 99])
+    assert e.value.status == _lib.PA_ERR_STATE
+    pool.close()
 
 
 def test_null_and_shape_arguments():
