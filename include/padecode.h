@@ -175,7 +175,11 @@ pa_status pa_decode(const pa_shape* shape, const void* q, const void* k_cache,
  * pa_decode's up to float rounding. The declaration is checked as the pages
  * are read: a sequence whose row differs from the row the prefix is read
  * from (a longest sequence) at some j < P_b, or whose prefix holds a block
- * id outside the pool, gets NaN outputs.
+ * id outside the pool, gets NaN outputs. A short prefix saves little: the
+ * call then takes about as long as pa_decode's balanced split or a little
+ * longer (every piece of a pair goes through the workspace to be merged
+ * with the prefix's), so it pays when the prefix is a good part of the
+ * batch's pages.
  * workspace: at least pa_decode_prefix_workspace_bytes(shape) bytes, 256-byte
  * aligned, with the same counter region (4 * batch * num_kv_heads bytes
  * first) and reset rule as pa_decode's balanced split; its partial slots are

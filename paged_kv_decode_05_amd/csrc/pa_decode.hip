@@ -866,11 +866,12 @@ struct ShareOf {
 // One wave's quarter [y0, y1) of share sh.
 // PFX: the line holds the pairs' suffixes (len: suffix length, -1 for an
 // out-of-contract sequence), whose pages start at page (full - len) / 16 of
-// the sequence; every piece goes through a workspace slot, since the pair's
-// prefix pieces are merged with it.
+// the sequence, pfx_pages the prefix pages read once; with a prefix every
+// piece goes through a workspace slot, since the pair's prefix pieces are
+// merged with it.
 template <typename IO, typename KV, int D, bool MQ, bool PFX>
 __device__ __forceinline__ void decode_quarter(const Params& a, const BalSm<D>& sm, const ShareOf& sh,
-                                               const int y0, const int y1, const PfxGeo& pg) {
+                                               const int y0, const int y1, const int pfx_pages) {
   using T = typename TileOf<IO, KV, D>::type;
   constexpr bool kFp8 = std::is_same<KV, FP8>::value;
   constexpr size_t kPageBytes = (size_t)kBlock * D * ElemSize<KV>::v;
@@ -882,7 +883,7 @@ __device__ __forceinline__ void decode_quarter(const Params& a, const BalSm<D>& 
   const int rr = lane & 15, jj = lane >> 4;
   const bool head_ok = rr < G;
   const int n = y1 - y0;
-  const int P = PFX ? pg.P : 0;
+  const int P = PFX ? pfx_pages : 0;
   if constexpr (PFX)
     if (n <= 0) return;   // a short suffix line leaves some quarters empty
 
@@ -1083,11 +1084,8 @@ __device__ __forceinline__ void decode_quarter(const Params& a, const BalSm<D>& 
       const int slot = cur.pair_first <= y0 ? 0 : 1;
       const int s_first = share_of(cur.pair_first, sh.n, sh.s);
       const int s_last = share_of(cur.pair_end - 1, sh.n, sh.s);
-      int parts = s_last - s_first + 1, slot0 = s_first + cur.b * H + cur.g;
-      if constexpr (PFX) {
-        parts += pfx_pieces(pg, pfx_unit(pg, cur.b, cur.g));
-        slot0 = s_first + (cur.b * H + cur.g) * (1 + kPfxPieces);
-      }
+      // (PFX: the workgroup adds the pair's prefix pieces and its slot stride)
+      const int parts = s_last - s_first + 1, slot0 = s_first + cur.b * H + cur.g;
       if (lane == 0) {
         int* e = sm.pm + (w * 2 + slot) * kPieceMeta;
         e[kPmB] = cur.b;
@@ -1796,7 +1794,7 @@ pa_decode_balanced_kernel(const Params a) {
   // this wave's quarter of the share
   const int wu = __builtin_amdgcn_readfirstlane(w);
   auto yq = [&](int ww) { return x0 + share_start(ww, x1 - x0, kWaves); };
-  decode_quarter<IO, KV, D, MQ, PFX>(a, sm, ShareOf{wg, N, S}, yq(wu), yq(wu + 1), pg);
+  decode_quarter<IO, KV, D, MQ, PFX>(a, sm, ShareOf{wg, N, S}, yq(wu), yq(wu + 1), pg.P);
   __syncthreads();
 
   // Pieces of the share whose state went through LDS, in three steps:
@@ -1813,8 +1811,14 @@ pa_decode_balanced_kernel(const Params a) {
   const int cl = lane < 2 * kWaves ? lane : 0;
   const int* rec = sm.pm + cl * kPieceMeta;
   const int fl = rec[kPmFlags];
-  const int parts = rec[kPmParts];
-  const int rb = rec[kPmB], rg = rec[kPmG], rs0 = rec[kPmSlot0];
+  int parts = rec[kPmParts];
+  const int rb = rec[kPmB], rg = rec[kPmG];
+  int rs0 = rec[kPmSlot0];
+  if constexpr (PFX) {
+    // the pair's prefix pieces follow its own, in slots of stride 1 + kPfxPieces
+    parts += pfx_pieces(pg, pfx_unit(pg, rb, rg));
+    rs0 += (rb * H + rg) * kPfxPieces;
+  }
   const uint32_t lead = (uint32_t)__ballot(lane < 2 * kWaves && (fl & kPmLead)) & 0xffu;
   const uint32_t split = (uint32_t)__ballot(lane < 2 * kWaves && (fl & kPmLead) && parts > 1) & 0xffu;
   if (!PFX && lead == 0) return;   // uniform

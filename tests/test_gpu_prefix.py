@@ -206,3 +206,23 @@ def test_stale_counter_gives_nan_rows_until_reset():
         assert np.abs(out[0] - exp[0]).max() <= 1e-2 and np.abs(out[2] - exp[2]).max() <= 1e-2
     pkd.reset_workspace(ws)
     check(wl, to_f64(run_prefix(wl, 64, t=t, workspace=ws)), exp, label="prefix stale after reset")
+
+
+def test_short_prefix_against_the_balanced_split_and_still_checked():
+    # 8 shared pages of sequences 2000-4000 tokens long: little is saved,
+    # the result is the plain balanced split's up to rounding, and the
+    # declaration is still checked (a broken row: NaN for that sequence)
+    sp = spec("p_small", 6, 32, 8, 128, "bf16", "bf16", ("uniform", 2000, 4000), 256, 25)
+    wl = W.make_workload(sp)
+    t = to_device(wl)
+    a = to_f64(run_prefix(wl, 8, t=t))
+    b = to_f64(run(wl, t, partition_size=BAL))
+    assert np.abs(a - b).max() <= 2.5e-2
+    exp = ref(wl)
+    check(wl, a, exp, label="short prefix")
+    # row 4 (not the longest, 2, whose ids are read) breaks it
+    assert int(np.argmax(wl.context_lens)) == 2
+    wl.block_table[4, 3] = wl.block_table[0, 40]
+    got = to_f64(run_prefix(wl, 8))
+    assert np.isnan(got[4]).all()
+    check(wl, got, exp, seqs=[0, 1, 2, 3, 5], label="short prefix, declaration broken")
