@@ -739,6 +739,7 @@ def config_record(args, torch, np, pkd, W, k):
     wl = bench.wl
     logical, unique = wl.kv_bytes_logical(), wl.kv_bytes_unique()
     mx, mean = oracle_errors(wl, out, ORACLE_SAMPLE[k])
+    floor = None if args.no_stream_ceiling else bench.page_read_floor()
     rec = {
         "workload": shape_name(spec), "spec_partition_size": spec.partition_size,
         "mode": mode_name(best), "us_per_call": round(ms * 1e3, 3),
@@ -751,6 +752,10 @@ def config_record(args, torch, np, pkd, W, k):
         "max_abs_vs_oracle": mx, "mean_abs_vs_oracle": mean,
         "oracle_sequences": "all" if ORACLE_SAMPLE[k] is None else ORACLE_SAMPLE[k],
         "modes_us": {mode_name(m): round(v[0] * 1e3, 3) for m, v in timed.items()},
+        # a kernel that reads exactly the call's pages (every sequence's, in
+        # pair order) and nothing else: logical KV bytes per second
+        "page_read_floor_GBps": None if floor is None else round(floor, 1),
+        "pct_page_read_floor": None if floor is None else round(100.0 * logical / (ms / 1e3) / 1e9 / floor, 2),
     }
     del bench
     torch.cuda.empty_cache()
