@@ -226,3 +226,49 @@ def test_short_prefix_against_the_balanced_split_and_still_checked():
     got = to_f64(run_prefix(wl, 8))
     assert np.isnan(got[4]).all()
     check(wl, got, exp, seqs=[0, 1, 2, 3, 5], label="short prefix, declaration broken")
+
+
+def random_prefix_config(seed):
+    """A seeded shared-prefix configuration: any dtype pair and head_dim,
+    1-8 KV heads, groups of 1-16, batches of 1-40, a shared prefix of 0-40
+    blocks, sequences shorter than it (ending inside it or on its last page),
+    empty, a whole table, and a declared prefix at, below or above the
+    shared one (but never declaring more than the rows share)."""
+    rng = np.random.default_rng(9100 + seed)
+    DT = [("f32", "f32"), ("f16", "f16"), ("bf16", "bf16"), ("f16", "fp8_e4m3"), ("bf16", "fp8_e4m3")]
+    io, kv = DT[int(rng.integers(len(DT)))]
+    D = int(rng.choice([64, 128]))
+    hkv = int(rng.choice([1, 2, 4, 8]))
+    G = int(rng.integers(1, 17))
+    B = int(rng.integers(1, 41))
+    shared = int(rng.integers(0, 41))
+    mbs = shared + int(rng.integers(1, 60))
+    top = mbs * 16
+    lens = []
+    for kind in rng.integers(0, 6, size=B):
+        lens.append([0, 16 * shared + int(rng.integers(1, 17)), top, int(rng.integers(1, top + 1)),
+                     int(rng.integers(1, 16 * shared + 2)), 16 * int(rng.integers(1, mbs + 1))][int(kind)])
+    declared = int(rng.integers(0, shared + 1)) if shared else 0
+    sp = W.Spec(f"prand{seed}_{io}_{kv}_d{D}_h{G * hkv}kv{hkv}_b{B}_shared{shared}_P{declared}", B, G * hkv,
+                hkv, D, io, kv, ("fixed", lens), mbs, ("ratio", 1.3), BAL, 16 * shared, 9100 + seed)
+    return sp, declared
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_random_shared_prefix_configuration(seed):
+    sp, P = random_prefix_config(seed)
+    print(f"case {sp.name} lens={sp.lens[1]}", flush=True)
+    wl = W.make_workload(sp)
+    out, lse = run_prefix(wl, P, lse=True)
+    exp_out, exp_lse = ref(wl, lse=True)
+    got = to_f64(out)
+    live = [b for b in range(sp.batch) if wl.context_lens[b] > 0]
+    for b in range(sp.batch):
+        if wl.context_lens[b] == 0:
+            assert np.array_equal(got[b], np.zeros_like(got[b])), sp.name
+    if live:
+        check(wl, got, exp_out, seqs=live, label=sp.name)
+        l = lse.cpu().double().numpy()
+        assert np.array_equal(np.isneginf(l), np.isneginf(exp_lse)), sp.name
+        fin = np.isfinite(exp_lse)
+        assert np.abs(l[fin] - exp_lse[fin]).max() <= 5e-3, sp.name
