@@ -393,15 +393,32 @@ pa_multi_kernel(const Params a) {
 
   // The chunk's query operand into LDS. Rows past R repeat row R-1: their
   // columns hold finite duplicates that are never stored.
-  for (int i = tid; i < NT * KQ * 64; i += kThreads) {
-    const int j = i / (KQ * 64);
-    const int rem = i - j * (KQ * 64);
-    const int cc = rem >> 6, ln = rem & 63;
-    const int rho = min(row0 + 16 * j + (ln & 15), R - 1);
-    const int t = rho / G, h = rho - t * G;
-    const uint8_t* qrow =
-        a.q + (((size_t)b * TQ + t) * a.num_q_heads + (size_t)g * G + h) * D * ElemSize<IO>::v;
-    sm.q[j][cc][ln] = __builtin_bit_cast(QC, *reinterpret_cast<const u32x4*>(qrow + T::qoff(cc, ln >> 4)));
+  // (every load of the thread issued before its first LDS write)
+  constexpr int kQItems = NT * KQ * 64;
+  constexpr int kQPer = (kQItems + kThreads - 1) / kThreads;
+  u32x4 qv[kQPer];
+#pragma unroll
+  for (int u = 0; u < kQPer; ++u) {
+    const int i = u * kThreads + tid;
+    if (i < kQItems) {
+      const int j = i / (KQ * 64);
+      const int rem = i - j * (KQ * 64);
+      const int cc = rem >> 6, ln = rem & 63;
+      const int rho = min(row0 + 16 * j + (ln & 15), R - 1);
+      const int t = rho / G, h = rho - t * G;
+      const uint8_t* qrow =
+          a.q + (((size_t)b * TQ + t) * a.num_q_heads + (size_t)g * G + h) * D * ElemSize<IO>::v;
+      qv[u] = *reinterpret_cast<const u32x4*>(qrow + T::qoff(cc, ln >> 4));
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < kQPer; ++u) {
+    const int i = u * kThreads + tid;
+    if (i < kQItems) {
+      const int j = i / (KQ * 64);
+      const int rem = i - j * (KQ * 64);
+      sm.q[j][rem >> 6][rem & 63] = __builtin_bit_cast(QC, qv[u]);
+    }
   }
 
   const int L = a.context_lens[b];
@@ -730,15 +747,26 @@ __global__ void __launch_bounds__(kThreads) pa_multi_bal_kernel(const Params a) 
         const int bt0 = fetch_ids(a, b, pg_lo + wi, WC, 0);
         if (cp > 0) lds_barrier();   // the previous pass's LDS readers are done
         // the pass's query operands into LDS; rows past R repeat row R-1
-        // (finite duplicates, never stored)
-        for (int i = tid; i < NCG * NT * KQ * 64; i += kThreads) {
-          const int tj = i / (KQ * 64);
-          const int rem = i - tj * (KQ * 64);
-          const int cc = rem >> 6, ln = rem & 63;
-          const int rho = min(16 * (cp * NCG * NT + tj) + (ln & 15), R - 1);
-          const uint8_t* qrow = a.q + row_of(b, g, rho) * D * ElemSize<IO>::v;
-          qsm[i] = __builtin_bit_cast(QC, *reinterpret_cast<const u32x4*>(qrow + T::qoff(cc, ln >> 4)));
+        // (finite duplicates, never stored). Every load of the thread is
+        // issued before its first LDS write: one memory round trip.
+        constexpr int kQItems = NCG * NT * KQ * 64;
+        constexpr int kQPer = (kQItems + kThreads - 1) / kThreads;
+        u32x4 qv[kQPer];
+#pragma unroll
+        for (int u = 0; u < kQPer; ++u) {
+          const int i = u * kThreads + tid;
+          if (i < kQItems) {
+            const int tj = i / (KQ * 64);
+            const int rem = i - tj * (KQ * 64);
+            const int cc = rem >> 6, ln = rem & 63;
+            const int rho = min(16 * (cp * NCG * NT + tj) + (ln & 15), R - 1);
+            const uint8_t* qrow = a.q + row_of(b, g, rho) * D * ElemSize<IO>::v;
+            qv[u] = *reinterpret_cast<const u32x4*>(qrow + T::qoff(cc, ln >> 4));
+          }
         }
+#pragma unroll
+        for (int u = 0; u < kQPer; ++u)
+          if (u * kThreads + tid < kQItems) qsm[u * kThreads + tid] = __builtin_bit_cast(QC, qv[u]);
         if (tid < kWaves) badw[tid] = 0;
         lds_barrier();
         int lim[NT];
