@@ -272,3 +272,15 @@ def test_random_shared_prefix_configuration(seed):
         assert np.array_equal(np.isneginf(l), np.isneginf(exp_lse)), sp.name
         fin = np.isfinite(exp_lse)
         assert np.abs(l[fin] - exp_lse[fin]).max() <= 5e-3, sp.name
+
+
+def test_largest_batch_under_a_shared_prefix():
+    # 4096 sequences of 1-200 tokens behind a 64-token prefix, 2 query heads
+    # per KV head: 8 sequences per tile, 512 tiles, 128 passes per KV head;
+    # the lengths scan covers the whole batch in LDS beside the prefix state
+    sp = spec("p_b4096", 4096, 4, 2, 128, "bf16", "bf16", ("uniform", 1, 200), 64, 26)
+    print(f"case {sp.name}", flush=True)
+    wl = W.make_workload(sp)
+    out = to_f64(run_prefix(wl, 4))
+    exp = ref(wl)
+    check(wl, out, exp, label="prefix largest batch")
