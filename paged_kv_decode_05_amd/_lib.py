@@ -305,6 +305,9 @@ def prepare(q, k_cache, v_cache, block_table, context_lens, scale, *, k_scale=No
     """
     import torch
     lib = load_library()
+    if prefix_blocks is not None and not -2**31 <= int(prefix_blocks) < 2**31:
+        # ctypes would wrap it into a 32-bit value the library might accept
+        raise PaError(2, "prefix_blocks is outside the 32-bit range")
     io = _torch_dtype_name(q)
     kv = _torch_dtype_name(k_cache)
     if io is None or kv is None or _torch_dtype_name(v_cache) != kv:

@@ -416,3 +416,17 @@ def test_buffer_checks_reject_misfit_buffers(what, status):
     with pytest.raises(_lib.PaError) as e:
         _lib.check_buffers(q, inp, on_device=on_device, fp8=fp8, **kw)
     assert e.value.status == status, (what, str(e.value))
+
+
+@pytest.mark.parametrize("pb", [2**31, 2**32 + 5, -2**31 - 1])
+def test_shared_prefix_count_outside_32_bits_is_refused_by_the_binding(pb):
+    # the C ABI takes an int32: a wider value must not wrap into a valid one
+    import torch
+    q = torch.zeros(2, 8, 128, dtype=torch.float16)
+    k = torch.zeros(4, 2, 16, 16, 8, dtype=torch.float16)
+    v = torch.zeros(4, 2, 128, 16, dtype=torch.float16)
+    bt = torch.zeros(2, 4, dtype=torch.int32)
+    cl = torch.ones(2, dtype=torch.int32)
+    with pytest.raises(_lib.PaError) as e:
+        _lib.prepare(q, k, v, bt, cl, 0.1, partition_size=_lib.SPLIT_BALANCED, prefix_blocks=pb)
+    assert e.value.status == 2 and "32-bit" in str(e.value)
