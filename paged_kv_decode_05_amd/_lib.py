@@ -31,6 +31,28 @@ class PaError(RuntimeError):
         self.status = status
 
 
+def _c_int(x, bits, what):
+    """x as an int that fits a signed `bits`-bit C argument (ctypes would
+    wrap a wider value into one the library might accept)."""
+    v = int(x)
+    if not -(1 << (bits - 1)) <= v < (1 << (bits - 1)):
+        raise PaError(2, f"{what} = {v} does not fit a {bits}-bit signed integer")
+    return v
+
+
+def _int32_array(x, what):
+    """A flat contiguous int32 copy of integer values x, refusing values a
+    cast to int32 would wrap."""
+    import numpy as np
+    a = np.asarray(x)
+    if a.size and a.dtype != np.int32:
+        if not np.issubdtype(a.dtype, np.integer):
+            raise PaError(3, f"{what} must be integers, got {a.dtype}")
+        if int(a.min()) < -2**31 or int(a.max()) >= 2**31:
+            raise PaError(2, f"{what} holds values outside int32")
+    return np.ascontiguousarray(a, dtype=np.int32).reshape(-1)
+
+
 class PaShape(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "batch", "num_q_heads", "num_kv_heads", "head_dim", "block_size",
@@ -305,9 +327,8 @@ def prepare(q, k_cache, v_cache, block_table, context_lens, scale, *, k_scale=No
     """
     import torch
     lib = load_library()
-    if prefix_blocks is not None and not -2**31 <= int(prefix_blocks) < 2**31:
-        # ctypes would wrap it into a 32-bit value the library might accept
-        raise PaError(2, "prefix_blocks is outside the 32-bit range")
+    if prefix_blocks is not None:
+        prefix_blocks = _c_int(prefix_blocks, 32, "prefix_blocks")
     io = _torch_dtype_name(q)
     kv = _torch_dtype_name(k_cache)
     if io is None or kv is None or _torch_dtype_name(v_cache) != kv:
@@ -352,7 +373,7 @@ def prepare(q, k_cache, v_cache, block_table, context_lens, scale, *, k_scale=No
     if multi:
         fn, args = lib.pa_decode_multi, (ctypes.byref(shape), q.shape[1]) + tail
     elif prefix_blocks is not None:
-        fn, args = lib.pa_decode_prefix, (ctypes.byref(shape), int(prefix_blocks)) + tail
+        fn, args = lib.pa_decode_prefix, (ctypes.byref(shape), prefix_blocks) + tail
     else:
         fn, args = lib.pa_decode, (ctypes.byref(shape),) + tail
     keep = (shape, q, k_cache, v_cache, block_table, context_lens, k_scale, v_scale,
@@ -479,7 +500,7 @@ class BlockPool:
     def __init__(self, num_blocks, seed=0):
         self._lib = load_library()
         h = ctypes.c_void_p()
-        _check(self._lib.pa_pool_create(int(num_blocks), int(seed) & (2**64 - 1),
+        _check(self._lib.pa_pool_create(_c_int(num_blocks, 32, "num_blocks"), int(seed) & (2**64 - 1),
                                         ctypes.byref(h)))
         self._h = h
 
@@ -497,17 +518,18 @@ class BlockPool:
     def add_sequence(self, seq_id, tokens):
         """Register a sequence's prompt; returns the leading tokens found cached."""
         import numpy as np
-        t = np.ascontiguousarray(tokens, dtype=np.int32).reshape(-1)
+        t = _int32_array(tokens, "tokens")
         got = ctypes.c_int32(0)
-        _check(self._lib.pa_pool_add_sequence(self._h, int(seq_id), t.ctypes.data, t.size,
+        _check(self._lib.pa_pool_add_sequence(self._h, _c_int(seq_id, 64, "seq_id"), t.ctypes.data,
+                                              _c_int(t.size, 32, "the token count"),
                                               ctypes.byref(got)))
         return got.value
 
     def append_token(self, seq_id, token):
-        _check(self._lib.pa_pool_append_token(self._h, int(seq_id), int(token)))
+        _check(self._lib.pa_pool_append_token(self._h, _c_int(seq_id, 64, "seq_id"), _c_int(token, 32, "token")))
 
     def free_sequence(self, seq_id):
-        _check(self._lib.pa_pool_free_sequence(self._h, int(seq_id)))
+        _check(self._lib.pa_pool_free_sequence(self._h, _c_int(seq_id, 64, "seq_id")))
 
     def num_free(self):
         return self._lib.pa_pool_num_free(self._h)
@@ -526,8 +548,11 @@ class BlockPool:
         """-> (int32 [len(seq_ids), max_blocks] block table, int32 context lengths)."""
         import numpy as np
         ids = np.ascontiguousarray(seq_ids, dtype=np.int64).reshape(-1)
-        table = np.empty((ids.size, int(max_blocks)), dtype=np.int32)
+        mb = _c_int(max_blocks, 32, "max_blocks")
+        if mb < 0:
+            raise PaError(2, f"max_blocks = {mb} is negative")
+        table = np.empty((ids.size, mb), dtype=np.int32)
         lens = np.empty(ids.size, dtype=np.int32)
-        _check(self._lib.pa_pool_block_table(self._h, ids.ctypes.data, ids.size, int(max_blocks),
-                                             int(pad), table.ctypes.data, lens.ctypes.data))
+        _check(self._lib.pa_pool_block_table(self._h, ids.ctypes.data, _c_int(ids.size, 32, "the sequence count"),
+                                             mb, _c_int(pad, 32, "pad"), table.ctypes.data, lens.ctypes.data))
         return table, lens

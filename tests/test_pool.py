@@ -238,3 +238,43 @@ def test_large_shared_prefix_pool_matches_the_oracle():
         for s in range(8):
             assert p.append(s, int(rng.integers(0, 32000)))
     p.compare()
+
+
+@pytest.mark.parametrize("call", [
+    "create_blocks", "seq_id_add", "seq_id_append", "seq_id_free", "token", "token_array",
+    "token_float", "max_blocks", "max_blocks_negative", "pad"])
+def test_scalars_outside_the_c_types_are_refused_not_wrapped(call):
+    # ctypes and numpy casts wrap silently; the binding refuses instead, and
+    # the pool is left as it was
+    status = 3 if call == "token_float" else 2
+    pool = pkd.BlockPool(8)
+    try:
+        assert pool.add_sequence(1, list(range(20))) == 0
+        before = pool.num_free()
+        with pytest.raises(_lib.PaError) as e:
+            if call == "create_blocks":
+                pkd.BlockPool(2**32 + 4)
+            elif call == "seq_id_add":
+                pool.add_sequence(2**63, [1, 2, 3])
+            elif call == "seq_id_append":
+                pool.append_token(-2**63 - 1, 7)
+            elif call == "seq_id_free":
+                pool.free_sequence(2**64 + 1)
+            elif call == "token":
+                pool.append_token(1, 2**31)
+            elif call == "token_array":
+                pool.add_sequence(2, np.array([1, 2**32 + 1], dtype=np.int64))
+            elif call == "token_float":
+                pool.add_sequence(2, np.array([1.5, 2.0]))
+            elif call == "max_blocks":
+                pool.block_table([1], 2**32 + 2)
+            elif call == "max_blocks_negative":
+                pool.block_table([1], -1)
+            elif call == "pad":
+                pool.block_table([1], 4, pad=2**31)
+        assert e.value.status == status, str(e.value)
+        assert pool.num_free() == before
+        table, lens = pool.block_table([1], 4)
+        assert lens.tolist() == [20]
+    finally:
+        pool.close()
