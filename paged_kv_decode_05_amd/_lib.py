@@ -147,9 +147,11 @@ def _torch_dtype_name(t):
 
 def make_shape(q, k_cache, block_table, partition_size):
     B, Hq, D = q.shape[0], q.shape[-2], q.shape[-1]
-    return PaShape(batch=B, num_q_heads=Hq, num_kv_heads=k_cache.shape[1], head_dim=D,
-                   block_size=k_cache.shape[3], max_blocks_per_seq=block_table.shape[1],
-                   num_blocks=k_cache.shape[0], partition_size=partition_size)
+    dims = dict(batch=B, num_q_heads=Hq, num_kv_heads=k_cache.shape[1], head_dim=D,
+                block_size=k_cache.shape[3], max_blocks_per_seq=block_table.shape[1],
+                num_blocks=k_cache.shape[0], partition_size=partition_size)
+    # the fields are int32: a wider value would wrap into one the library accepts
+    return PaShape(**{k: _c_int(v, 32, k) for k, v in dims.items()})
 
 
 def workspace_bytes(q, k_cache, block_table, partition_size):

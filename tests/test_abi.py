@@ -430,3 +430,15 @@ def test_shared_prefix_count_outside_32_bits_is_refused_by_the_binding(pb):
     with pytest.raises(_lib.PaError) as e:
         _lib.prepare(q, k, v, bt, cl, 0.1, partition_size=_lib.SPLIT_BALANCED, prefix_blocks=pb)
     assert e.value.status == 2 and "32-bit" in str(e.value)
+
+
+def test_partition_size_outside_32_bits_is_refused_not_wrapped():
+    # 2**32 + 512 would wrap to a valid 512-token split in the int32 field
+    import torch
+    q = torch.zeros(2, 8, 128, dtype=torch.float16)
+    k = torch.zeros(4, 2, 16, 16, 8, dtype=torch.float16)
+    bt = torch.zeros(2, 4, dtype=torch.int32)
+    with pytest.raises(_lib.PaError) as e:
+        _lib.make_shape(q, k, bt, 2**32 + 512)
+    assert e.value.status == 2 and "partition_size" in str(e.value)
+    assert _lib.make_shape(q, k, bt, 512).partition_size == 512
