@@ -122,12 +122,19 @@ struct MergeJob {
   long long dst;
 };
 
-constexpr int kMergeBatch = 8;                 // piece loads in flight per item
 constexpr int kMergeScratch = 12 * kThreads;   // floats: slice results of 2 * kThreads items
+
+// Piece loads in flight per merge item (MB below): 8, or 4 for an fp8 cache,
+// whose balanced kernel holds the widened operands beside the merge state
+// and spilled registers at 256 per lane with 8.
+template <typename KV>
+constexpr int merge_batch() {
+  return std::is_same<KV, FP8>::value ? 4 : 8;
+}
 
 // Run m merges (job j = jobs(j), all with a.group rows per pair). Threads take
 // (job, slice, row, 4-float quad) items two at a time and issue the loads of
-// up to kMergeBatch pieces of both before folding either, so two jobs, or the
+// up to MB pieces of both before folding either, so two jobs, or the
 // two halves of a job with more items than threads, cost one memory round
 // trip rather than two. A job's items fill whole waves (its item count
 // rounded up to 64), so the job, and with it the base of the buffer resource
@@ -142,10 +149,11 @@ constexpr int kMergeScratch = 12 * kThreads;   // floats: slice results of 2 * k
 // -inf) adds nothing, a row with nothing in any piece gets out = 0 and lse =
 // -inf, and a NaN piece makes the row NaN. red: LDS scratch of kMergeScratch
 // floats. Control flow is uniform across the workgroup.
-// Slices for a job of np pieces alone in a pass (its items in one round).
-__device__ __forceinline__ int merge_slices(int np, int npad, int* shift) {
+// Slices for a job of np pieces alone in a pass (its items in one round),
+// mb pieces a batch.
+__device__ __forceinline__ int merge_slices(int np, int npad, int mb, int* shift) {
   int S = 1, sh = 0;
-  while (S < 8 && S * kMergeBatch < np && 2 * S * npad <= 2 * kThreads) {
+  while (S < 8 && S * mb < np && 2 * S * npad <= 2 * kThreads) {
     S *= 2;
     ++sh;
   }
@@ -153,7 +161,7 @@ __device__ __forceinline__ int merge_slices(int np, int npad, int* shift) {
   return S;
 }
 
-template <typename IO, int D, typename Jobs>
+template <typename IO, int D, int MB, typename Jobs>
 __device__ __forceinline__ void merge_pass(const Params& a, float* red, int m, int S, int sshift, Jobs jobs) {
   constexpr int kQuads = D / 4;
   const int tid = threadIdx.x;
@@ -196,13 +204,13 @@ __device__ __forceinline__ void merge_pass(const Params& a, float* red, int m, i
       ar[u] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
     const int nmax = max(cnt[0], cnt[1]);
-    for (int i0 = 0; i0 < nmax; i0 += kMergeBatch) {
-      float lp[2][kMergeBatch];
-      f32x4 ov[2][kMergeBatch];
+    for (int i0 = 0; i0 < nmax; i0 += MB) {
+      float lp[2][MB];
+      f32x4 ov[2][MB];
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         if (i0 < cnt[u]) {   // uniform
-          const int nb = min(kMergeBatch, cnt[u] - i0);
+          const int nb = min(MB, cnt[u] - i0);
           const size_t s0 = J[u].slot0 + sl[u] + (size_t)S * i0;   // first slot of the batch
           const uint32_t nslots = (uint32_t)((nb - 1) * S + 1);
           const brsrc ro = buffer_rsrc(a.ws_o + s0 * slot_floats, (uint32_t)(nslots * slot_floats * sizeof(float)));
@@ -210,7 +218,7 @@ __device__ __forceinline__ void merge_pass(const Params& a, float* red, int m, i
           const uint32_t vo = (uint32_t)((h[u] * D + 4 * dq[u]) * sizeof(float));
           const uint32_t vl = (uint32_t)(h[u] * sizeof(float));
 #pragma unroll
-          for (int q = 0; q < kMergeBatch; ++q) {
+          for (int q = 0; q < MB; ++q) {
             if (on[u] && q < nb) {
               lp[u][q] = ld_agent1(rl, vl, (uint32_t)(q * S * a.group * sizeof(float)));
               ov[u][q] = ld_agent4(ro, vo, (uint32_t)(q * S * slot_floats * sizeof(float)));
@@ -221,7 +229,7 @@ __device__ __forceinline__ void merge_pass(const Params& a, float* red, int m, i
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
 #pragma unroll
-        for (int q = 0; q < kMergeBatch; ++q) {
+        for (int q = 0; q < MB; ++q) {
           if (on[u] && i0 + q < cnt[u]) {
             const float l = lp[u][q];
             if (l != l) {
@@ -301,28 +309,28 @@ __device__ __forceinline__ void merge_pass(const Params& a, float* red, int m, i
   }
 }
 
-// Run m merges: jobs of at most kMergeBatch pieces all in one pass (one slice
-// each); otherwise every job in a pass of its own, with its own slice count.
-template <typename IO, int D, typename Jobs>
+// Run m merges: jobs of at most MB pieces all in one pass (one slice each);
+// otherwise every job in a pass of its own, with its own slice count.
+template <typename IO, int D, int MB, typename Jobs>
 __device__ __forceinline__ void merge_jobs(const Params& a, float* red, int m, int np_max, Jobs jobs) {
-  if (np_max <= kMergeBatch) {
-    merge_pass<IO, D>(a, red, m, 1, 0, jobs);
+  if (np_max <= MB) {
+    merge_pass<IO, D, MB>(a, red, m, 1, 0, jobs);
     return;
   }
   const int npad = (a.group * (D / 4) + 63) & ~63;
   for (int j = 0; j < m; ++j) {
     const MergeJob J = jobs(j);
     int sh;
-    const int S = merge_slices(J.np, npad, &sh);
+    const int S = merge_slices(J.np, npad, MB, &sh);
     if (j > 0) __syncthreads();   // the previous pass's slice results in LDS are consumed
-    merge_pass<IO, D>(a, red, 1, S, sh, [&](int) { return J; });
+    merge_pass<IO, D, MB>(a, red, 1, S, sh, [&](int) { return J; });
   }
 }
 
 // The single merge of one pair.
-template <typename IO, int D>
+template <typename IO, int D, int MB>
 __device__ __forceinline__ void merge_one(const Params& a, float* red, const MergeJob& job) {
-  merge_jobs<IO, D>(a, red, 1, job.np, [&](int) { return job; });
+  merge_jobs<IO, D, MB>(a, red, 1, job.np, [&](int) { return job; });
 }
 
 // Every output row of pair (b, g) (and its lse) set to x by the workgroup.
@@ -644,14 +652,15 @@ __device__ __forceinline__ void decode_piece(const Params& a, Smem<D>& sm, const
       if (pc.k != gfirst) return;
       if (tid < G) st_agent(a.ws_lse + (first + grp) * G + tid, __builtin_nanf(""));
     } else {
-      merge_one<IO, D>(a, red, MergeJob{b, g, gn, (size_t)pc.slot0 + gfirst, (long long)(first + grp)});
+      merge_one<IO, D, merge_batch<KV>()>(a, red,
+                                          MergeJob{b, g, gn, (size_t)pc.slot0 + gfirst, (long long)(first + grp)});
     }
     np = (pc.nparts + a.fan - 1) / a.fan;
     reporter = grp == 0;
   }
   const int c2 = last_to_finish(a.ws_cnt + bg, np, &sm.last);
   if (c2 == kCountLast) {
-    merge_one<IO, D>(a, red, MergeJob{b, g, np, first, -1});
+    merge_one<IO, D, merge_batch<KV>()>(a, red, MergeJob{b, g, np, first, -1});
   } else if (c2 == kCountStale && reporter) {
     fill_rows<IO, D, MQ>(a, b, g, __builtin_nanf(""));
   }
@@ -1653,7 +1662,7 @@ __device__ __forceinline__ void prefix_share(const Params& a, const BalSm<D>& sm
         const PfxSlots ps = pfx_pair_slots(a, sm, pg, b_pass + __builtin_ctzll(mk), g, n_s, s_n);
         npm = max(npm, ps.own + pp);
       }
-      merge_jobs<IO, D>(a, sm.red, nm, npm, [&](int j) {
+      merge_jobs<IO, D, merge_batch<KV>()>(a, sm.red, nm, npm, [&](int j) {
         uint64_t mk = done;   // the j-th completed sequence
         for (int i = 0; i < j && i < nm - 1; ++i) mk &= mk - 1;
         const int b = b_pass + __builtin_ctzll(mk);
@@ -1867,7 +1876,7 @@ pa_decode_balanced_kernel(const Params a) {
     for (uint32_t mk = done; mk; mk &= mk - 1)
       npm = max(npm, __builtin_amdgcn_readlane(parts, __builtin_ctz(mk)));
     const int m = __builtin_popcount(done);
-    merge_jobs<IO, D>(a, sm.red, m, npm, [&](int j) {
+    merge_jobs<IO, D, merge_batch<KV>()>(a, sm.red, m, npm, [&](int j) {
       uint32_t mk = done;   // the j-th completed pair
       for (int i = 0; i < j && i < m - 1; ++i) mk &= mk - 1;
       const int c = __builtin_ctz(mk);
@@ -1983,7 +1992,7 @@ pa_decode_balanced_kernel(const Params a) {
         };
         int npm = 0;
         for (int j = 0; j < nm; ++j) npm = max(npm, job(j).np);
-        merge_jobs<IO, D>(a, sm.red, nm, npm, job);
+        merge_jobs<IO, D, merge_batch<KV>()>(a, sm.red, nm, npm, job);
       }
     }
   }

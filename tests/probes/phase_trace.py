@@ -65,10 +65,10 @@ def _patches():
         ("    lds_barrier();\n    const uint32_t stale = (uint32_t)__builtin_amdgcn_readfirstlane(sm.split[1]);\n",
          "    lds_barrier();\n    " + _stamp(5) +
          "\n    const uint32_t stale = (uint32_t)__builtin_amdgcn_readfirstlane(sm.split[1]);\n"),
-        ("    const int m = __builtin_popcount(done);\n    merge_jobs<IO, D>(a, sm.red, m, npm, [&](int j) {",
+        ("    const int m = __builtin_popcount(done);\n    merge_jobs<IO, D, merge_batch<KV>()>(a, sm.red, m, npm,",
          "    const int m = __builtin_popcount(done);\n"
          f"    if (a.trace && threadIdx.x == 0) a.trace[(size_t)blockIdx.x * {SLOTS} + 7] = m;\n"
-         "    merge_jobs<IO, D>(a, sm.red, m, npm, [&](int j) {"),
+         "    merge_jobs<IO, D, merge_batch<KV>()>(a, sm.red, m, npm,"),
         ("    combine_pieces<IO, KV, D, MQ, PFX>(a, sm, lead, facts);\n"
          "    if (split == 0) return;   // uniform\n"
          "    __builtin_amdgcn_s_waitcnt(0);   // this wave's partial stores are complete\n"
