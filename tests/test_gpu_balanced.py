@@ -203,3 +203,18 @@ def test_bit_identical_when_merging_workgroups_hold_several_pairs():
         again = run(wl, t, partition_size=BAL).cpu()
         assert torch.equal(first.view(torch.int16), again.view(torch.int16)), i
     check(wl, to_f64(first), ref(wl), label="bal determinism")
+
+
+def test_fp8_merges_of_more_pieces_than_one_batch_are_bit_identical():
+    # With an fp8 cache a merge takes four pieces per batch: pairs cut into
+    # about five to nine pieces here take two or more slices, combined in
+    # order through LDS, whichever workgroup finishes the pair
+    spec = W.small_variant(W.SPECS[4], 10, ("uniform", 1000, 3000))
+    wl = W.make_workload(spec, seed=43)
+    print(f"case fp8 slices {spec.name}", flush=True)
+    t = to_device(wl)
+    first = run(wl, t, partition_size=BAL).cpu()
+    for i in range(8):
+        again = run(wl, t, partition_size=BAL).cpu()
+        assert torch.equal(first.view(torch.int16), again.view(torch.int16)), i
+    check(wl, to_f64(first), ref(wl), label="bal fp8 slices")
