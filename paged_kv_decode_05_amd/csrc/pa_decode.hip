@@ -1214,10 +1214,12 @@ struct SlotFacts {
 // Combine, for every piece of the share that leads in LDS (candidate slots c
 // in the bit mask lead), the slots of the waves holding it, and write the
 // pair's output (a pair whose pieces are all in this share) or the piece's
-// partial result to its workspace slot. One piece at a time, uniform across
-// the workgroup; its G x D/4 (row, 4-float quad) items at most two per
-// thread (G <= 16), every LDS read of both issued before any arithmetic, so a
-// piece costs one LDS round trip.
+// partial result to its workspace slot. Uniform across the workgroup, a pass
+// at a time; a thread has two item slots: with G x D/4 (row, 4-float quad)
+// items of a piece at most the thread count (G <= 8 at head_dim 128) a pass
+// takes two pieces, one item of each per thread, else one piece, two items
+// per thread (G <= 16). Every LDS read of both slots is issued before any
+// arithmetic, so a pass costs one LDS round trip.
 template <typename IO, typename KV, int D, bool MQ, bool PFX>
 __device__ __forceinline__ void combine_pieces(const Params& a, const BalSm<D>& sm, uint32_t lead,
                                                const SlotFacts& f) {
@@ -1227,43 +1229,54 @@ __device__ __forceinline__ void combine_pieces(const Params& a, const BalSm<D>& 
   const int tid = threadIdx.x;
   const int G = a.group;
   const int items = G * kQuads;
-  for (uint32_t mk = lead; mk; mk &= mk - 1) {
-    const int c = __builtin_ctz(mk);   // uniform
-    const int wa = c >> 1, sa = c & 1;
-    const int b = __builtin_amdgcn_readlane(f.b, c);
-    const int g = __builtin_amdgcn_readlane(f.g, c);
-    const float vmul = __builtin_bit_cast(float, __builtin_amdgcn_readlane(f.vmul, c));
-    const int nparts = __builtin_amdgcn_readlane(f.parts, c);
-    const int wslot = __builtin_amdgcn_readlane(f.slot, c);
-    const int hold = __builtin_amdgcn_readlane(f.hold, c);
+  const bool two_pieces = items <= kThreads;   // uniform
+  for (uint32_t mk = lead; mk;) {
+    // the pass's pieces (candidate slots, uniform): cs[1] == cs[0] when the
+    // pass takes one
+    int cs[2];
+    cs[0] = __builtin_ctz(mk);
+    mk &= mk - 1;
+    cs[1] = cs[0];
+    bool second = false;
+    if (two_pieces && mk) {
+      cs[1] = __builtin_ctz(mk);
+      mk &= mk - 1;
+      second = true;
+    }
     bool on[2];
-    int h[2], d[2], bd[kWaves];
+    int h[2], d[2], bd[2][kWaves];
     float mv[2][kWaves], lv[2][kWaves];
     f32x4 av[2][kWaves];
 #pragma unroll
-    for (int ww = 0; ww < kWaves; ++ww) bd[ww] = sm.bad[ww * 2 + (ww == wa ? sa : 0)];
-#pragma unroll
     for (int u = 0; u < 2; ++u) {
-      const int i = tid + u * kThreads;
-      on[u] = i < items;
+      const int wa = cs[u] >> 1, sa = cs[u] & 1;
+      const int i = two_pieces ? tid : tid + u * kThreads;
+      on[u] = i < items && (u == 0 || !two_pieces || second);
       h[u] = on[u] ? i / kQuads : 0;
       d[u] = on[u] ? 4 * (i - h[u] * kQuads) : 0;
 #pragma unroll
       for (int ww = 0; ww < kWaves; ++ww) {
         const int sl = ww == wa ? sa : 0;
+        bd[u][ww] = sm.bad[ww * 2 + sl];
         mv[u][ww] = sm.m[sm.mi(ww, sl, h[u])];
         lv[u][ww] = sm.l[sm.mi(ww, sl, h[u])];
         av[u][ww] = *reinterpret_cast<const f32x4*>(sm.acc_row(ww, sl, h[u]) + d[u]);
       }
     }
-    int bad = 0;
-#pragma unroll
-    for (int ww = 0; ww < kWaves; ++ww)
-      if ((hold >> ww) & 1) bad |= bd[ww];
-    const brsrc wr_slot = buffer_rsrc(a.ws_o + (size_t)wslot * G * D, (uint32_t)(G * D * sizeof(float)));
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       if (!on[u]) continue;
+      const int c = cs[u];
+      const int b = __builtin_amdgcn_readlane(f.b, c);
+      const int g = __builtin_amdgcn_readlane(f.g, c);
+      const float vmul = __builtin_bit_cast(float, __builtin_amdgcn_readlane(f.vmul, c));
+      const int nparts = __builtin_amdgcn_readlane(f.parts, c);
+      const int wslot = __builtin_amdgcn_readlane(f.slot, c);
+      const int hold = __builtin_amdgcn_readlane(f.hold, c);
+      int bad = 0;
+#pragma unroll
+      for (int ww = 0; ww < kWaves; ++ww)
+        if ((hold >> ww) & 1) bad |= bd[u][ww];
       float M = -INFINITY;
 #pragma unroll
       for (int ww = 0; ww < kWaves; ++ww)
@@ -1298,6 +1311,7 @@ __device__ __forceinline__ void combine_pieces(const Params& a, const BalSm<D>& 
         store_out4<IO>(a.out, row * D + d[u], val);
         if (d[u] == 0 && a.lse_out) a.lse_out[row] = lse2 * kLn2;
       } else {
+        const brsrc wr_slot = buffer_rsrc(a.ws_o + (size_t)wslot * G * D, (uint32_t)(G * D * sizeof(float)));
         st_agent4(wr_slot, (uint32_t)((h[u] * D + d[u]) * sizeof(float)), val);
         if (d[u] == 0) st_agent(a.ws_lse + (size_t)wslot * G + h[u], lse2);
       }
